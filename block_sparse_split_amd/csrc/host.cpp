@@ -1,0 +1,720 @@
+// Host side of libsplitkv: argument checks, the chunk cost model, LPT
+// placement, the in-GPU work schedule and the C entry points.
+//
+// Sources: arXiv abstract of "Split-KV: Efficient Context Parallelism for
+// Training Diffusion Drafters" and the rit.work blog post on Split-KV,
+// section "Split-KV moves queries, not keys and values" (chunk costs known
+// in advance from the full query set; chunks ordered from most to least
+// expensive, each placed on the least-loaded participant).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <functional>
+#include <mutex>
+#include <new>
+#include <queue>
+#include <stdexcept>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "launch.h"
+#include "schedule.h"
+#include "splitkv.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+struct Fail {
+  skv_status code;
+  std::string msg;
+};
+
+[[noreturn]] void fail(skv_status code, const std::string& msg) {
+  throw Fail{code, msg};
+}
+
+void require(bool ok, const char* msg) {
+  if (!ok) fail(SKV_ERR_INVALID_ARG, msg);
+}
+
+template <class F>
+skv_status guarded(F&& f) {
+  try {
+    g_err.clear();
+    f();
+    return SKV_OK;
+  } catch (const Fail& e) {
+    g_err = e.msg;
+    return e.code;
+  } catch (const std::bad_alloc&) {
+    g_err = "host allocation failed";
+    return SKV_ERR_INVALID_ARG;
+  } catch (const std::exception& e) {
+    g_err = e.what();
+    return SKV_ERR_INVALID_ARG;
+  }
+}
+
+void check_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    fail(SKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Number of anchor blocks whose visible interval [lo_i, a_i) meets [t0, t1).
+int64_t pairs_visible(const int32_t* anchors, const int32_t* lo, int32_t nb,
+                      int64_t t0, int64_t t1) {
+  int64_t n = 0;
+  for (int32_t i = 0; i < nb; ++i)
+    n += std::max<int64_t>(lo[i], t0) < std::min<int64_t>(anchors[i], t1);
+  return n;
+}
+
+void check_blocks(const int32_t* anchors, const int32_t* lo, int32_t nb) {
+  require(nb >= 0, "nb must be >= 0");
+  require(nb == 0 || (anchors && lo), "anchors/lo must not be NULL");
+  for (int32_t i = 0; i < nb; ++i)
+    require(lo[i] >= 0 && anchors[i] >= lo[i], "need 0 <= lo[i] <= anchors[i]");
+}
+
+void chunk_costs(const int32_t* anchors, const int32_t* lo, int32_t nb,
+                 const int32_t* pos, const int32_t* len, int32_t n,
+                 int32_t tile_k, int64_t* out) {
+  check_blocks(anchors, lo, nb);
+  require(n >= 0 && tile_k >= 1, "need n_chunks >= 0 and tile_k >= 1");
+  require(n == 0 || (pos && len && out), "chunk arrays must not be NULL");
+  for (int32_t c = 0; c < n; ++c) {
+    require(len[c] >= 1 && pos[c] >= 0, "chunk_len must be >= 1, pos >= 0");
+    int64_t total = 0;
+    const int64_t end = int64_t(pos[c]) + len[c];
+    for (int64_t t0 = pos[c]; t0 < end; t0 += tile_k)
+      total += pairs_visible(anchors, lo, nb, t0, std::min(t0 + tile_k, end));
+    out[c] = total;
+  }
+}
+
+// LPT with a binary heap keyed by (load, bin): jobs by decreasing cost
+// (stable in job index), each to the least-loaded bin, lowest bin on ties.
+std::vector<int32_t> lpt(const std::vector<int64_t>& cost, int32_t m,
+                         std::vector<int64_t>* load_out,
+                         std::vector<int32_t>* order_out = nullptr) {
+  require(m >= 1, "n_bins must be >= 1");
+  const int32_t n = int32_t(cost.size());
+  std::vector<int32_t> order(n);
+  for (int32_t i = 0; i < n; ++i) {
+    require(cost[i] >= 0, "costs must be >= 0");
+    order[i] = i;
+  }
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
+  using Entry = std::pair<int64_t, int32_t>;  // (load, bin)
+  std::priority_queue<Entry, std::vector<Entry>, std::greater<Entry>> heap;
+  for (int32_t b = 0; b < m; ++b) heap.push({0, b});
+  std::vector<int32_t> bin(n);
+  std::vector<int64_t> load(m, 0);
+  for (int32_t j : order) {
+    Entry e = heap.top();
+    heap.pop();
+    bin[j] = e.second;
+    e.first += cost[j];
+    load[e.second] = e.first;
+    heap.push(e);
+  }
+  if (load_out) *load_out = std::move(load);
+  if (order_out) *order_out = std::move(order);
+  return bin;
+}
+
+std::atomic<int32_t> g_cu_cache[64];
+
+int32_t device_cu_count() {
+  int dev = 0;
+  check_hip(hipGetDevice(&dev), "hipGetDevice");
+  if (dev >= 0 && dev < 64) {
+    int32_t c = g_cu_cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  check_hip(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev),
+            "hipDeviceGetAttribute(CU count)");
+  if (dev >= 0 && dev < 64) g_cu_cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+struct Tile {
+  int32_t row, pos, len;
+};
+
+struct Geometry {
+  int32_t nb, hq, hkv, d, G, nq, rows_per_head, qt_per_head, n_local;
+};
+
+Geometry check_problem(const skv_problem* p) {
+  require(p != nullptr, "problem must not be NULL");
+  require(p->nb >= 1, "nb must be >= 1");
+  require(p->hq >= 1 && p->hkv >= 1 && p->hq % p->hkv == 0,
+          "hq must be a positive multiple of hkv");
+  const int32_t G = p->hq / p->hkv;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8 || G == 16))
+    fail(SKV_ERR_UNSUPPORTED, "hq/hkv must be 1, 2, 4, 8 or 16");
+  if (!(p->d == 64 || p->d == 128)) fail(SKV_ERR_UNSUPPORTED, "d must be 64 or 128");
+  if (!(p->dtype == SKV_BF16 || p->dtype == SKV_F32))
+    fail(SKV_ERR_UNSUPPORTED, "dtype must be SKV_BF16 or SKV_F32");
+  require(std::isfinite(p->scale) && p->scale > 0.f, "scale must be finite and > 0");
+  require(p->nb <= (1 << 22), "nb too large");
+  check_blocks(p->anchors, p->lo, p->nb);
+  require(p->n_chunks >= 0, "n_chunks must be >= 0");
+  require(p->with_draft == 0 || p->with_draft == 1, "with_draft must be 0 or 1");
+  Geometry g{};
+  g.nb = p->nb;
+  g.hq = p->hq;
+  g.hkv = p->hkv;
+  g.d = p->d;
+  g.G = G;
+  g.nq = p->nb * skv::kBlock;
+  g.rows_per_head = g.nq * G;
+  g.qt_per_head = (g.rows_per_head + skv::kQTile - 1) / skv::kQTile;
+  g.n_local = 0;
+  if (p->n_chunks > 0) {
+    require(p->chunk_pos && p->chunk_off, "chunk_pos/chunk_off must not be NULL");
+    require(p->chunk_off[0] == 0, "chunk_off[0] must be 0");
+    for (int32_t c = 0; c < p->n_chunks; ++c) {
+      require(p->chunk_off[c + 1] > p->chunk_off[c], "chunks must hold >= 1 key");
+      require(p->chunk_pos[c] >= 0, "chunk_pos must be >= 0");
+    }
+    g.n_local = p->chunk_off[p->n_chunks];
+  }
+  return g;
+}
+
+// Key tiles of the shard, sorted by absolute position; chunks must not
+// overlap in absolute position.
+std::vector<Tile> build_tiles(const skv_problem* p) {
+  std::vector<Tile> tiles;
+  for (int32_t c = 0; c < p->n_chunks; ++c) {
+    const int32_t n = p->chunk_off[c + 1] - p->chunk_off[c];
+    for (int32_t u = 0; u < n; u += skv::kTileK)
+      tiles.push_back({p->chunk_off[c] + u, p->chunk_pos[c] + u,
+                       std::min(skv::kTileK, n - u)});
+  }
+  std::stable_sort(tiles.begin(), tiles.end(),
+                   [](const Tile& a, const Tile& b) { return a.pos < b.pos; });
+  for (size_t t = 1; t < tiles.size(); ++t)
+    require(int64_t(tiles[t - 1].pos) + tiles[t - 1].len <= tiles[t].pos,
+            "chunks overlap in absolute key position");
+  return tiles;
+}
+
+int32_t env_int(const char* name, int32_t dflt, int32_t lo, int32_t hi) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  long v = std::strtol(s, nullptr, 10);
+  return int32_t(std::min<long>(hi, std::max<long>(lo, v)));
+}
+
+struct Item {
+  int32_t head, qt, t0, t1, slot, flags;
+  int64_t cost;
+};
+
+struct KvItem {
+  int32_t head, t0, nt, dtok0, ndraft, b0, b1;
+  int64_t cost;
+};
+
+// XCD classes: workgroup w runs on XCD w % 8 (round-robin dispatch), so the
+// work of kv head h is kept on workgroups w with w % n_cls == h % n_cls.
+int32_t xcd_classes(int32_t hkv, int32_t n_wg) {
+  int32_t c = 1;
+  if (hkv % 8 == 0 || 8 % hkv == 0) c = std::min(hkv, 8);
+  if (n_wg % c != 0 || n_wg < c) c = 1;
+  return c;
+}
+
+// LPT per XCD class; returns per-workgroup queues in assignment order.
+template <class CostOf, class HeadOf>
+std::vector<std::vector<int32_t>> place(int32_t n_items, int32_t n_wg,
+                                        int32_t n_cls, CostOf cost_of,
+                                        HeadOf head_of, int64_t* max_bin) {
+  std::vector<std::vector<int32_t>> queue(n_wg);
+  *max_bin = 0;
+  const int32_t per = n_wg / n_cls;
+  for (int32_t c = 0; c < n_cls; ++c) {
+    std::vector<int32_t> ids;
+    std::vector<int64_t> costs;
+    for (int32_t i = 0; i < n_items; ++i)
+      if (head_of(i) % n_cls == c) {
+        ids.push_back(i);
+        costs.push_back(cost_of(i));
+      }
+    std::vector<int64_t> load;
+    std::vector<int32_t> order;
+    std::vector<int32_t> bin = lpt(costs, per, &load, &order);
+    for (int32_t j : order) queue[c + bin[j] * n_cls].push_back(ids[j]);
+    for (int64_t l : load) *max_bin = std::max(*max_bin, l);
+  }
+  return queue;
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
+                    int64_t capacity, skv_schedule_info* info) {
+  require(info != nullptr, "info must not be NULL");
+  const Geometry g = check_problem(p);
+  if (n_wg == 0) n_wg = device_cu_count();
+  require(n_wg >= 1 && n_wg <= 65536, "n_workgroups must be in [1, 65536]");
+  const std::vector<Tile> tiles = build_tiles(p);
+  const int32_t nt = int32_t(tiles.size());
+  const int32_t* A = p->anchors;
+  const int32_t* L = p->lo;
+  const int32_t tok_per_qt = skv::kQTile / g.G;
+
+  // Visible (anchor block, tile) pairs per query tile and tile.
+  std::vector<Item> items;
+  std::vector<std::vector<int32_t>> qt_vis(g.qt_per_head);
+  std::vector<std::vector<int64_t>> qt_cost(g.qt_per_head);
+  int64_t total = 0;
+  for (int32_t qt = 0; qt < g.qt_per_head; ++qt) {
+    const int32_t b0 = qt * tok_per_qt / skv::kBlock;
+    const int32_t b1 = std::min(g.nb, ((qt + 1) * tok_per_qt + skv::kBlock - 1) / skv::kBlock);
+    for (int32_t t = 0; t < nt; ++t) {
+      int64_t c = 0;
+      for (int32_t b = b0; b < b1; ++b)
+        c += std::max<int64_t>(L[b], tiles[t].pos) <
+             std::min<int64_t>(A[b], int64_t(tiles[t].pos) + tiles[t].len);
+      if (c) {
+        qt_vis[qt].push_back(t);
+        qt_cost[qt].push_back(c);
+        total += c * g.hkv;
+      }
+    }
+    if (p->with_draft) total += int64_t(b1 - b0) * g.hkv;
+  }
+  // Cut each query tile's visible tiles into runs of consecutive tile
+  // indices, then each run into pieces of `piece` cost (the last piece of a
+  // run keeps the remainder).  The remainders, of varied sizes, are what LPT
+  // places last, so they fill the bins evenly.  Several piece sizes (the
+  // per-workgroup mean load divided by r) are tried and the one with the
+  // smallest LPT makespan is kept (ties: fewer items).
+  struct Piece {
+    int32_t t0, t1;
+    int64_t cost;
+  };
+  auto cut = [&](int64_t piece) {
+    std::vector<std::vector<Piece>> out(g.qt_per_head);
+    for (int32_t qt = 0; qt < g.qt_per_head; ++qt) {
+      const auto& vis = qt_vis[qt];
+      const auto& cst = qt_cost[qt];
+      size_t i = 0;
+      while (i < vis.size()) {
+        size_t j = i + 1;
+        while (j < vis.size() && vis[j] == vis[j - 1] + 1) ++j;
+        size_t start = i;
+        int64_t acc = 0;
+        for (size_t k = i; k < j; ++k) {
+          acc += cst[k];
+          if (acc >= piece || k + 1 == j) {
+            out[qt].push_back({vis[start], vis[k] + 1, acc});
+            start = k + 1;
+            acc = 0;
+          }
+        }
+        i = j;
+      }
+    }
+    return out;
+  };
+  const int32_t n_cls_fwd = xcd_classes(g.hkv, n_wg);
+  auto make_items = [&](const std::vector<std::vector<Piece>>& pieces, std::vector<Item>& out,
+                        std::vector<int32_t>& split, int32_t& slots) {
+    out.clear();
+    split.clear();
+    slots = 0;
+    for (int32_t h = 0; h < g.hkv; ++h) {
+      for (int32_t qt = 0; qt < g.qt_per_head; ++qt) {
+        const int32_t b0 = qt * tok_per_qt / skv::kBlock;
+        const int32_t b1 =
+            std::min(g.nb, ((qt + 1) * tok_per_qt + skv::kBlock - 1) / skv::kBlock);
+        std::vector<Piece> ps = pieces[qt];
+        if (ps.empty()) ps.push_back({0, 0, 0});
+        const int32_t n = int32_t(ps.size());
+        const int32_t slot0 = n > 1 ? slots : -1;
+        if (n > 1) {
+          split.insert(split.end(), {h, qt, slot0, n});
+          slots += n;
+        }
+        for (int32_t k = 0; k < n; ++k) {
+          Item it{h, qt, ps[k].t0, ps[k].t1, n > 1 ? slot0 + k : -1, 0, ps[k].cost};
+          if (k == 0 && p->with_draft) {
+            it.flags |= skv::kItemDraft;
+            it.cost += b1 - b0;
+          }
+          out.push_back(it);
+        }
+      }
+    }
+  };
+  const int32_t forced = env_int("SKV_PIECE_DIV", 0, 0, 64);
+  const int32_t divs_all[] = {1, 2, 3, 4, 5, 6, 8, 12, 16};
+  std::vector<int32_t> divs;
+  if (forced) divs.push_back(forced); else divs.assign(std::begin(divs_all), std::end(divs_all));
+  // Each partial slot costs a write and a read of 256 rows of fp32 O + LSE
+  // at chip bandwidth, while one (block, tile) pair costs its MFMA work on one
+  // of n_wg workgroups.  With the bf16 MFMA peak (~2.5 PFLOP/s, ~60% of it
+  // reached) and 8 TB/s, one slot weighs `slot_w` pairs of makespan.
+  const double pair_flops = double(skv::kBlock) * g.G * skv::kTileK * g.d * 4.0;
+  const double slot_bytes = double(skv::kQTile) * (g.d + 1) * 4.0 * 2.0;
+  const double slot_w = (slot_bytes / 8e12) / (pair_flops * n_wg / 1.5e15);
+  std::vector<int32_t> split_rec;  // S_WORDS per split query tile
+  int32_t n_slots = 0;
+  double best_obj = -1.0;
+  for (int32_t r : divs) {
+    const int64_t piece = std::max<int64_t>(1, total / (int64_t(n_wg) * r));
+    std::vector<Item> cand;
+    std::vector<int32_t> cand_split;
+    int32_t cand_slots = 0;
+    make_items(cut(piece), cand, cand_split, cand_slots);
+    int64_t mb = 0;
+    place(int32_t(cand.size()), n_wg, n_cls_fwd, [&](int32_t i) { return cand[i].cost; },
+          [&](int32_t i) { return cand[i].head; }, &mb);
+    const double obj = double(mb) + slot_w * cand_slots;
+    if (best_obj < 0 || obj < best_obj) {
+      best_obj = obj;
+      items.swap(cand);
+      split_rec.swap(cand_split);
+      n_slots = cand_slots;
+    }
+  }
+  // dK/dV items: two consecutive tiles per item (one if a lone tile is
+  // left), plus draft groups of 128 draft tokens.
+  std::vector<KvItem> kv;
+  for (int32_t h = 0; h < g.hkv; ++h) {
+    for (int32_t t = 0; t < nt; t += 2) {
+      const int32_t n2 = std::min(2, nt - t);
+      int32_t bmin = g.nb, bmax = -1;
+      int64_t c = 0;
+      for (int32_t u = t; u < t + n2; ++u)
+        for (int32_t b = 0; b < g.nb; ++b)
+          if (std::max<int64_t>(L[b], tiles[u].pos) <
+              std::min<int64_t>(A[b], int64_t(tiles[u].pos) + tiles[u].len)) {
+            ++c;
+            bmin = std::min(bmin, b);
+            bmax = std::max(bmax, b);
+          }
+      if (bmax < 0) {  // no block sees these keys: zero gradients
+        bmin = 0;
+        bmax = -1;
+      }
+      kv.push_back({h, t, n2, 0, 0, bmin, bmax + 1, c});
+    }
+    if (p->with_draft) {
+      for (int32_t tok = 0; tok < g.nq; tok += skv::kKvGroup) {
+        const int32_t nd = std::min(skv::kKvGroup, g.nq - tok);
+        const int32_t b0 = tok / skv::kBlock, b1 = (tok + nd) / skv::kBlock;
+        kv.push_back({h, 0, 0, tok, nd, b0, b1, int64_t(b1 - b0)});
+      }
+    }
+  }
+  const int32_t n_cls = xcd_classes(g.hkv, n_wg);
+  int64_t max_bin = 0, kv_max_bin = 0;
+  auto q = place(int32_t(items.size()), n_wg, n_cls,
+                 [&](int32_t i) { return items[i].cost; },
+                 [&](int32_t i) { return items[i].head; }, &max_bin);
+  auto kq = place(int32_t(kv.size()), n_wg, n_cls,
+                  [&](int32_t i) { return kv[i].cost; },
+                  [&](int32_t i) { return kv[i].head; }, &kv_max_bin);
+  int64_t kv_total = 0;
+  for (const auto& k : kv) kv_total += k.cost;
+  int64_t item_total = 0;
+  for (const auto& it : items) item_total += it.cost;
+
+  // Image layout.
+  using namespace skv;
+  int64_t off = H_WORDS;
+  const int64_t off_anchors = off; off += g.nb;
+  const int64_t off_lo = off; off += g.nb;
+  const int64_t off_tiles = off; off += int64_t(nt) * T_WORDS;
+  const int64_t off_items = off; off += int64_t(items.size()) * I_WORDS;
+  const int64_t off_qoff = off; off += n_wg + 1;
+  const int64_t off_queue = off; off += int64_t(items.size());
+  const int64_t off_split = off; off += int64_t(split_rec.size());
+  const int64_t off_kv = off; off += int64_t(kv.size()) * K_WORDS;
+  const int64_t off_kvqoff = off; off += n_wg + 1;
+  const int64_t off_kvqueue = off; off += int64_t(kv.size());
+  const int64_t words = off;
+  require(words < (int64_t(1) << 31), "schedule image too large");
+
+  const int64_t rows_slot = skv::kQTile;
+  const int64_t fwd_ws = align_up(int64_t(n_slots) * rows_slot * g.d * 4, 256) +
+                         align_up(int64_t(n_slots) * rows_slot * 4, 256);
+  const int64_t bwd_ws = align_up(int64_t(g.nq) * g.hq * 4, 256) +
+                         align_up(int64_t(n_slots) * rows_slot * g.d * 4, 256);
+  std::memset(info, 0, sizeof(*info));
+  info->words = words;
+  info->n_workgroups = n_wg;
+  info->n_tiles = nt;
+  info->n_qtiles = g.qt_per_head * g.hkv;
+  info->n_items = int32_t(items.size());
+  info->n_split_qtiles = int32_t(split_rec.size() / S_WORDS);
+  info->n_partial_slots = n_slots;
+  info->n_kv_items = int32_t(kv.size());
+  info->fwd_workspace_bytes = fwd_ws;
+  info->bwd_workspace_bytes = bwd_ws;
+  info->item_cost_total = item_total;
+  info->item_cost_max_bin = max_bin;
+  info->kv_cost_total = kv_total;
+  info->kv_cost_max_bin = kv_max_bin;
+  info->nb = g.nb;
+  info->hq = g.hq;
+  info->hkv = g.hkv;
+  info->d = g.d;
+  info->n_local = g.n_local;
+  info->with_draft = p->with_draft;
+  if (image == nullptr) return;
+  if (capacity < words)
+    fail(SKV_ERR_WORKSPACE, "schedule image too small: need " +
+                                std::to_string(words) + " int32 words");
+  std::memset(image, 0, size_t(words) * 4);
+  int32_t* H = image;
+  H[H_MAGIC] = kMagic;
+  H[H_VERSION] = kVersion;
+  H[H_NB] = g.nb;
+  H[H_HQ] = g.hq;
+  H[H_HKV] = g.hkv;
+  H[H_D] = g.d;
+  H[H_G] = g.G;
+  H[H_NLOCAL] = g.n_local;
+  H[H_DRAFT] = p->with_draft;
+  H[H_NTILES] = nt;
+  H[H_QT_PER_HEAD] = g.qt_per_head;
+  H[H_NITEMS] = int32_t(items.size());
+  H[H_NWG] = n_wg;
+  H[H_NSPLIT] = info->n_split_qtiles;
+  H[H_NSLOTS] = n_slots;
+  H[H_NKV] = int32_t(kv.size());
+  H[H_OFF_ANCHORS] = int32_t(off_anchors);
+  H[H_OFF_LO] = int32_t(off_lo);
+  H[H_OFF_TILES] = int32_t(off_tiles);
+  H[H_OFF_ITEMS] = int32_t(off_items);
+  H[H_OFF_QOFF] = int32_t(off_qoff);
+  H[H_OFF_QUEUE] = int32_t(off_queue);
+  H[H_OFF_SPLIT] = int32_t(off_split);
+  H[H_OFF_KV] = int32_t(off_kv);
+  H[H_OFF_KVQOFF] = int32_t(off_kvqoff);
+  H[H_OFF_KVQUEUE] = int32_t(off_kvqueue);
+  H[H_NCLASS] = n_cls;
+  std::memcpy(image + off_anchors, A, size_t(g.nb) * 4);
+  std::memcpy(image + off_lo, L, size_t(g.nb) * 4);
+  for (int32_t t = 0; t < nt; ++t) {
+    int32_t* w = image + off_tiles + int64_t(t) * T_WORDS;
+    w[T_ROW] = tiles[t].row;
+    w[T_POS] = tiles[t].pos;
+    w[T_LEN] = tiles[t].len;
+  }
+  for (size_t i = 0; i < items.size(); ++i) {
+    int32_t* w = image + off_items + int64_t(i) * I_WORDS;
+    w[I_HEAD] = items[i].head;
+    w[I_QT] = items[i].qt;
+    w[I_T0] = items[i].t0;
+    w[I_T1] = items[i].t1;
+    w[I_SLOT] = items[i].slot;
+    w[I_FLAGS] = items[i].flags;
+    w[I_COST] = int32_t(std::min<int64_t>(items[i].cost, INT32_MAX));
+  }
+  int32_t pos = 0;
+  for (int32_t w = 0; w < n_wg; ++w) {
+    image[off_qoff + w] = pos;
+    for (int32_t it : q[w]) image[off_queue + pos++] = it;
+  }
+  image[off_qoff + n_wg] = pos;
+  std::copy(split_rec.begin(), split_rec.end(), image + off_split);
+  for (size_t i = 0; i < kv.size(); ++i) {
+    int32_t* w = image + off_kv + int64_t(i) * K_WORDS;
+    w[K_HEAD] = kv[i].head;
+    w[K_T0] = kv[i].t0;
+    w[K_NT] = kv[i].nt;
+    w[K_DTOK0] = kv[i].dtok0;
+    w[K_NDRAFT] = kv[i].ndraft;
+    w[K_B0] = kv[i].b0;
+    w[K_B1] = kv[i].b1;
+    w[K_COST] = int32_t(std::min<int64_t>(kv[i].cost, INT32_MAX));
+  }
+  pos = 0;
+  for (int32_t w = 0; w < n_wg; ++w) {
+    image[off_kvqoff + w] = pos;
+    for (int32_t it : kq[w]) image[off_kvqueue + pos++] = it;
+  }
+  image[off_kvqoff + n_wg] = pos;
+}
+
+void check_info(const skv_problem* p, const skv_schedule_info* info,
+                const int32_t* schedule) {
+  const Geometry g = check_problem(p);
+  require(info != nullptr && schedule != nullptr, "info/schedule must not be NULL");
+  require(info->nb == g.nb && info->hq == g.hq && info->hkv == g.hkv &&
+              info->d == g.d && info->n_local == g.n_local &&
+              info->with_draft == p->with_draft,
+          "schedule was built for a different problem");
+  require(info->n_workgroups >= 1, "schedule has no workgroups");
+}
+
+size_t elem_size(int32_t dt) { return dt == SKV_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+const char* skv_last_error(void) { return g_err.c_str(); }
+
+int32_t skv_abi_version(void) { return SKV_ABI_VERSION; }
+
+skv_status skv_chunk_costs(const int32_t* anchors, const int32_t* lo, int32_t nb,
+                           const int32_t* chunk_pos, const int32_t* chunk_len,
+                           int32_t n_chunks, int32_t tile_k, int64_t* out_cost) {
+  return guarded([&] {
+    chunk_costs(anchors, lo, nb, chunk_pos, chunk_len, n_chunks, tile_k, out_cost);
+  });
+}
+
+skv_status skv_plan_lpt_costs(const int64_t* cost, int32_t n, int32_t n_bins,
+                              int32_t* out_bin, int64_t* out_load) {
+  return guarded([&] {
+    require(n >= 0, "n must be >= 0");
+    require(n == 0 || (cost && out_bin), "cost/out_bin must not be NULL");
+    require(n_bins >= 1, "n_bins must be >= 1");
+    std::vector<int64_t> c(cost, cost + n);
+    std::vector<int64_t> load;
+    std::vector<int32_t> bin = lpt(c, n_bins, &load);
+    if (n) std::memcpy(out_bin, bin.data(), size_t(n) * 4);
+    if (out_load) std::memcpy(out_load, load.data(), size_t(n_bins) * 8);
+  });
+}
+
+skv_status skv_plan_lpt(const int32_t* anchors, const int32_t* lo, int32_t nb,
+                        const int32_t* chunk_pos, const int32_t* chunk_len,
+                        int32_t n_chunks, int32_t tile_k, int32_t n_bins,
+                        int32_t* out_bin, int64_t* out_cost, int64_t* out_load) {
+  return guarded([&] {
+    require(n_bins >= 1, "n_bins must be >= 1");
+    require(n_chunks >= 0, "n_chunks must be >= 0");
+    require(n_chunks == 0 || out_bin, "out_bin must not be NULL");
+    std::vector<int64_t> c(size_t(std::max(n_chunks, 0)));
+    chunk_costs(anchors, lo, nb, chunk_pos, chunk_len, n_chunks, tile_k, c.data());
+    std::vector<int64_t> load;
+    std::vector<int32_t> bin = lpt(c, n_bins, &load);
+    if (n_chunks) std::memcpy(out_bin, bin.data(), size_t(n_chunks) * 4);
+    if (out_cost && n_chunks) std::memcpy(out_cost, c.data(), size_t(n_chunks) * 8);
+    if (out_load) std::memcpy(out_load, load.data(), size_t(n_bins) * 8);
+  });
+}
+
+skv_status skv_schedule_build(const skv_problem* p, int32_t n_workgroups,
+                              int32_t* image, int64_t capacity_words,
+                              skv_schedule_info* info) {
+  return guarded([&] { build_schedule(p, n_workgroups, image, capacity_words, info); });
+}
+
+skv_status skv_attn_fwd_partial(const skv_problem* p, const skv_schedule_info* info,
+                                const int32_t* schedule, const void* Q, const void* K,
+                                const void* V, const void* Kd, const void* Vd, void* O,
+                                int32_t o_dtype, float* LSE, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    check_info(p, info, schedule);
+    require(Q && O && LSE, "Q/O/LSE must not be NULL");
+    require(info->n_local == 0 || (K && V), "K/V must not be NULL");
+    require(!p->with_draft || (Kd && Vd), "Kd/Vd must not be NULL with with_draft");
+    if (!(o_dtype == SKV_BF16 || o_dtype == SKV_F32))
+      fail(SKV_ERR_UNSUPPORTED, "o_dtype must be SKV_BF16 or SKV_F32");
+    if (info->fwd_workspace_bytes > 0) {
+      if (workspace_bytes < info->fwd_workspace_bytes || !workspace)
+        fail(SKV_ERR_WORKSPACE, "workspace too small: need " +
+                                    std::to_string(info->fwd_workspace_bytes) + " bytes");
+    }
+    skv::FwdArgs a{};
+    a.sched = schedule;
+    a.Q = Q; a.K = K; a.V = V; a.Kd = Kd; a.Vd = Vd;
+    a.O = O; a.LSE = LSE;
+    a.o_bf16 = o_dtype == SKV_BF16;
+    a.dtype_bf16 = p->dtype == SKV_BF16;
+    a.hq = p->hq; a.hkv = p->hkv; a.d = p->d; a.nb = p->nb;
+    a.scale = p->scale;
+    a.n_wg = info->n_workgroups;
+    a.n_split = info->n_split_qtiles;
+    a.n_slots = info->n_partial_slots;
+    a.ws_O = static_cast<float*>(workspace);
+    a.ws_LSE = workspace ? reinterpret_cast<float*>(
+                   static_cast<char*>(workspace) +
+                   align_up(int64_t(info->n_partial_slots) * skv::kQTile * p->d * 4, 256))
+                         : nullptr;
+    check_hip(skv::launch_fwd(a, static_cast<hipStream_t>(stream)), "forward launch");
+  });
+}
+
+skv_status skv_merge_lse(int32_t n_parts, int64_t rows, int32_t d, const void* O_parts,
+                         int32_t in_dtype, const float* LSE_parts, void* O_out,
+                         int32_t out_dtype, float* LSE_out, void* stream) {
+  return guarded([&] {
+    require(n_parts >= 1 && rows >= 0, "need n_parts >= 1 and rows >= 0");
+    if (!(d == 64 || d == 128)) fail(SKV_ERR_UNSUPPORTED, "d must be 64 or 128");
+    if (!((in_dtype == SKV_BF16 || in_dtype == SKV_F32) &&
+          (out_dtype == SKV_BF16 || out_dtype == SKV_F32)))
+      fail(SKV_ERR_UNSUPPORTED, "dtypes must be SKV_BF16 or SKV_F32");
+    if (rows == 0) return;
+    require(O_parts && LSE_parts && O_out && LSE_out, "pointers must not be NULL");
+    const char* ob = static_cast<const char*>(O_out);
+    const char* ib = static_cast<const char*>(O_parts);
+    const int64_t out_bytes = rows * d * int64_t(elem_size(out_dtype));
+    const int64_t in_bytes = int64_t(n_parts) * rows * d * int64_t(elem_size(in_dtype));
+    require(ob + out_bytes <= ib || ib + in_bytes <= ob, "O_out must not alias O_parts");
+    check_hip(skv::launch_merge(n_parts, rows, d, O_parts, in_dtype == SKV_BF16, LSE_parts,
+                                O_out, out_dtype == SKV_BF16, LSE_out,
+                                static_cast<hipStream_t>(stream)),
+              "merge launch");
+  });
+}
+
+skv_status skv_attn_bwd(const skv_problem* p, const skv_schedule_info* info,
+                        const int32_t* schedule, const void* Q, const void* K,
+                        const void* V, const void* Kd, const void* Vd, const void* O,
+                        const void* dO, const float* LSE, float* dQ, void* dK, void* dV,
+                        void* dKd, void* dVd, int32_t grad_dtype, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    check_info(p, info, schedule);
+    require(Q && O && dO && LSE && dQ, "Q/O/dO/LSE/dQ must not be NULL");
+    require(info->n_local == 0 || (K && V && dK && dV), "K/V/dK/dV must not be NULL");
+    require(!p->with_draft || (Kd && Vd && dKd && dVd),
+            "Kd/Vd/dKd/dVd must not be NULL with with_draft");
+    if (!(grad_dtype == SKV_BF16 || grad_dtype == SKV_F32))
+      fail(SKV_ERR_UNSUPPORTED, "grad_dtype must be SKV_BF16 or SKV_F32");
+    if (workspace_bytes < info->bwd_workspace_bytes || !workspace)
+      fail(SKV_ERR_WORKSPACE, "workspace too small: need " +
+                                  std::to_string(info->bwd_workspace_bytes) + " bytes");
+    skv::BwdArgs a{};
+    a.sched = schedule;
+    a.Q = Q; a.K = K; a.V = V; a.Kd = Kd; a.Vd = Vd; a.O = O; a.dO = dO; a.LSE = LSE;
+    a.dQ = dQ; a.dK = dK; a.dV = dV; a.dKd = dKd; a.dVd = dVd;
+    a.grad_bf16 = grad_dtype == SKV_BF16;
+    a.dtype_bf16 = p->dtype == SKV_BF16;
+    a.hq = p->hq; a.hkv = p->hkv; a.d = p->d; a.nb = p->nb;
+    a.n_local = info->n_local;
+    a.scale = p->scale;
+    a.n_wg = info->n_workgroups;
+    a.n_split = info->n_split_qtiles;
+    a.n_slots = info->n_partial_slots;
+    a.with_draft = p->with_draft;
+    a.ws_D = static_cast<float*>(workspace);
+    a.ws_dQ = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align_up(int64_t(p->nb) * 16 * p->hq * 4, 256));
+    check_hip(skv::launch_bwd(a, static_cast<hipStream_t>(stream)), "backward launch");
+  });
+}
+
+}  // extern "C"

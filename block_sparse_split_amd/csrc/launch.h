@@ -1,0 +1,54 @@
+// Internal interface between the C entry points and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skv {
+
+struct FwdArgs {
+  const int32_t* sched;     // device schedule image
+  const void* Q;            // [Nq, hq, d]
+  const void* K;            // [n_local, hkv, d]
+  const void* V;
+  const void* Kd;           // [Nq, hkv, d] or null
+  const void* Vd;
+  void* O;                  // [Nq, hq, d]
+  float* LSE;               // [Nq, hq]
+  float* ws_O;              // partial slots [n_slots, 256, d] fp32
+  float* ws_LSE;            // [n_slots, 256]
+  int32_t o_bf16, dtype_bf16;
+  int32_t hq, hkv, d, nb;
+  int32_t n_wg, n_split, n_slots;
+  float scale;
+};
+
+struct BwdArgs {
+  const int32_t* sched;
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* Kd;
+  const void* Vd;
+  const void* O;            // final merged output
+  const void* dO;
+  const float* LSE;         // final merged LSE (natural log)
+  float* dQ;                // [Nq, hq, d] fp32
+  void* dK;                 // [n_local, hkv, d]
+  void* dV;
+  void* dKd;                // [Nq, hkv, d]
+  void* dVd;
+  float* ws_D;              // [Nq, hq] rowsum(dO * O)
+  float* ws_dQ;             // partial slots [n_slots, 256, d]
+  int32_t grad_bf16, dtype_bf16;
+  int32_t hq, hkv, d, nb, n_local;
+  int32_t n_wg, n_split, n_slots, with_draft;
+  float scale;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_merge(int32_t n_parts, int64_t rows, int32_t d, const void* O_parts,
+                        bool in_bf16, const float* LSE_parts, void* O_out, bool out_bf16,
+                        float* LSE_out, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace skv

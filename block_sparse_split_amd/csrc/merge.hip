@@ -1,0 +1,181 @@
+// Exact merge of split partial attention results by their log-sum-exp
+// (rit.work blog post on Split-KV, section "Split-KV moves queries, not keys
+// and values": the participants reconcile the softmax normalisation and the
+// split reproduces single-device attention exactly).
+//
+// For one row with partials (O_k, LSE_k), M = max_k LSE_k,
+// LSE = M + ln sum_k exp(LSE_k - M) and O = sum_k exp(LSE_k - LSE) O_k.
+// Partials with LSE_k = -inf weigh zero; a row without a finite LSE_k gets
+// O = 0, LSE = -inf.
+//
+// The merge is HBM-bound (a few flops per byte): each thread owns 8
+// consecutive elements of one row (16-byte loads for bf16), rows are
+// contiguous, so every wave streams whole rows; partial loads are unrolled
+// for memory-level parallelism.
+#include "device_common.h"
+#include "launch.h"
+
+namespace skv {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<__bf16> {
+  static __device__ __forceinline__ void load(const __bf16* p, float* x) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(__bf16* p, const float* x) {
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = f32_to_bf16(x[i]);
+    *reinterpret_cast<bf16x8*>(p) = v;
+  }
+};
+template <>
+struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float* p, float* x) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float* x) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  }
+};
+
+// Merge one row: partial k of this row is at O + k*ostride, L + k*lstride.
+template <typename Tin, typename Tout>
+__device__ __forceinline__ void merge_row(int n, const Tin* O, int64_t ostride, const float* L,
+                                          int64_t lstride, Tout* out, float* lse_out,
+                                          bool write_lse) {
+  float M = kNegInf;
+  for (int k = 0; k < n; ++k) M = fmaxf(M, L[k * lstride]);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  if (M == kNegInf) {
+    Vec8<Tout>::store(out, acc);
+    if (write_lse) *lse_out = kNegInf;
+    return;
+  }
+  float sum = 0.f;
+  for (int k = 0; k < n; ++k) sum += exp2_fast((L[k * lstride] - M) * kLog2e);
+  const float lse = M + logf(sum);
+  const float lse2 = lse * kLog2e;
+  int k = 0;
+  for (; k + 4 <= n; k += 4) {
+    float x[4][8], w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      w[u] = exp2_fast(L[(k + u) * lstride] * kLog2e - lse2);
+      Vec8<Tin>::load(O + (k + u) * ostride, x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = w[u] > 0.f ? fmaf(w[u], x[u][i], acc[i]) : acc[i];
+  }
+  for (; k < n; ++k) {
+    float x[8];
+    const float w = exp2_fast(L[k * lstride] * kLog2e - lse2);
+    Vec8<Tin>::load(O + k * ostride, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = w > 0.f ? fmaf(w, x[i], acc[i]) : acc[i];
+  }
+  Vec8<Tout>::store(out, acc);
+  if (write_lse) *lse_out = lse;
+}
+
+template <typename Tin, typename Tout, int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(int n, int64_t rows, const Tin* O,
+                                                         const float* L, Tout* Oo, float* Lo) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = kThreads / TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = (threadIdx.x % TPR) * 8;
+  if (row >= rows) return;
+  merge_row<Tin, Tout>(n, O + row * D + c, rows * D, L + row, rows, Oo + row * D + c, Lo + row,
+                       c == 0);
+}
+
+// Merge the in-GPU segments of split query tiles from the forward workspace.
+template <typename Tout, int D>
+__global__ __launch_bounds__(kThreads) void merge_split_kernel(const int32_t* S, const float* wsO,
+                                                               const float* wsL, Tout* O,
+                                                               float* LSE) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = kThreads / TPR;
+  constexpr int BPT = kQTile / RPB;  // blocks per split query tile
+  const int sidx = blockIdx.x / BPT;
+  const int32_t* rec = S + S[H_OFF_SPLIT] + sidx * S_WORDS;
+  const int head = rec[S_HEAD], qt = rec[S_QT], slot0 = rec[S_SLOT0], ns = rec[S_NSLOT];
+  const int rloc = (blockIdx.x % BPT) * RPB + threadIdx.x / TPR;
+  const int c = (threadIdx.x % TPR) * 8;
+  const int G = S[H_G], hq = S[H_HQ], nq = S[H_NB] * kBlock;
+  const int rho = qt * kQTile + rloc;
+  if (rho >= nq * G) return;
+  const int64_t orow = (int64_t)(rho / G) * hq + head * G + rho % G;
+  const int64_t prow = (int64_t)slot0 * kQTile + rloc;
+  merge_row<float, Tout>(ns, wsO + prow * D + c, (int64_t)kQTile * D, wsL + prow, kQTile,
+                         O + orow * D + c, LSE + orow, c == 0);
+}
+
+template <int D>
+hipError_t launch_merge_d(int32_t n, int64_t rows, const void* O, bool in_bf16, const float* L,
+                          void* Oo, bool out_bf16, float* Lo, hipStream_t s) {
+  constexpr int RPB = kThreads / (D / 8);
+  const int64_t blocks = (rows + RPB - 1) / RPB;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 g(static_cast<unsigned>(blocks)), b(kThreads);
+  if (in_bf16 && out_bf16)
+    hipLaunchKernelGGL((merge_kernel<__bf16, __bf16, D>), g, b, 0, s, n, rows,
+                       static_cast<const __bf16*>(O), L, static_cast<__bf16*>(Oo), Lo);
+  else if (in_bf16)
+    hipLaunchKernelGGL((merge_kernel<__bf16, float, D>), g, b, 0, s, n, rows,
+                       static_cast<const __bf16*>(O), L, static_cast<float*>(Oo), Lo);
+  else if (out_bf16)
+    hipLaunchKernelGGL((merge_kernel<float, __bf16, D>), g, b, 0, s, n, rows,
+                       static_cast<const float*>(O), L, static_cast<__bf16*>(Oo), Lo);
+  else
+    hipLaunchKernelGGL((merge_kernel<float, float, D>), g, b, 0, s, n, rows,
+                       static_cast<const float*>(O), L, static_cast<float*>(Oo), Lo);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_merge_split_d(const FwdArgs& a, hipStream_t s) {
+  constexpr int RPB = kThreads / (D / 8);
+  const dim3 g(a.n_split * (kQTile / RPB)), b(kThreads);
+  if (a.o_bf16)
+    hipLaunchKernelGGL((merge_split_kernel<__bf16, D>), g, b, 0, s, a.sched, a.ws_O, a.ws_LSE,
+                       static_cast<__bf16*>(a.O), a.LSE);
+  else
+    hipLaunchKernelGGL((merge_split_kernel<float, D>), g, b, 0, s, a.sched, a.ws_O, a.ws_LSE,
+                       static_cast<float*>(a.O), a.LSE);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge(int32_t n, int64_t rows, int32_t d, const void* O, bool in_bf16,
+                        const float* L, void* Oo, bool out_bf16, float* Lo, hipStream_t s) {
+  return d == 128 ? launch_merge_d<128>(n, rows, O, in_bf16, L, Oo, out_bf16, Lo, s)
+                  : launch_merge_d<64>(n, rows, O, in_bf16, L, Oo, out_bf16, Lo, s);
+}
+
+hipError_t launch_merge_split(const FwdArgs& a, hipStream_t s) {
+  return a.d == 128 ? launch_merge_split_d<128>(a, s) : launch_merge_split_d<64>(a, s);
+}
+
+}  // namespace skv

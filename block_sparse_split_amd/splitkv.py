@@ -1,0 +1,311 @@
+"""Python binding of libsplitkv (argument marshalling only).
+
+Each function has the name of the C entry point it calls and does nothing
+but check shapes/dtypes, take pointers and forward the call; every step of
+the attention path runs in the HIP kernels of ``libsplitkv.so``.  PyTorch is
+used for device memory and streams.  If the library is not built, every call
+raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsplitkv.so")
+
+SKV_F32 = 0
+SKV_BF16 = 1
+SKV_OK = 0
+STATUS_NAMES = {0: "SKV_OK", -1: "SKV_ERR_INVALID_ARG", -2: "SKV_ERR_UNSUPPORTED",
+                -3: "SKV_ERR_HIP", -4: "SKV_ERR_WORKSPACE"}
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+
+
+class SplitKVError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class SkvProblem(ctypes.Structure):
+    _fields_ = [("nb", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("anchors", _i32p), ("lo", _i32p), ("n_chunks", ctypes.c_int32),
+                ("chunk_pos", _i32p), ("chunk_off", _i32p), ("with_draft", ctypes.c_int32)]
+
+
+class SkvScheduleInfo(ctypes.Structure):
+    _fields_ = [("words", ctypes.c_int64), ("n_workgroups", ctypes.c_int32),
+                ("n_tiles", ctypes.c_int32), ("n_qtiles", ctypes.c_int32),
+                ("n_items", ctypes.c_int32), ("n_split_qtiles", ctypes.c_int32),
+                ("n_partial_slots", ctypes.c_int32), ("n_kv_items", ctypes.c_int32),
+                ("reserved", ctypes.c_int32),
+                ("fwd_workspace_bytes", ctypes.c_int64), ("bwd_workspace_bytes", ctypes.c_int64),
+                ("item_cost_total", ctypes.c_int64), ("item_cost_max_bin", ctypes.c_int64),
+                ("kv_cost_total", ctypes.c_int64), ("kv_cost_max_bin", ctypes.c_int64),
+                ("nb", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("n_local", ctypes.c_int32), ("with_draft", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libsplitkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run "
+                           "`python -m block_sparse_split_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.skv_last_error.restype = ctypes.c_char_p
+    L.skv_last_error.argtypes = []
+    L.skv_abi_version.restype = ctypes.c_int32
+    L.skv_chunk_costs.argtypes = [_i32p, _i32p, ctypes.c_int32, _i32p, _i32p, ctypes.c_int32,
+                                  ctypes.c_int32, _i64p]
+    L.skv_plan_lpt_costs.argtypes = [_i64p, ctypes.c_int32, ctypes.c_int32, _i32p, _i64p]
+    L.skv_plan_lpt.argtypes = [_i32p, _i32p, ctypes.c_int32, _i32p, _i32p, ctypes.c_int32,
+                               ctypes.c_int32, ctypes.c_int32, _i32p, _i64p, _i64p]
+    L.skv_schedule_build.argtypes = [ctypes.POINTER(SkvProblem), ctypes.c_int32, _i32p,
+                                     ctypes.c_int64, ctypes.POINTER(SkvScheduleInfo)]
+    L.skv_attn_fwd_partial.argtypes = [ctypes.POINTER(SkvProblem),
+                                       ctypes.POINTER(SkvScheduleInfo), _vp, _vp, _vp, _vp,
+                                       _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int64,
+                                       _vp]
+    L.skv_merge_lse.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _vp,
+                                ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, _vp]
+    L.skv_attn_bwd.argtypes = [ctypes.POINTER(SkvProblem), ctypes.POINTER(SkvScheduleInfo),
+                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _vp, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_int64, _vp]
+    for name in ("skv_chunk_costs", "skv_plan_lpt_costs", "skv_plan_lpt", "skv_schedule_build",
+                 "skv_attn_fwd_partial", "skv_merge_lse", "skv_attn_bwd"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(fn, status):
+    if status != SKV_OK:
+        raise SplitKVError(fn, status, lib().skv_last_error().decode())
+
+
+def _i32(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(_i32p)
+
+
+def _i64(a):
+    a = np.ascontiguousarray(a, dtype=np.int64)
+    return a, a.ctypes.data_as(_i64p)
+
+
+# ---------------------------------------------------------------- planner
+
+def skv_chunk_costs(anchors, lo, chunk_pos, chunk_len, tile_k):
+    a, ap = _i32(anchors)
+    l, lp = _i32(lo)
+    p, pp = _i32(chunk_pos)
+    n, np_ = _i32(chunk_len)
+    out = np.zeros(len(p), np.int64)
+    _check("skv_chunk_costs", lib().skv_chunk_costs(ap, lp, len(a), pp, np_, len(p), tile_k,
+                                                   out.ctypes.data_as(_i64p)))
+    return out
+
+
+def skv_plan_lpt_costs(costs, n_bins):
+    c, cp = _i64(costs)
+    bins = np.zeros(len(c), np.int32)
+    load = np.zeros(n_bins, np.int64)
+    _check("skv_plan_lpt_costs", lib().skv_plan_lpt_costs(
+        cp, len(c), n_bins, bins.ctypes.data_as(_i32p), load.ctypes.data_as(_i64p)))
+    return bins, load
+
+
+def skv_plan_lpt(anchors, lo, chunk_pos, chunk_len, tile_k, n_bins):
+    a, ap = _i32(anchors)
+    l, lp = _i32(lo)
+    p, pp = _i32(chunk_pos)
+    n, np_ = _i32(chunk_len)
+    bins = np.zeros(len(p), np.int32)
+    cost = np.zeros(len(p), np.int64)
+    load = np.zeros(n_bins, np.int64)
+    _check("skv_plan_lpt", lib().skv_plan_lpt(
+        ap, lp, len(a), pp, np_, len(p), tile_k, n_bins, bins.ctypes.data_as(_i32p),
+        cost.ctypes.data_as(_i64p), load.ctypes.data_as(_i64p)))
+    return bins, cost, load
+
+
+# ---------------------------------------------------------------- problem
+
+class Problem:
+    """Host description of one shard's attention problem (skv_problem)."""
+
+    def __init__(self, nb, hq, hkv, d, scale, dtype, anchors, lo, chunk_pos=(),
+                 chunk_off=(0,), with_draft=True):
+        self.anchors, ap = _i32(anchors)
+        self.lo, lp = _i32(lo)
+        self.chunk_pos, cp = _i32(chunk_pos)
+        self.chunk_off, co = _i32(chunk_off)
+        self.dtype = dtype
+        self.c = SkvProblem(nb, hq, hkv, d, scale, dtype, ap, lp, len(self.chunk_pos), cp, co,
+                            int(bool(with_draft)))
+
+    @property
+    def nq(self):
+        return self.c.nb * 16
+
+    @property
+    def n_local(self):
+        return int(self.chunk_off[-1]) if len(self.chunk_off) else 0
+
+
+def skv_schedule_build(problem: Problem, n_workgroups: int = 0):
+    info = SkvScheduleInfo()
+    L = lib()
+    _check("skv_schedule_build", L.skv_schedule_build(ctypes.byref(problem.c), n_workgroups,
+                                                      None, 0, ctypes.byref(info)))
+    image = np.zeros(info.words, np.int32)
+    # build with the workgroup count resolved by the size query
+    _check("skv_schedule_build", L.skv_schedule_build(
+        ctypes.byref(problem.c), info.n_workgroups, image.ctypes.data_as(_i32p), len(image),
+        ctypes.byref(info)))
+    return image, info
+
+
+# ---------------------------------------------------------------- device calls
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SKV_BF16
+    if t.dtype == torch.float32:
+        return SKV_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t, name, dtype=None, shape=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} must not be None")
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _tdtype(code):
+    torch = _torch()
+    return torch.bfloat16 if code == SKV_BF16 else torch.float32
+
+
+def skv_attn_fwd_partial(problem: Problem, info, schedule, Q, K, V, Kd, Vd, O, LSE,
+                         workspace=None, stream=None):
+    torch = _torch()
+    p = problem.c
+    dt = _tdtype(problem.dtype)
+    nq, nl = problem.nq, problem.n_local
+    args = [ctypes.byref(p), ctypes.byref(info),
+            _ptr(schedule, "schedule", torch.int32, (info.words,)),
+            _ptr(Q, "Q", dt, (nq, p.hq, p.d)),
+            _ptr(K, "K", dt, (nl, p.hkv, p.d), allow_none=nl == 0),
+            _ptr(V, "V", dt, (nl, p.hkv, p.d), allow_none=nl == 0),
+            _ptr(Kd, "Kd", dt, (nq, p.hkv, p.d), allow_none=not p.with_draft),
+            _ptr(Vd, "Vd", dt, (nq, p.hkv, p.d), allow_none=not p.with_draft),
+            _ptr(O, "O", None, (nq, p.hq, p.d)), _dtype_code(O),
+            _ptr(LSE, "LSE", torch.float32, (nq, p.hq)),
+            _ptr(workspace, "workspace", None, None, allow_none=True),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _stream(stream)]
+    if not p.with_draft:
+        args[6] = args[7] = None
+    _check("skv_attn_fwd_partial", lib().skv_attn_fwd_partial(*args))
+
+
+def skv_merge_lse(O_parts, LSE_parts, O_out, LSE_out, stream=None):
+    torch = _torch()
+    k = O_parts.shape[0]
+    d = O_parts.shape[-1]
+    rows = O_parts[0].numel() // d
+    _check("skv_merge_lse", lib().skv_merge_lse(
+        k, rows, d, _ptr(O_parts, "O_parts"), _dtype_code(O_parts),
+        _ptr(LSE_parts, "LSE_parts", torch.float32, (k,) + tuple(O_parts.shape[1:-1])),
+        _ptr(O_out, "O_out", None, tuple(O_parts.shape[1:])), _dtype_code(O_out),
+        _ptr(LSE_out, "LSE_out", torch.float32, tuple(O_parts.shape[1:-1])), _stream(stream)))
+
+
+def skv_attn_bwd(problem: Problem, info, schedule, Q, K, V, Kd, Vd, O, dO, LSE, dQ, dK, dV,
+                 dKd, dVd, grad_dtype=SKV_F32, workspace=None, stream=None):
+    torch = _torch()
+    p = problem.c
+    dt = _tdtype(problem.dtype)
+    gt = _tdtype(grad_dtype)
+    nq, nl = problem.nq, problem.n_local
+    nd = not p.with_draft
+    _check("skv_attn_bwd", lib().skv_attn_bwd(
+        ctypes.byref(p), ctypes.byref(info),
+        _ptr(schedule, "schedule", torch.int32, (info.words,)),
+        _ptr(Q, "Q", dt, (nq, p.hq, p.d)),
+        _ptr(K, "K", dt, (nl, p.hkv, p.d), allow_none=nl == 0),
+        _ptr(V, "V", dt, (nl, p.hkv, p.d), allow_none=nl == 0),
+        None if nd else _ptr(Kd, "Kd", dt, (nq, p.hkv, p.d)),
+        None if nd else _ptr(Vd, "Vd", dt, (nq, p.hkv, p.d)),
+        _ptr(O, "O", dt, (nq, p.hq, p.d)), _ptr(dO, "dO", dt, (nq, p.hq, p.d)),
+        _ptr(LSE, "LSE", torch.float32, (nq, p.hq)),
+        _ptr(dQ, "dQ", torch.float32, (nq, p.hq, p.d)),
+        _ptr(dK, "dK", gt, (nl, p.hkv, p.d), allow_none=nl == 0),
+        _ptr(dV, "dV", gt, (nl, p.hkv, p.d), allow_none=nl == 0),
+        None if nd else _ptr(dKd, "dKd", gt, (nq, p.hkv, p.d)),
+        None if nd else _ptr(dVd, "dVd", gt, (nq, p.hkv, p.d)),
+        grad_dtype, _ptr(workspace, "workspace", None, None, allow_none=True),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+class Shard:
+    """A problem with its schedule uploaded and workspaces allocated.
+
+    Convenience wrapper for repeated calls (one schedule per batch serves
+    every layer).  Allocation happens here, never inside the calls."""
+
+    def __init__(self, problem: Problem, device="cuda", n_workgroups: int = 0):
+        torch = _torch()
+        self.problem = problem
+        self.image, self.info = skv_schedule_build(problem, n_workgroups)
+        self.schedule = torch.from_numpy(self.image).to(device)
+        nbytes = max(self.info.fwd_workspace_bytes, self.info.bwd_workspace_bytes, 256)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+    def fwd(self, Q, K, V, Kd, Vd, O, LSE, stream=None):
+        skv_attn_fwd_partial(self.problem, self.info, self.schedule, Q, K, V, Kd, Vd, O, LSE,
+                             self.workspace, stream)
+
+    def bwd(self, Q, K, V, Kd, Vd, O, dO, LSE, dQ, dK, dV, dKd, dVd, grad_dtype=SKV_F32,
+            stream=None):
+        skv_attn_bwd(self.problem, self.info, self.schedule, Q, K, V, Kd, Vd, O, dO, LSE, dQ,
+                     dK, dV, dKd, dVd, grad_dtype, self.workspace, stream)

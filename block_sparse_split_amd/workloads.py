@@ -12,8 +12,10 @@ abstract; rit.work blog, section on why a short query suffices for a long
 context).  Real drafter training data is not available; these seeded inputs
 stand in for it.
 
-Draw order per workload (one ``numpy.random.default_rng(seed)`` stream):
-sequence lengths, anchors, Q, K, V, Kd, Vd, dO.
+Seeds: ``numpy.random.default_rng(seed)`` draws the geometry (sequence
+lengths, then anchors); each tensor comes from its own stream
+``default_rng([seed, tag])`` and each context chunk of K and V from
+``default_rng([seed, tag, chunk])``, so a shard can draw only its own rows.
 """
 from __future__ import annotations
 
@@ -160,34 +162,56 @@ def draw_normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
     return round_to_bf16(x) if dtype == "bf16" else x
 
 
+# Stream tags: every tensor (and every context chunk of K and V) has its own
+# counter-free numpy stream, so any subset of chunks can be drawn alone.
+_TAG = {"Q": 0x51, "K": 0x4B, "V": 0x56, "Kd": 0x4B44, "Vd": 0x5644, "dO": 0x644F}
+
+
+def _rng(seed: int, tag: str, *extra: int) -> np.random.Generator:
+    return np.random.default_rng([seed, _TAG[tag], *extra])
+
+
 @dataclasses.dataclass
 class Tensors:
     Q: np.ndarray            # [Nq, Hq, d]
-    K: np.ndarray            # [ctx, Hkv, d]
-    V: np.ndarray            # [ctx, Hkv, d]
+    K: np.ndarray            # [n_local, Hkv, d]: rows of the drawn chunks
+    V: np.ndarray            # [n_local, Hkv, d]
     Kd: np.ndarray           # [Nq, Hkv, d] draft-block keys
     Vd: np.ndarray           # [Nq, Hkv, d]
     dO: Optional[np.ndarray]  # [Nq, Hq, d]
+    chunk_ids: np.ndarray    # chunks whose rows K/V hold, in order
 
 
-def draw_tensors(w: Workload, g: Geometry, rng: np.random.Generator,
-                 with_grad: bool = False, ctx_rows: Optional[int] = None) -> Tensors:
-    n = g.ctx if ctx_rows is None else ctx_rows
-    Q = draw_normal(rng, (w.nq, w.hq, w.d), w.dtype)
-    K = draw_normal(rng, (n, w.hkv, w.d), w.dtype)
-    V = draw_normal(rng, (n, w.hkv, w.d), w.dtype)
-    Kd = draw_normal(rng, (w.nq, w.hkv, w.d), w.dtype)
-    Vd = draw_normal(rng, (w.nq, w.hkv, w.d), w.dtype)
-    dO = draw_normal(rng, (w.nq, w.hq, w.d), w.dtype) if with_grad else None
-    return Tensors(Q, K, V, Kd, Vd, dO)
+def draw_kv_chunks(w: Workload, g: Geometry, seed: int, chunk_ids, tag: str) -> np.ndarray:
+    parts = [draw_normal(_rng(seed, tag, int(c)), (int(g.chunk_len[c]), w.hkv, w.d), w.dtype)
+             for c in chunk_ids]
+    if not parts:
+        return np.zeros((0, w.hkv, w.d), np.float32)
+    return np.concatenate(parts, axis=0)
 
 
-def make(name_or_w, seed: int, with_grad: bool = False, tensors: bool = True):
+def draw_tensors(w: Workload, g: Geometry, seed: int, with_grad: bool = False,
+                 chunk_ids=None) -> Tensors:
+    """Q, Kd, Vd (and dO) for all draft queries; K, V for the given chunks
+    (default: every chunk, i.e. the whole packed context in order)."""
+    if chunk_ids is None:
+        chunk_ids = np.arange(len(g.chunk_pos))
+    chunk_ids = np.asarray(chunk_ids, np.int64)
+    Q = draw_normal(_rng(seed, "Q"), (w.nq, w.hq, w.d), w.dtype)
+    K = draw_kv_chunks(w, g, seed, chunk_ids, "K")
+    V = draw_kv_chunks(w, g, seed, chunk_ids, "V")
+    Kd = draw_normal(_rng(seed, "Kd"), (w.nq, w.hkv, w.d), w.dtype)
+    Vd = draw_normal(_rng(seed, "Vd"), (w.nq, w.hkv, w.d), w.dtype)
+    dO = draw_normal(_rng(seed, "dO"), (w.nq, w.hq, w.d), w.dtype) if with_grad else None
+    return Tensors(Q, K, V, Kd, Vd, dO, chunk_ids)
+
+
+def make(name_or_w, seed: int, with_grad: bool = False, tensors: bool = True,
+         chunk_ids=None):
     """Geometry (+ tensors) of a named workload for a given seed."""
     w = WORKLOADS[name_or_w] if isinstance(name_or_w, str) else name_or_w
-    rng = np.random.default_rng(seed)
-    g = draw_geometry(w, rng)
-    t = draw_tensors(w, g, rng, with_grad) if tensors else None
+    g = draw_geometry(w, np.random.default_rng(seed))
+    t = draw_tensors(w, g, seed, with_grad, chunk_ids) if tensors else None
     return w, g, t
 
 

@@ -1,0 +1,232 @@
+/*
+ * libsplitkv — Split-KV draft cross-attention on one AMD Instinct MI355X
+ * (CDNA4, gfx950).
+ *
+ * The method (arXiv abstract of "Split-KV: Efficient Context Parallelism for
+ * Training Diffusion Drafters"; rit.work blog post on Split-KV, sections
+ * "A short query sufficed for a long context" and "Split-KV moves queries,
+ * not keys and values"):
+ *   - a short set of draft queries, built in blocks of 16 tokens around
+ *     anchor positions sampled in the responses, attends to a much longer
+ *     context through a block-sparse mask;
+ *   - context keys/values stay on the participant that holds them; every
+ *     participant sees the full query set, computes the attention of all
+ *     queries over its local keys, and the per-participant results are
+ *     combined exactly by reconciling the softmax normaliser;
+ *   - the cost of each context chunk is known before the step, and chunks
+ *     are placed longest-processing-time-first (LPT) on the least-loaded
+ *     participant.
+ *
+ * Mask (the reading this library implements): anchor block i (draft query
+ * rows 16i .. 16i+15) sees the context keys at absolute positions
+ * lo[i] <= j < anchors[i] and the 16 draft keys of its own block (rows
+ * 16i .. 16i+15 of Kd/Vd) in both directions.  Query head h reads kv head
+ * h / (hq / hkv).
+ *
+ * Conventions
+ *   - Every call returns an skv_status; SKV_OK is 0, errors are negative.
+ *     skv_last_error() returns a description of the last failure on the
+ *     calling thread.  No call aborts the process.
+ *   - Device pointers are HIP device addresses.  The caller owns every
+ *     buffer; the library allocates no device memory.  Scratch space is the
+ *     caller's `workspace` of the size the schedule reports.
+ *   - Device calls are asynchronous on the caller's stream (`stream` is a
+ *     hipStream_t passed as void*; NULL is the default stream).  Launch
+ *     errors are returned as SKV_ERR_HIP.  Host calls are synchronous.
+ *   - Tensors are dense, row-major, 16-byte aligned:
+ *       Q, O, dO, dQ   [Nq, hq, d]       (Nq = 16 * nb, token-major)
+ *       LSE            [Nq, hq]          fp32, natural log
+ *       K, V, dK, dV   [n_local, hkv, d] (local key rows of the shard)
+ *       Kd, Vd, dKd... [Nq, hkv, d]      (draft-block keys/values)
+ *   - dtypes: SKV_BF16 (bfloat16) or SKV_F32.  d is 64 or 128.  hq must be
+ *     a multiple of hkv with hq / hkv in {1, 2, 4, 8, 16}.
+ *   - The library keeps no state across calls except a per-device cache of
+ *     the compute-unit count; it is safe to call from several threads.
+ */
+#ifndef SPLITKV_H
+#define SPLITKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SKV_OK = 0,
+  SKV_ERR_INVALID_ARG = -1,   /* bad pointer, size, layout or value */
+  SKV_ERR_UNSUPPORTED = -2,   /* valid but not implemented (d, dtype, G) */
+  SKV_ERR_HIP = -3,           /* a HIP runtime call or launch failed */
+  SKV_ERR_WORKSPACE = -4,     /* workspace or schedule buffer too small */
+} skv_status;
+
+typedef enum { SKV_F32 = 0, SKV_BF16 = 1 } skv_dtype;
+
+/* Last error text on this thread ("" after a successful call). */
+const char* skv_last_error(void);
+
+/* ABI version of this header (bumped on incompatible changes). */
+int32_t skv_abi_version(void);
+#define SKV_ABI_VERSION 1
+
+/* ------------------------------------------------------------------------
+ * Planner (host only, synchronous, deterministic).
+ * ---------------------------------------------------------------------- */
+
+/* Realised cost of each context chunk (arXiv abstract: chunks are balanced
+ * by their realised attention cost, computable in advance from the global
+ * query view; rit.work blog, section "Split-KV moves queries, not keys and
+ * values").  Chunk c covers absolute keys [chunk_pos[c], chunk_pos[c] +
+ * chunk_len[c]) and is cut into key tiles of tile_k keys from its first key
+ * (the last tile may be short).  cost[c] counts the (anchor block, key tile)
+ * pairs where the tile holds at least one key in [lo[i], anchors[i]).
+ *   anchors, lo: host int32 [nb];  chunk_pos, chunk_len: host int32
+ *   [n_chunks], chunk_len >= 1;  tile_k >= 1;  out_cost: host int64
+ *   [n_chunks].  Errors: SKV_ERR_INVALID_ARG on NULL or bad sizes. */
+skv_status skv_chunk_costs(const int32_t* anchors, const int32_t* lo,
+                           int32_t nb, const int32_t* chunk_pos,
+                           const int32_t* chunk_len, int32_t n_chunks,
+                           int32_t tile_k, int64_t* out_cost);
+
+/* LPT placement of n jobs with costs cost[n] >= 0 on n_bins bins (same
+ * sources as above: most expensive first, each to the least-loaded bin).
+ * Ties: equal costs in increasing job index, equal loads to the lowest bin.
+ *   out_bin: host int32 [n];  out_load: host int64 [n_bins] or NULL.
+ *   n may be 0.  Errors: SKV_ERR_INVALID_ARG on NULL, n_bins < 1 or a
+ *   negative cost. */
+skv_status skv_plan_lpt_costs(const int64_t* cost, int32_t n, int32_t n_bins,
+                              int32_t* out_bin, int64_t* out_load);
+
+/* skv_chunk_costs followed by skv_plan_lpt_costs: the chunk -> bin plan of
+ * a context-parallel split (bins = participants) or of chunks over compute
+ * units.  out_cost [n_chunks] and out_load [n_bins] may be NULL. */
+skv_status skv_plan_lpt(const int32_t* anchors, const int32_t* lo, int32_t nb,
+                        const int32_t* chunk_pos, const int32_t* chunk_len,
+                        int32_t n_chunks, int32_t tile_k, int32_t n_bins,
+                        int32_t* out_bin, int64_t* out_cost,
+                        int64_t* out_load);
+
+/* ------------------------------------------------------------------------
+ * Problem description and the in-GPU work schedule.
+ * ---------------------------------------------------------------------- */
+
+/* One participant's view: the full draft-query set and one local shard of
+ * context chunks (rit.work blog, section "Split-KV moves queries, not keys
+ * and values": every participant gathers all queries and keeps its own
+ * keys/values).  All pointers are HOST pointers; the schedule builder copies
+ * what the kernels need into the schedule image. */
+typedef struct skv_problem {
+  int32_t nb;              /* anchor blocks; Nq = 16 * nb                   */
+  int32_t hq, hkv, d;      /* heads and head dim                            */
+  float scale;             /* softmax scale on q.k, > 0                     */
+  int32_t dtype;           /* skv_dtype of Q, K, V, Kd, Vd, O, dO           */
+  const int32_t* anchors;  /* [nb] exclusive bound of block i's context     */
+  const int32_t* lo;       /* [nb] first context key block i may see        */
+  int32_t n_chunks;        /* chunks held by this shard (may be 0)          */
+  const int32_t* chunk_pos;/* [n_chunks] absolute position of the first key */
+  const int32_t* chunk_off;/* [n_chunks+1] local rows: chunk c is K rows    */
+                           /*   chunk_off[c] .. chunk_off[c+1]-1; [0] == 0  */
+  int32_t with_draft;      /* 1 if this shard adds the draft-block keys     */
+} skv_problem;
+
+/* Summary of a schedule image, filled by skv_schedule_build. */
+typedef struct skv_schedule_info {
+  int64_t words;               /* int32 words of the image                  */
+  int32_t n_workgroups;        /* persistent workgroups (bins)              */
+  int32_t n_tiles;             /* 64-key tiles of the shard                 */
+  int32_t n_qtiles;            /* 256-row query tiles (all kv heads)        */
+  int32_t n_items;             /* forward / dQ work items                   */
+  int32_t n_split_qtiles;      /* query tiles cut into several items        */
+  int32_t n_partial_slots;     /* partial (O, LSE) slots for those tiles    */
+  int32_t n_kv_items;          /* backward dK/dV work items                 */
+  int32_t reserved;
+  int64_t fwd_workspace_bytes; /* workspace for skv_attn_fwd_partial        */
+  int64_t bwd_workspace_bytes; /* workspace for skv_attn_bwd                */
+  int64_t item_cost_total;     /* sum of forward item costs                 */
+  int64_t item_cost_max_bin;   /* largest workgroup load (forward items)    */
+  int64_t kv_cost_total;       /* same for the dK/dV items                  */
+  int64_t kv_cost_max_bin;
+  /* geometry the image was built for (checked by the device calls) */
+  int32_t nb, hq, hkv, d, n_local, with_draft;
+} skv_schedule_info;
+
+/* Build the work schedule of one problem for n_workgroups persistent
+ * workgroups (0 = the current device's compute-unit count; this call then
+ * queries the device).  Forward work is cut into items (kv head, 256-row
+ * query tile, run of visible 64-key tiles); item cost counts visible
+ * (anchor block, key tile) pairs as in skv_chunk_costs, and items are
+ * placed by LPT on workgroups.  Work of one kv head is kept on the
+ * workgroups of the same XCD class so its keys/values share an L2.
+ * Backward dK/dV items are (kv head, 64-key tile) placed the same way.
+ *   image: host int32 buffer of capacity_words, or NULL to only fill
+ *   `info` (size query).  The caller copies the image to device memory
+ *   and passes that copy, with `info`, to the device calls below.  The
+ *   schedule stays valid for every layer that shares the anchors and the
+ *   shard (the mask does not change across layers).
+ * Errors: SKV_ERR_INVALID_ARG, SKV_ERR_UNSUPPORTED, SKV_ERR_WORKSPACE
+ * (image too small; info->words says how much is needed). */
+skv_status skv_schedule_build(const skv_problem* p, int32_t n_workgroups,
+                              int32_t* image, int64_t capacity_words,
+                              skv_schedule_info* info);
+
+/* ------------------------------------------------------------------------
+ * Device calls.
+ * ---------------------------------------------------------------------- */
+
+/* Forward partial attention of all draft queries over this shard's keys
+ * (rit.work blog, section "Split-KV moves queries, not keys and values":
+ * each participant computes the local parts of attention for the whole
+ * query set).  Writes O [Nq, hq, d] (o_dtype, normalised by this shard's
+ * own softmax sum) and LSE [Nq, hq] fp32, the natural-log normaliser of
+ * this shard.  Rows that see no key of this shard get O = 0, LSE = -inf.
+ * With with_draft = 0, Kd/Vd are ignored and may be NULL.
+ *   schedule: device copy of the image built for exactly this problem.
+ *   workspace: device buffer of >= info->fwd_workspace_bytes (may be NULL
+ *   when that is 0).  Errors: SKV_ERR_INVALID_ARG (mismatch with info,
+ *   NULL), SKV_ERR_WORKSPACE, SKV_ERR_UNSUPPORTED, SKV_ERR_HIP. */
+skv_status skv_attn_fwd_partial(const skv_problem* p,
+                                const skv_schedule_info* info,
+                                const int32_t* schedule, const void* Q,
+                                const void* K, const void* V, const void* Kd,
+                                const void* Vd, void* O, int32_t o_dtype,
+                                float* LSE, void* workspace,
+                                int64_t workspace_bytes, void* stream);
+
+/* Exact merge of n_parts partial results (rit.work blog, section "Split-KV
+ * moves queries, not keys and values": participants reconcile the
+ * normalisation; the split reproduces single-device attention exactly).
+ *   O_parts [n_parts, rows, d] (in_dtype), LSE_parts [n_parts, rows] fp32;
+ *   O_out [rows, d] (out_dtype), LSE_out [rows] fp32.  rows = Nq * hq.
+ *   LSE = M + ln sum_k exp(LSE_k - M), M = max_k LSE_k; O = sum_k
+ *   exp(LSE_k - LSE) O_k.  Partials with LSE_k = -inf weigh zero; a row
+ *   with no finite LSE_k gets O = 0, LSE = -inf.  O_out may not alias the
+ *   inputs.  Errors: SKV_ERR_INVALID_ARG, SKV_ERR_UNSUPPORTED, SKV_ERR_HIP. */
+skv_status skv_merge_lse(int32_t n_parts, int64_t rows, int32_t d,
+                         const void* O_parts, int32_t in_dtype,
+                         const float* LSE_parts, void* O_out,
+                         int32_t out_dtype, float* LSE_out, void* stream);
+
+/* Backward of this shard (rit.work blog, section "Split-KV moves queries,
+ * not keys and values": only the queries and their gradients cross
+ * participants; key/value gradients stay local).  With the FINAL merged
+ * output O and normaliser LSE of the whole context:
+ *   dQ  [Nq, hq, d] fp32: this shard's share of the query gradient
+ *       (shares over shards sum to the full dQ); overwritten.
+ *   dK, dV [n_local, hkv, d] (grad_dtype): gradients of the local keys.
+ *   dKd, dVd [Nq, hkv, d] (grad_dtype): draft-key gradients, only with
+ *       with_draft = 1 (else ignored, may be NULL).
+ *   workspace: >= info->bwd_workspace_bytes.
+ * Errors as skv_attn_fwd_partial. */
+skv_status skv_attn_bwd(const skv_problem* p, const skv_schedule_info* info,
+                        const int32_t* schedule, const void* Q, const void* K,
+                        const void* V, const void* Kd, const void* Vd,
+                        const void* O, const void* dO, const float* LSE,
+                        float* dQ, void* dK, void* dV, void* dKd, void* dVd,
+                        int32_t grad_dtype, void* workspace,
+                        int64_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPLITKV_H */

@@ -1,0 +1,246 @@
+"""CPU checks of the C-ABI library: exports, argument errors, the planner
+(bit-exact against the oracle) and the in-GPU schedule (coverage and LPT
+placement re-derived with the oracle).  No device call is made here."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from block_sparse_split_amd import splitkv as skv
+from block_sparse_split_amd import workloads as wl
+from block_sparse_split_amd import shards
+from block_sparse_split_amd.csrc_layout import (H, T_WORDS, I_WORDS, S_WORDS, K_WORDS,
+                                                QTILE, TILE_K, BLOCK)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "splitkv.h")
+
+
+def test_library_exports_every_declared_symbol():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:const char\*|int32_t|skv_status)\s+(skv_\w+)\(",
+                              text, re.M))
+    assert {"skv_plan_lpt", "skv_attn_fwd_partial", "skv_merge_lse",
+            "skv_attn_bwd"} <= declared
+    out = subprocess.run(["nm", "-D", "--defined-only", skv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (skv_\w+)$", out, re.M))
+    assert declared <= exported, declared - exported
+    L = skv.lib()
+    for name in declared:
+        assert hasattr(L, name)
+    assert L.skv_abi_version() == 1
+
+
+def test_invalid_arguments_return_status_codes():
+    L = skv.lib()
+    assert L.skv_plan_lpt_costs(None, 3, 2, None, None) == -1
+    assert b"NULL" in L.skv_last_error()
+    with pytest.raises(skv.SplitKVError) as e:
+        skv.skv_plan_lpt_costs([1, -2, 3], 2)
+    assert e.value.status == -1
+    with pytest.raises(skv.SplitKVError):
+        skv.skv_plan_lpt_costs([1, 2], 0)
+    with pytest.raises(skv.SplitKVError):
+        skv.skv_chunk_costs([5], [0], [0], [0], 4)  # empty chunk
+    with pytest.raises(skv.SplitKVError):
+        skv.skv_chunk_costs([5], [6], [0], [4], 4)  # lo > anchor
+    # problem validation
+    base = dict(nb=1, hq=4, hkv=2, d=128, scale=0.1, dtype=skv.SKV_BF16, anchors=[10],
+                lo=[0], chunk_pos=[0], chunk_off=[0, 64])
+    for bad, status in [(dict(hq=3), -1), (dict(hq=6, hkv=2), -2), (dict(d=96), -2),
+                        (dict(scale=0.0), -1), (dict(dtype=7), -2),
+                        (dict(chunk_off=[1, 64]), -1),
+                        (dict(chunk_pos=[0, 32], chunk_off=[0, 64, 128]), -1)]:
+        kw = dict(base, **bad)
+        with pytest.raises(skv.SplitKVError) as e:
+            skv.skv_schedule_build(skv.Problem(**kw), 8)
+        assert e.value.status == status, bad
+    # merge argument checks need no device
+    assert L.skv_merge_lse(0, 4, 128, None, 1, None, None, 1, None, None) == -1
+    assert L.skv_merge_lse(2, 4, 96, None, 1, None, None, 1, None, None) == -2
+    assert L.skv_merge_lse(2, 0, 128, None, 1, None, None, 1, None, None) == 0
+
+
+def test_error_text_clears_after_success():
+    L = skv.lib()
+    L.skv_plan_lpt_costs(None, 3, 2, None, None)
+    skv.skv_plan_lpt_costs([1, 2, 3], 2)
+    assert L.skv_last_error() == b""
+
+
+@pytest.mark.parametrize("name,seed", [("tiny_f32_ctx1k", 0), ("tiny_f32_ctx1k", 5),
+                                       ("ctx32k_q2k", 1), ("cp64_rank0_ctx512k", 2),
+                                       ("varlen8_fwdbwd", 3), ("ctx1m_merge64", 4)])
+def test_chunk_costs_and_lpt_bit_exact_vs_oracle(name, seed):
+    w, g, _ = wl.make(name, seed, tensors=False)
+    bins_list = [w.n_shards, 256] if w.n_shards > 1 else [256, 64]
+    c_lib = skv.skv_chunk_costs(g.anchors, g.lo, g.chunk_pos, g.chunk_len, w.tile_k)
+    c_or = oracle.chunk_costs(g.anchors, g.lo, g.chunk_pos, g.chunk_len, w.tile_k)
+    np.testing.assert_array_equal(c_lib, c_or)
+    for m in bins_list:
+        b_lib, cost, load = skv.skv_plan_lpt(g.anchors, g.lo, g.chunk_pos, g.chunk_len,
+                                            w.tile_k, m)
+        b_or, load_or = oracle.plan_lpt(c_or, m)
+        np.testing.assert_array_equal(b_lib, b_or)
+        np.testing.assert_array_equal(load, load_or)
+        np.testing.assert_array_equal(cost, c_or)
+
+
+def test_lpt_costs_random_bit_exact():
+    rng = np.random.default_rng(0)
+    for _ in range(50):
+        n = int(rng.integers(0, 300))
+        m = int(rng.integers(1, 40))
+        costs = rng.integers(0, int(rng.integers(1, 50)), size=n)  # many ties
+        b, ld = skv.skv_plan_lpt_costs(costs, m)
+        bo, lo_ = oracle.plan_lpt(costs, m)
+        np.testing.assert_array_equal(b, bo)
+        np.testing.assert_array_equal(ld, lo_)
+
+
+def test_lpt_deterministic_across_calls():
+    w, g, _ = wl.make("ctx1m_merge64", 4, tensors=False)
+    a = skv.skv_plan_lpt(g.anchors, g.lo, g.chunk_pos, g.chunk_len, 64, 256)
+    b = skv.skv_plan_lpt(g.anchors, g.lo, g.chunk_pos, g.chunk_len, 64, 256)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+# ------------------------------------------------------------------ schedule
+
+def _decode(image):
+    h = {k: int(image[v]) for k, v in H.items()}
+    tiles = image[h["OFF_TILES"]: h["OFF_TILES"] + h["NTILES"] * T_WORDS].reshape(-1, T_WORDS)
+    items = image[h["OFF_ITEMS"]: h["OFF_ITEMS"] + h["NITEMS"] * I_WORDS].reshape(-1, I_WORDS)
+    qoff = image[h["OFF_QOFF"]: h["OFF_QOFF"] + h["NWG"] + 1]
+    queue = image[h["OFF_QUEUE"]: h["OFF_QUEUE"] + h["NITEMS"]]
+    split = image[h["OFF_SPLIT"]: h["OFF_SPLIT"] + h["NSPLIT"] * S_WORDS].reshape(-1, S_WORDS)
+    kv = image[h["OFF_KV"]: h["OFF_KV"] + h["NKV"] * K_WORDS].reshape(-1, K_WORDS)
+    kvqoff = image[h["OFF_KVQOFF"]: h["OFF_KVQOFF"] + h["NWG"] + 1]
+    kvqueue = image[h["OFF_KVQUEUE"]: h["OFF_KVQUEUE"] + h["NKV"]]
+    return h, tiles, items, qoff, queue, split, kv, kvqoff, kvqueue
+
+
+def _check_lpt_per_class(costs, heads, qoff, queue, n_wg, n_cls):
+    """Re-derive the per-XCD-class LPT with the oracle and compare queues."""
+    per = n_wg // n_cls
+    for c in range(n_cls):
+        ids = np.nonzero(heads % n_cls == c)[0]
+        bins, _ = oracle.plan_lpt(costs[ids], per)
+        order = sorted(range(len(ids)), key=lambda j: (-int(costs[ids[j]]), j))
+        want = {c + b * n_cls: [] for b in range(per)}
+        for j in order:
+            want[c + int(bins[j]) * n_cls].append(int(ids[j]))
+        for wgi, lst in want.items():
+            assert queue[qoff[wgi]:qoff[wgi + 1]].tolist() == lst
+
+
+def _schedule_case(name, seed, shard_of=None, n_wg=256, **over):
+    w = wl.scaled(wl.WORKLOADS[name], **over) if over else wl.WORKLOADS[name]
+    w, g, _ = wl.make(w, seed, tensors=False)
+    if shard_of is None:
+        prob = shards.whole_context_problem(w, g)
+        pos = np.arange(g.ctx)
+    else:
+        ids, _, _, _ = shards.lpt_shards(w, g, w.n_shards)
+        chunk_ids = ids[shard_of]
+        prob = shards.shard_problem(w, g, chunk_ids, shard_of == 0)
+        pos = shards.shard_rows(g, chunk_ids)
+    image, info = skv.skv_schedule_build(prob, n_wg)
+    return w, g, prob, pos, image, info
+
+
+@pytest.mark.parametrize("case", [
+    ("ctx32k_q2k", 1, None, 256, {}),
+    ("ctx32k_q2k", 2, None, 40, dict(ctx=4096, anchor_lo=512, anchor_hi=4096, blocks_per_seq=16)),
+    ("varlen8_fwdbwd", 3, None, 256, dict(len_median=2048, len_min=512, len_max=8192)),
+    ("cp64_rank0_ctx512k", 2, 0, 256, {}),
+    ("cp64_rank0_ctx512k", 2, 5, 256, {}),
+    ("tiny_f32_ctx1k", 0, 1, 8, {}),
+    ("tiny_f32_ctx1k", 0, 0, 3, {}),
+])
+def test_schedule_covers_visible_work_once_and_is_lpt(case):
+    name, seed, shard_of, n_wg, over = case
+    w, g, prob, pos, image, info = _schedule_case(name, seed, shard_of, n_wg, **over)
+    h, tiles, items, qoff, queue, split, kv, kvqoff, kvqueue = _decode(image)
+    assert h["MAGIC"] == 0x314B5653 and h["NWG"] == n_wg
+    G = w.hq // w.hkv
+    # tiles: sorted, non-overlapping, rows map to the right absolute keys
+    assert np.all(np.diff(tiles[:, 1]) > 0)
+    for t in tiles:
+        assert np.array_equal(pos[t[0]:t[0] + t[2]], np.arange(t[1], t[1] + t[2]))
+    assert tiles[:, 2].sum() == len(pos)
+    # every (kv head, query tile, visible tile) appears in exactly one item
+    rows = w.nq * G
+    qtph = -(-rows // QTILE)
+    seen = np.zeros((w.hkv, qtph, len(tiles)), np.int32)
+    draft_seen = np.zeros((w.hkv, qtph), np.int32)
+    for it in items:
+        hd, qt, t0, t1, slot, flags, cost = it[:7]
+        seen[hd, qt, t0:t1] += 1
+        draft_seen[hd, qt] += flags & 1
+        # the item cost is the oracle's pair count over its tiles (+ draft)
+        b0 = qt * (QTILE // G) // BLOCK
+        b1 = min(w.nb, -(-((qt + 1) * (QTILE // G)) // BLOCK))
+        want = sum(oracle.tile_pairs_visible(g.anchors[b0:b1], g.lo[b0:b1], tiles[t, 1],
+                                             tiles[t, 1] + tiles[t, 2]) for t in range(t0, t1))
+        want += (b1 - b0) if flags & 1 else 0
+        assert cost == want
+    for qt in range(qtph):
+        b0 = qt * (QTILE // G) // BLOCK
+        b1 = min(w.nb, -(-((qt + 1) * (QTILE // G)) // BLOCK))
+        vis = np.array([oracle.tile_pairs_visible(g.anchors[b0:b1], g.lo[b0:b1], t[1],
+                                                  t[1] + t[2]) > 0 for t in tiles], bool)
+        for hd in range(w.hkv):
+            assert np.array_equal(seen[hd, qt] > 0, vis)
+            assert seen[hd, qt].max(initial=0) <= 1
+            assert draft_seen[hd, qt] == int(prob.c.with_draft)
+    # every query tile has at least one item; split tiles own consecutive slots
+    per_qt = {}
+    for it in items:
+        per_qt.setdefault((it[0], it[1]), []).append(it[4])
+    assert len(per_qt) == w.hkv * qtph
+    nsl = 0
+    for s in split:
+        slots = sorted(per_qt[(s[0], s[1])])
+        assert slots == list(range(s[2], s[2] + s[3]))
+        nsl += s[3]
+    assert nsl == info.n_partial_slots
+    for k, v in per_qt.items():
+        if len(v) == 1:
+            assert v[0] == -1
+    # queues: each item once, LPT per XCD class re-derived by the oracle
+    assert sorted(queue.tolist()) == list(range(len(items)))
+    _check_lpt_per_class(items[:, 6].astype(np.int64), items[:, 0], qoff, queue, n_wg,
+                         h["NCLASS"])
+    _check_lpt_per_class(kv[:, 7].astype(np.int64), kv[:, 0], kvqoff, kvqueue, n_wg,
+                         h["NCLASS"])
+    loads = np.zeros(n_wg, np.int64)
+    for wgi in range(n_wg):
+        loads[wgi] = items[queue[qoff[wgi]:qoff[wgi + 1]], 6].sum()
+    assert loads.max() == info.item_cost_max_bin and loads.sum() == info.item_cost_total
+    # dK/dV items cover every tile once per kv head (+ draft groups)
+    for hd in range(w.hkv):
+        cover = np.zeros(len(tiles), np.int32)
+        dcover = np.zeros(w.nq, np.int32)
+        for k in kv[kv[:, 0] == hd]:
+            cover[k[1]:k[1] + k[2]] += 1
+            dcover[k[3]:k[3] + k[4]] += 1
+            for t in range(k[1], k[1] + k[2]):
+                vb = np.nonzero((np.maximum(g.lo, tiles[t, 1]) <
+                                 np.minimum(g.anchors, tiles[t, 1] + tiles[t, 2])))[0]
+                if vb.size:
+                    assert k[5] <= vb.min() and vb.max() < k[6]
+        assert np.all(cover == 1)
+        assert np.all(dcover == int(prob.c.with_draft))
+
+
+def test_in_gpu_item_plan_imbalance_32k():
+    """Item-level LPT over 256 workgroups at the 32K context."""
+    w, g, prob, pos, image, info = _schedule_case("ctx32k_q2k", 1, None, 256)
+    imb = info.item_cost_max_bin / (info.item_cost_total / 256) - 1
+    assert imb < 0.05, imb
