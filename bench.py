@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the Split-KV draft cross-attention hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input
+already resident in HBM: forward partial attention with its in-library
+merge of split query tiles, then the backward (rowsum(dO*O), dQ, dK/dV).
+The schedule (chunk costs + LPT placement of work items on the persistent
+workgroups) is built once per batch before the timed region, as the pages
+describe the plan being built in advance; its host time is reported apart.
+
+Workload: 32K-token context, 2048 draft queries (128 anchor blocks of 16,
+anchors uniform in [8192, 32768)), GQA 32 query / 8 kv heads, d = 128,
+bf16 N(0,1) inputs, KV chunks of 256, 256 CU bins.
+
+FLOPs are realised-mask: every visible (query row, key) pair counts 4*d per
+query head in the forward and 10*d in the backward (5 GEMMs), draft keys
+included; masked-tile waste is not credited.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "masked-attn TFLOP/s fwd & fwd+bwd, % of MFMA peak; LPT imbalance %"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def visible_elements(g, hq):
+    """Visible (query row x head, key) pairs: context keys [lo, a) + 16 draft keys."""
+    per_block = (g.anchors.astype(np.int64) - g.lo.astype(np.int64)) + 16
+    return int(per_block.sum()) * 16 * hq
+
+
+def cpu_baseline(w, g, t, target_s=15.0):
+    """The fp64 oracle (as it stands) on a bounded sample of anchor blocks,
+    forward + backward, timed on this host's cores."""
+    import oracle
+    from block_sparse_split_amd import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    scale = wl.softmax_scale(w.d)
+    nb = len(g.anchors)
+    pos = np.arange(g.ctx)
+
+    def run(blocks):
+        O = np.zeros((w.nq, w.hq, w.d))
+        L = np.full((w.nq, w.hq), -np.inf)
+        t0 = time.perf_counter()
+        Ob, Lb = oracle.attention(t.Q, t.K, t.V, t.Kd, t.Vd, g.anchors, g.lo, scale,
+                                  blocks=blocks)
+        for k, b in enumerate(blocks):
+            O[16 * b:16 * b + 16] = Ob[16 * k:16 * k + 16]
+            L[16 * b:16 * b + 16] = Lb[16 * k:16 * k + 16]
+        oracle.attention_bwd(t.Q, t.K, t.V, pos, g.anchors, g.lo, scale, O, t.dO, L, t.Kd,
+                             t.Vd, blocks=blocks)
+        return time.perf_counter() - t0
+
+    probe = [nb // 2]
+    t1 = run(probe)
+    n = int(max(1, min(nb, target_s / max(t1, 1e-3))))
+    blocks = sorted(set(np.linspace(0, nb - 1, n).astype(int).tolist()))
+    dt = run(blocks)
+    per_block = (g.anchors[blocks].astype(np.int64) - g.lo[blocks] + 16).sum() * 16 * w.hq
+    flops = 14.0 * w.d * per_block
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 oracle forward+backward of {len(blocks)} of {nb} anchor blocks "
+                      f"(all {w.hq} query heads), {dt:.1f} s wall"}
+
+
+def traffic_for(kernel, workload, src_hash):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if
+    they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != src_hash:
+        return None
+    try:
+        return float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_split_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ctx32k_q2k")
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="time the forward alone (diagnostic; not the benchmark step)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_split_amd import splitkv as skv
+    from block_sparse_split_amd import shards
+    from block_sparse_split_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    skv.lib()  # fail loudly if the HIP library is not built
+
+    w, g, t = wl.make(args.workload, args.seed, with_grad=True)
+    log(f"workload {w.name}: ctx {g.ctx}, nb {w.nb}, hq {w.hq}, hkv {w.hkv}, d {w.d}")
+    prob = shards.whole_context_problem(w, g)
+    plan_times = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        image, info = skv.skv_schedule_build(prob, 0)
+        plan_times.append(time.perf_counter() - t0)
+    sh = skv.Shard(prob)
+    n_wg = sh.info.n_workgroups
+    chunk_bins, chunk_cost, chunk_load = skv.skv_plan_lpt(g.anchors, g.lo, g.chunk_pos,
+                                                          g.chunk_len, w.tile_k, n_wg)
+    dev = "cuda"
+    to = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    Q, K, V, Kd, Vd, dO = (to(x) for x in (t.Q, t.K, t.V, t.Kd, t.Vd, t.dO))
+    O = torch.empty((w.nq, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+    LSE = torch.empty((w.nq, w.hq), dtype=torch.float32, device=dev)
+    dQ = torch.empty((w.nq, w.hq, w.d), dtype=torch.float32, device=dev)
+    dK = torch.empty_like(K)
+    dV = torch.empty_like(V)
+    dKd = torch.empty_like(Kd)
+    dVd = torch.empty_like(Vd)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sh.fwd(Q, K, V, Kd, Vd, O, LSE, stream)
+        if not args.fwd_only:
+            sh.bwd(Q, K, V, Kd, Vd, O, dO, LSE, dQ, dK, dV, dKd, dVd, skv.SKV_BF16, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    skv.skv_timing_collect()  # discard anything recorded before
+    skv.skv_timing_enable(True)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    skv.skv_timing_enable(False)
+    kernels = skv.skv_timing_collect()
+    ms = start.elapsed_time(stop) / args.steps
+    log(f"{ms:.3f} ms/step")
+
+    E = visible_elements(g, w.hq)
+    fwd_flops = 4.0 * w.d * E
+    bwd_flops = 10.0 * w.d * E
+    step_flops = fwd_flops + (0 if args.fwd_only else bwd_flops)
+    algo = {"fwd_bf16": ("mfma", fwd_flops), "bwd_dkdv": ("mfma", 8.0 * w.d * E),
+            "bwd_dq": ("mfma", 2.0 * w.d * E)}
+    per_kernel = {}
+    for name, (cnt, tot) in kernels.items():
+        per_kernel[name] = {"launches": cnt, "avg_ms": tot / cnt,
+                            "share_of_step": (tot / args.steps) / ms}
+        if name in algo:
+            per_kernel[name]["tflops"] = algo[name][1] / (tot / cnt * 1e-3) / 1e12
+    dom = max(kernels, key=lambda k: kernels[k][1])
+    cnt, tot = kernels[dom]
+    avg_s = tot / cnt * 1e-3
+    if dom in algo:
+        achieved = algo[dom][1] / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": None}
+    roof["kernel"] = dom
+    roof["avg_ms"] = avg_s * 1e3
+    roof["traffic"] = traffic_for(dom, w.name, kernel_source_hash())
+
+    fwd_ms = sum(kernels[k][1] for k in ("fwd_bf16", "merge_split") if k in kernels) / args.steps
+    value = step_flops / (ms * 1e-3) / 1e12
+    item_imb = sh.info.item_cost_max_bin / (sh.info.item_cost_total / n_wg) - 1
+    kv_imb = sh.info.kv_cost_max_bin / (sh.info.kv_cost_total / n_wg) - 1
+    chunk_imb = float(chunk_load.max() / chunk_load.mean() - 1)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "context": g.ctx, "draft_queries": w.nq,
+                   "anchor_blocks": w.nb, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d,
+                   "chunk": w.chunk, "seed": args.seed,
+                   "step": "fwd" if args.fwd_only else "fwd+bwd"},
+        "frac_of_bf16_peak": value / PEAK_BF16_TFLOPS,
+        "fwd_tflops": fwd_flops / (fwd_ms * 1e-3) / 1e12,
+        "fwd_frac_of_bf16_peak": fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "fwd_ms": fwd_ms,
+        "algorithmic_tflop_per_step": step_flops / 1e12,
+        "lpt": {"work_items": sh.info.n_items, "item_imbalance_256cu": item_imb,
+                "kv_items": sh.info.n_kv_items, "kv_item_imbalance_256cu": kv_imb,
+                "chunk_imbalance_256bins": chunk_imb, "plan_ms": 1e3 * float(np.median(plan_times)),
+                "workgroups": n_wg},
+        "kernels": per_kernel,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(w, g, t)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

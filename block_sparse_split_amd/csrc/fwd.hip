@@ -30,6 +30,7 @@
 // MFMAs.
 #include "device_common.h"
 #include "launch.h"
+#include "timing.h"
 
 namespace skv {
 namespace {
@@ -530,13 +531,13 @@ hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_kernel<D>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(a.n_wg), dim3(kThreads), bytes, stream, a);
+    SKV_LAUNCH("fwd_bf16", fwd_bf16_kernel<D>, dim3(a.n_wg), dim3(kThreads), bytes, stream, a);
   } else {
     constexpr int bytes = F32Lds<D>::bytes;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_f32_kernel<D>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fwd_f32_kernel<D>, dim3(a.n_wg), dim3(kThreads), bytes, stream, a);
+    SKV_LAUNCH("fwd_f32", fwd_f32_kernel<D>, dim3(a.n_wg), dim3(kThreads), bytes, stream, a);
   }
   return hipGetLastError();
 }

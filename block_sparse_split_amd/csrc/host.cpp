@@ -694,6 +694,7 @@ skv_status skv_attn_bwd(const skv_problem* p, const skv_schedule_info* info,
             "Kd/Vd/dKd/dVd must not be NULL with with_draft");
     if (!(grad_dtype == SKV_BF16 || grad_dtype == SKV_F32))
       fail(SKV_ERR_UNSUPPORTED, "grad_dtype must be SKV_BF16 or SKV_F32");
+    if (p->dtype != SKV_BF16) fail(SKV_ERR_UNSUPPORTED, "the backward takes bf16 inputs only");
     if (workspace_bytes < info->bwd_workspace_bytes || !workspace)
       fail(SKV_ERR_WORKSPACE, "workspace too small: need " +
                                   std::to_string(info->bwd_workspace_bytes) + " bytes");

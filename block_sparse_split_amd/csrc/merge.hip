@@ -14,6 +14,7 @@
 // for memory-level parallelism.
 #include "device_common.h"
 #include "launch.h"
+#include "timing.h"
 
 namespace skv {
 namespace {
@@ -139,16 +140,16 @@ hipError_t launch_merge_d(int32_t n, int64_t rows, const void* O, bool in_bf16, 
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 g(static_cast<unsigned>(blocks)), b(kThreads);
   if (in_bf16 && out_bf16)
-    hipLaunchKernelGGL((merge_kernel<__bf16, __bf16, D>), g, b, 0, s, n, rows,
+    SKV_LAUNCH("merge", (merge_kernel<__bf16, __bf16, D>), g, b, 0, s, n, rows,
                        static_cast<const __bf16*>(O), L, static_cast<__bf16*>(Oo), Lo);
   else if (in_bf16)
-    hipLaunchKernelGGL((merge_kernel<__bf16, float, D>), g, b, 0, s, n, rows,
+    SKV_LAUNCH("merge", (merge_kernel<__bf16, float, D>), g, b, 0, s, n, rows,
                        static_cast<const __bf16*>(O), L, static_cast<float*>(Oo), Lo);
   else if (out_bf16)
-    hipLaunchKernelGGL((merge_kernel<float, __bf16, D>), g, b, 0, s, n, rows,
+    SKV_LAUNCH("merge", (merge_kernel<float, __bf16, D>), g, b, 0, s, n, rows,
                        static_cast<const float*>(O), L, static_cast<__bf16*>(Oo), Lo);
   else
-    hipLaunchKernelGGL((merge_kernel<float, float, D>), g, b, 0, s, n, rows,
+    SKV_LAUNCH("merge", (merge_kernel<float, float, D>), g, b, 0, s, n, rows,
                        static_cast<const float*>(O), L, static_cast<float*>(Oo), Lo);
   return hipGetLastError();
 }
@@ -158,10 +159,10 @@ hipError_t launch_merge_split_d(const FwdArgs& a, hipStream_t s) {
   constexpr int RPB = kThreads / (D / 8);
   const dim3 g(a.n_split * (kQTile / RPB)), b(kThreads);
   if (a.o_bf16)
-    hipLaunchKernelGGL((merge_split_kernel<__bf16, D>), g, b, 0, s, a.sched, a.ws_O, a.ws_LSE,
+    SKV_LAUNCH("merge_split", (merge_split_kernel<__bf16, D>), g, b, 0, s, a.sched, a.ws_O, a.ws_LSE,
                        static_cast<__bf16*>(a.O), a.LSE);
   else
-    hipLaunchKernelGGL((merge_split_kernel<float, D>), g, b, 0, s, a.sched, a.ws_O, a.ws_LSE,
+    SKV_LAUNCH("merge_split", (merge_split_kernel<float, D>), g, b, 0, s, a.sched, a.ws_O, a.ws_LSE,
                        static_cast<float*>(a.O), a.LSE);
   return hipGetLastError();
 }

@@ -83,10 +83,18 @@ def lib():
     L.skv_merge_lse.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _vp,
                                 ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, _vp]
     L.skv_attn_bwd.argtypes = [ctypes.POINTER(SkvProblem), ctypes.POINTER(SkvScheduleInfo),
-                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                               _vp, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_int64, _vp]
+                               _vp,                                  # schedule
+                               _vp, _vp, _vp, _vp, _vp,              # Q K V Kd Vd
+                               _vp, _vp, _vp,                        # O dO LSE
+                               _vp, _vp, _vp, _vp, _vp,              # dQ dK dV dKd dVd
+                               ctypes.c_int32, _vp, ctypes.c_int64, _vp]
+    L.skv_timing_enable.argtypes = [ctypes.c_int32]
+    L.skv_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int32)]
+    L.skv_timing_result.argtypes = [ctypes.c_int32, ctypes.c_char_p, ctypes.c_int32, _i64p,
+                                    ctypes.POINTER(ctypes.c_double)]
     for name in ("skv_chunk_costs", "skv_plan_lpt_costs", "skv_plan_lpt", "skv_schedule_build",
-                 "skv_attn_fwd_partial", "skv_merge_lse", "skv_attn_bwd"):
+                 "skv_attn_fwd_partial", "skv_merge_lse", "skv_attn_bwd", "skv_timing_enable",
+                 "skv_timing_collect", "skv_timing_result"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -309,3 +317,24 @@ class Shard:
             stream=None):
         skv_attn_bwd(self.problem, self.info, self.schedule, Q, K, V, Kd, Vd, O, dO, LSE, dQ,
                      dK, dV, dKd, dVd, grad_dtype, self.workspace, stream)
+
+
+# ---------------------------------------------------------------- timing
+
+def skv_timing_enable(on: bool = True):
+    _check("skv_timing_enable", lib().skv_timing_enable(int(bool(on))))
+
+
+def skv_timing_collect():
+    """{kernel name: (launches, total ms)} of the events recorded so far."""
+    n = ctypes.c_int32(0)
+    _check("skv_timing_collect", lib().skv_timing_collect(ctypes.byref(n)))
+    out = {}
+    buf = ctypes.create_string_buffer(64)
+    for k in range(n.value):
+        cnt = ctypes.c_int64(0)
+        ms = ctypes.c_double(0)
+        _check("skv_timing_result", lib().skv_timing_result(k, buf, 64, ctypes.byref(cnt),
+                                                            ctypes.byref(ms)))
+        out[buf.value.decode()] = (cnt.value, ms.value)
+    return out

@@ -226,6 +226,26 @@ skv_status skv_attn_bwd(const skv_problem* p, const skv_schedule_info* info,
                         int32_t grad_dtype, void* workspace,
                         int64_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Benchmark support: per-kernel timing with HIP events.
+ * ---------------------------------------------------------------------- */
+
+/* While enabled on the calling thread, every kernel a device call launches
+ * is bracketed by a hipEventRecord pair on its launch stream.  Records are
+ * per thread and kept until collected.  Disabled by default. */
+skv_status skv_timing_enable(int32_t on);
+
+/* Wait for the recorded events, fold them into per-kernel totals (launch
+ * count and summed milliseconds) and clear the records; *n_kernels gets the
+ * number of distinct kernels.  Errors: SKV_ERR_HIP if an event failed. */
+skv_status skv_timing_collect(int32_t* n_kernels);
+
+/* Kernel k of the last collect: its name (NUL-terminated, truncated to
+ * name_cap), launch count and total milliseconds.  Errors:
+ * SKV_ERR_INVALID_ARG for k out of range or a NULL/empty name buffer. */
+skv_status skv_timing_result(int32_t k, char* name, int32_t name_cap, int64_t* launches,
+                             double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -128,7 +128,7 @@ def merge_lse(O_parts, LSE_parts):
 
 
 def attention_bwd(Q, K, V, pos, anchors, lo, scale, O, dO, LSE, Kd=None,
-                  Vd=None):
+                  Vd=None, blocks=None):
     """Gradients of sum(O * dO) for the keys of one subset.
 
     O and LSE must be the FINAL (merged, single-device) output and
@@ -137,6 +137,9 @@ def attention_bwd(Q, K, V, pos, anchors, lo, scale, O, dO, LSE, Kd=None,
     D = rowsum(dO * O) and dP = dO V^T:
         dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
     Query heads sharing a kv head sum into its dK/dV.
+
+    ``blocks`` restricts the sum to some anchor blocks: their dQ rows are
+    then exact, while dK/dV only hold those blocks' contributions.
 
     Returns dQ [Nq, Hq, d] (this subset's share; shares sum to the full dQ),
     dK, dV [n, Hkv, d] and dKd, dVd [Nq, Hkv, d] (None without draft keys).
@@ -156,7 +159,7 @@ def attention_bwd(Q, K, V, pos, anchors, lo, scale, O, dO, LSE, Kd=None,
     dV = np.zeros_like(V)
     dKd = None if Kd is None else np.zeros_like(Kd)
     dVd = None if Vd is None else np.zeros_like(Vd)
-    for i in range(nb):
+    for i in (range(nb) if blocks is None else blocks):
         rows = slice(BLOCK * i, BLOCK * (i + 1))
         for g in range(hkv):
             idx, keys, vals = _block_keys(K, V, Kd, Vd, vis[i], i, g)

@@ -244,3 +244,35 @@ def test_in_gpu_item_plan_imbalance_32k():
     w, g, prob, pos, image, info = _schedule_case("ctx32k_q2k", 1, None, 256)
     imb = info.item_cost_max_bin / (info.item_cost_total / 256) - 1
     assert imb < 0.05, imb
+
+
+def test_device_calls_reject_bad_dtypes_before_launch():
+    """Argument errors are returned before anything touches a device (the
+    fake pointers below are never dereferenced)."""
+    import ctypes
+    w, g, _ = wl.make("tiny_f32_ctx1k", 0, tensors=False)
+    prob = shards.whole_context_problem(w, g)
+    image, info = skv.skv_schedule_build(prob, 8)
+    L = skv.lib()
+    fake = ctypes.c_void_p(256)
+    st = L.skv_attn_fwd_partial(ctypes.byref(prob.c), ctypes.byref(info), fake, fake, fake, fake,
+                                fake, fake, fake, 7, fake, fake, 1 << 30, None)
+    assert st == -2 and b"o_dtype" in L.skv_last_error()
+    # backward takes bf16 inputs only
+    st = L.skv_attn_bwd(ctypes.byref(prob.c), ctypes.byref(info), fake, fake, fake, fake, fake,
+                        fake, fake, fake, fake, fake, fake, fake, fake, fake, 0, fake, 1 << 30,
+                        None)
+    assert st == -2 and b"bf16" in L.skv_last_error()
+    # a schedule built for another problem is refused
+    prob2 = shards.shard_problem(w, g, [0, 1], False)
+    st = L.skv_attn_fwd_partial(ctypes.byref(prob2.c), ctypes.byref(info), fake, fake, fake,
+                                fake, fake, fake, fake, 1, fake, fake, 1 << 30, None)
+    assert st == -1 and b"different problem" in L.skv_last_error()
+    # workspace too small
+    w1, g1, _ = wl.make("ctx32k_q2k", 1, tensors=False)
+    p1 = shards.whole_context_problem(w1, g1)
+    _, i1 = skv.skv_schedule_build(p1, 256)
+    assert i1.fwd_workspace_bytes > 0
+    st = L.skv_attn_fwd_partial(ctypes.byref(p1.c), ctypes.byref(i1), fake, fake, fake, fake,
+                                fake, fake, fake, 1, fake, fake, 16, None)
+    assert st == -4

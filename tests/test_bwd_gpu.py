@@ -1,0 +1,171 @@
+"""GPU parity of the backward (dQ, dK, dV and the draft-key gradients)
+against the fp64 oracle through the C ABI.  Bar: max-abs <= 2e-2 for the
+bf16 path; every check also bounds the error relative to the largest
+reference value, so small gradients cannot pass by being small."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_split_amd import splitkv as skv
+from block_sparse_split_amd import shards
+from block_sparse_split_amd import workloads as wl
+from gpu_util import announce, block_rows, gpu_fwd, rows_of, to_dev
+
+pytestmark = pytest.mark.gpu
+
+ABS_TOL = 2e-2
+REL_TOL = 2e-2  # of max |reference|
+
+
+def check_grad(got, want, what):
+    got = got.float().cpu().numpy().astype(np.float64) if torch.is_tensor(got) else got
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    err = np.abs(got - want).max(initial=0.0)
+    scale = np.abs(want).max(initial=0.0)
+    assert err <= ABS_TOL, f"{what}: max-abs {err:.3g} > {ABS_TOL}"
+    assert err <= REL_TOL * scale + 1e-7, f"{what}: max-abs {err:.3g} vs max|ref| {scale:.3g}"
+    return err, scale
+
+
+def gpu_bwd(w, g, t, chunk_ids, with_draft, O, LSE, n_wg=0, grad_dtype=skv.SKV_F32):
+    prob = shards.shard_problem(w, g, chunk_ids, with_draft)
+    sh = skv.Shard(prob, n_workgroups=n_wg)
+    r = rows_of(t, g, chunk_ids)
+    dt = w.dtype
+    Q, K, V = to_dev(t.Q, dt), to_dev(t.K[r], dt), to_dev(t.V[r], dt)
+    Kd = to_dev(t.Kd, dt) if with_draft else None
+    Vd = to_dev(t.Vd, dt) if with_draft else None
+    dO = to_dev(t.dO, dt)
+    gdt = torch.float32 if grad_dtype == skv.SKV_F32 else torch.bfloat16
+    nl = len(r)
+    dQ = torch.full((w.nq, w.hq, w.d), float("nan"), device="cuda")
+    dK = torch.full((nl, w.hkv, w.d), float("nan"), dtype=gdt, device="cuda")
+    dV = torch.full_like(dK, float("nan"))
+    dKd = torch.full((w.nq, w.hkv, w.d), float("nan"), dtype=gdt, device="cuda") \
+        if with_draft else None
+    dVd = torch.full_like(dKd, float("nan")) if with_draft else None
+    sh.bwd(Q, K, V, Kd, Vd, O, dO, LSE, dQ, dK, dV, dKd, dVd, grad_dtype)
+    torch.cuda.synchronize()
+    return dQ, dK, dV, dKd, dVd
+
+
+def oracle_fwd_bwd(w, g, t, chunk_ids, with_draft, blocks=None):
+    scale = wl.softmax_scale(w.d)
+    O, L = oracle.attention(t.Q, t.K, t.V, t.Kd, t.Vd, g.anchors, g.lo, scale,
+                            pos=shards.shard_rows(g, t.chunk_ids))
+    r = rows_of(t, g, chunk_ids)
+    pos = shards.shard_rows(g, chunk_ids)
+    grads = oracle.attention_bwd(t.Q, t.K[r], t.V[r], pos, g.anchors, g.lo, scale, O, t.dO, L,
+                                 t.Kd if with_draft else None, t.Vd if with_draft else None,
+                                 blocks=blocks)
+    return O, L, grads
+
+
+def _small(seed, **over):
+    base = dict(ctx=4096, anchor_lo=1024, anchor_hi=4096, blocks_per_seq=16)
+    base.update(over)
+    return wl.make(wl.scaled(wl.WORKLOADS["ctx32k_q2k"], **base), seed, with_grad=True)
+
+
+@pytest.mark.parametrize("seed,n_wg,gdt", [(0, 256, skv.SKV_F32), (1, 17, skv.SKV_BF16),
+                                           (2, 1, skv.SKV_F32)])
+def test_bwd_small_with_oracle_stats(seed, n_wg, gdt):
+    """The backward alone, fed the oracle's O (rounded to bf16) and LSE."""
+    w, g, t = _small(seed)
+    allc = np.arange(len(g.chunk_pos))
+    O, L, (dQ, dK, dV, dKd, dVd) = oracle_fwd_bwd(w, g, t, allc, True)
+    announce("bwd small oracle-stats", seed, n_wg, gdt)
+    got = gpu_bwd(w, g, t, allc, True, to_dev(wl.round_to_bf16(O.astype(np.float32)), "bf16"),
+                  torch.from_numpy(L.astype(np.float32)).cuda(), n_wg=n_wg, grad_dtype=gdt)
+    for name, a, b in zip(("dQ", "dK", "dV", "dKd", "dVd"), got, (dQ, dK, dV, dKd, dVd)):
+        check_grad(a, b, name)
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_fwd_then_bwd_chain_small(seed):
+    """GPU forward output and LSE feed the GPU backward."""
+    w, g, t = _small(seed)
+    allc = np.arange(len(g.chunk_pos))
+    announce("fwd->bwd chain", seed)
+    O, L, _ = gpu_fwd(w, g, t, allc, True, n_wg=64)
+    got = gpu_bwd(w, g, t, allc, True, O, L, n_wg=64)
+    _, _, want = oracle_fwd_bwd(w, g, t, allc, True)
+    for name, a, b in zip(("dQ", "dK", "dV", "dKd", "dVd"), got, want):
+        check_grad(a, b, name)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 4, 64), (16, 1, 128), (8, 4, 128), (16, 2, 64)])
+def test_bwd_gqa_and_head_dims(hq, hkv, d):
+    w, g, t = _small(5, hq=hq, hkv=hkv, d=d, ctx=2048, anchor_lo=100, anchor_hi=2048,
+                     blocks_per_seq=9)
+    allc = np.arange(len(g.chunk_pos))
+    O, L, want = oracle_fwd_bwd(w, g, t, allc, True)
+    announce("bwd gqa", hq, hkv, d)
+    got = gpu_bwd(w, g, t, allc, True, to_dev(wl.round_to_bf16(O.astype(np.float32)), "bf16"),
+                  torch.from_numpy(L.astype(np.float32)).cuda(), n_wg=24)
+    for name, a, b in zip(("dQ", "dK", "dV", "dKd", "dVd"), got, want):
+        check_grad(a, b, f"{name} G={hq // hkv} d={d}")
+
+
+def test_bwd_split_over_shards():
+    """Per-shard backward with the final merged O/LSE: the dQ shares sum to
+    the full dQ and each shard's dK/dV are its rows of the unsplit ones."""
+    w = wl.scaled(wl.WORKLOADS["cp64_rank0_ctx512k"], ctx=8192, anchor_lo=2048,
+                  anchor_hi=8192, blocks_per_seq=8, chunk=512, n_shards=4)
+    w, g, t = wl.make(w, 6, with_grad=True)
+    ids, _, _, _ = shards.lpt_shards(w, g, w.n_shards)
+    allc = np.arange(len(g.chunk_pos))
+    O, L, full = oracle_fwd_bwd(w, g, t, allc, True)
+    Od = to_dev(wl.round_to_bf16(O.astype(np.float32)), "bf16")
+    Ld = torch.from_numpy(L.astype(np.float32)).cuda()
+    dq_sum = torch.zeros((w.nq, w.hq, w.d), device="cuda")
+    for r in range(w.n_shards):
+        announce("bwd shard", r)
+        dQ, dK, dV, dKd, dVd = gpu_bwd(w, g, t, ids[r], r == 0, Od, Ld, n_wg=32)
+        dq_sum += dQ
+        rr = rows_of(t, g, ids[r])
+        check_grad(dK, full[1][rr], f"dK shard {r}")
+        check_grad(dV, full[2][rr], f"dV shard {r}")
+        if r == 0:
+            check_grad(dKd, full[3], "dKd")
+            check_grad(dVd, full[4], "dVd")
+    check_grad(dq_sum, full[0], "sum of dQ shares")
+
+
+def test_bwd_varlen_small():
+    w = wl.scaled(wl.WORKLOADS["varlen8_fwdbwd"], len_median=1500, len_min=300, len_max=5000,
+                  blocks_per_seq=6, n_seq=5)
+    w, g, t = wl.make(w, 7, with_grad=True)
+    allc = np.arange(len(g.chunk_pos))
+    announce("bwd varlen small")
+    O, L, _ = gpu_fwd(w, g, t, allc, True, n_wg=40)
+    got = gpu_bwd(w, g, t, allc, True, O, L, n_wg=40)
+    _, _, want = oracle_fwd_bwd(w, g, t, allc, True)
+    for name, a, b in zip(("dQ", "dK", "dV", "dKd", "dVd"), got, want):
+        check_grad(a, b, f"varlen {name}")
+
+
+def test_bwd_full_ctx32k_sampled():
+    """The 32K-context shapes on all CUs: dQ on sampled anchor blocks and
+    dK/dV on sampled key ranges, against the oracle (which recomputes the
+    full forward for the normaliser)."""
+    w, g, t = wl.make("ctx32k_q2k", 1, with_grad=True)
+    allc = np.arange(len(g.chunk_pos))
+    announce("bwd full ctx32k")
+    O, L, _ = gpu_fwd(w, g, t, allc, True)
+    dQ, dK, dV, dKd, dVd = gpu_bwd(w, g, t, allc, True, O, L)
+    scale = wl.softmax_scale(w.d)
+    Oo, Lo = oracle.attention(t.Q, t.K, t.V, t.Kd, t.Vd, g.anchors, g.lo, scale)
+    blocks = [0, 5, 63, 64, 126, 127]
+    rows = block_rows(blocks)
+    gq = oracle.attention_bwd(t.Q, t.K, t.V, np.arange(g.ctx), g.anchors, g.lo, scale, Oo,
+                              t.dO, Lo, t.Kd, t.Vd, blocks=blocks)
+    check_grad(dQ[rows], gq[0][rows], "dQ sampled rows")
+    check_grad(dKd[rows], gq[3][rows], "dKd sampled rows")
+    check_grad(dVd[rows], gq[4][rows], "dVd sampled rows")
+    keys = np.concatenate([np.arange(0, 64), np.arange(20000, 20100), np.arange(32700, 32768)])
+    gk = oracle.attention_bwd(t.Q, t.K[keys], t.V[keys], keys, g.anchors, g.lo, scale, Oo, t.dO,
+                              Lo)
+    check_grad(dK[keys], gk[1], "dK sampled keys")
+    check_grad(dV[keys], gk[2], "dV sampled keys")

@@ -356,3 +356,20 @@ def test_generator_bf16_rounding_and_shapes():
     for s in range(8):
         sl = slice(4 * s, 4 * s + 4)
         assert np.all(g3.anchors[sl] < g3.seq_start[s] + g3.seq_len[s])
+
+
+def test_bwd_block_subset_gives_exact_dq_rows():
+    p = tiny_problem(18, nb=4, ctx=90, nseq=2)
+    dO = np.random.default_rng(9).standard_normal(p["Q"].shape)
+    O, L = oracle.attention(p["Q"], p["K"], p["V"], p["Kd"], p["Vd"],
+                            p["anchors"], p["lo"], p["scale"])
+    pos = np.arange(p["K"].shape[0])
+    full = oracle.attention_bwd(p["Q"], p["K"], p["V"], pos, p["anchors"], p["lo"],
+                                p["scale"], O, dO, L, p["Kd"], p["Vd"])
+    parts = [oracle.attention_bwd(p["Q"], p["K"], p["V"], pos, p["anchors"], p["lo"],
+                                  p["scale"], O, dO, L, p["Kd"], p["Vd"], blocks=b)
+             for b in ([0, 2], [1, 3])]
+    np.testing.assert_array_equal(parts[0][0][:16], full[0][:16])
+    np.testing.assert_array_equal(parts[1][0][16:32], full[0][16:32])
+    for k in range(1, 5):
+        np.testing.assert_allclose(parts[0][k] + parts[1][k], full[k], atol=1e-13)
