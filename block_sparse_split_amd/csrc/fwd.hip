@@ -40,87 +40,123 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kQB = 2;             // 32-query column blocks per wave
 constexpr int kKB = kTileK / 32;   // 32-key blocks per step
 
+// ---------------------------------------------------------------------------
+// bf16 path.  Eight waves (two per SIMD, so one wave's MFMAs overlap the
+// other's softmax) each own 32 query rows of the 256-row tile.  K and V tiles
+// reach LDS by direct global->LDS DMA (global_load_lds_dwordx4) into a
+// 3-stage ring, so two steps of loads are in flight while one computes and no
+// registers hold staged data.  Each DMA lane picks its own global address, so
+// the tiles are written in the order they are consumed:
+//   K  fragment-major: the A operand of MFMA (key block kb, d-step t) -- 32
+//      rows x 32 bytes -- is one contiguous 1 KB, lane L at byte 16 L;
+//   V  in blocks of 4 keys x 16 d (128 bytes, row-major inside), grouped per
+//      4-key quad; a 16-lane ds_read_b64_tr_b16 of one block returns, in lane
+//      i, column i of the 4 keys -- half of a V^T A-operand fragment.
+// Every LDS read is then one base register plus an immediate offset, reads
+// are contiguous (no bank conflicts) and V is never transposed in memory.
 template <int D>
-struct Bf16Lds {
-  static constexpr int kPitch = D + 8;        // K row pitch (elements)
-  static constexpr int vPitch = kTileK + 8;   // V^T row pitch (elements)
-  static constexpr int kElems = kTileK * kPitch;
-  static constexpr int vElems = D * vPitch;
-  static constexpr int bufElems = kElems + vElems;
-  static constexpr int bytes = 2 * bufElems * 2;
+struct FwdCfg {
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kTileBytes = kTileK * D * 2;        // 16 KB (d=128) / 8 KB
+  static constexpr int kStageBytes = 2 * kTileBytes;       // K then V
+  static constexpr int kStages = 3;
+  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kKFrags = 2 * (D / 16);             // 1 KB K fragments per tile
+  static constexpr int kQuadBytes = 4 * D * 2;             // one 4-key quad of V
+  static constexpr int kDmaPerWave = 2 * (kTileBytes / 1024) / kWaves;
 };
 
-template <int D>
-struct StepRegs {
-  static constexpr int NK = kTileK * D / 8 / kThreads;
-  uint4 k[NK];
-  uint4 v[4];
-};
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from global memory straight into LDS at
+// lds_base + 16 * lane (lds_base wave-uniform).  Issued as inline asm so the
+// compiler neither serialises it against LDS reads nor waits on it; the
+// kernel waits with explicit vmcnt counts before its barriers.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gsrc), "s"(lds_base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
-__device__ __forceinline__ uint4 ld16(const __bf16* p) {
-  return *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
+// s_waitcnt vmcnt(n) (n < 16) leaving lgkmcnt/expcnt alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(3))) char* lds_cptr;
+
+// An LDS byte address the optimiser cannot see through: per-step bases are
+// laundered so that each read becomes `base + immediate offset` instead of
+// one loop-invariant address register per read.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+      static_cast<uintptr_t>(addr));
+}
+
+__device__ __forceinline__ short4v ds_read_tr(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4v*)(static_cast<uintptr_t>(addr)));
+}
+
+// Issue this wave's share of the DMA for one step into `stage` (LDS bytes).
+// DMA block u < kKFrags is K fragment (kb, t) = (u / (D/16), u % (D/16)):
+// lane i loads row 32 kb + i % 32, d = 16 t + 8 (i / 32).  The other blocks
+// are V: byte 16 i of block j lies in quad q = (1024 j + 16 i) / quadBytes at
+// offset w, holding row 4 q + (w % 128) / 32 and d = 16 (w / 128) + 8 ((w % 32) / 16).
+// Rows past the end of a ragged step repeat the last valid row (their keys are
+// masked, the values stay finite).
 template <int D>
-__device__ __forceinline__ void load_step(StepRegs<D>& r, const __bf16* Kg, const __bf16* Vg,
-                                          const Step& st, int head, int hkv, int tid) {
-  constexpr int CPR = D / 8;
+__device__ __forceinline__ void issue_step(const __bf16* Kg, const __bf16* Vg, const Step& st,
+                                           int head, int hkv, uint32_t stage, int wave,
+                                           int lane) {
+  using C = FwdCfg<D>;
 #pragma unroll
-  for (int i = 0; i < StepRegs<D>::NK; ++i) {
-    const int c = tid + i * kThreads;
-    const int row = c / CPR, col = (c % CPR) * 8;
-    r.k[i] = row < st.n ? ld16(Kg + ((int64_t)(st.row + row) * hkv + head) * D + col)
-                        : make_uint4(0, 0, 0, 0);
-  }
-  if (tid < (kTileK / 4) * CPR) {
-    const int m = tid / CPR, dr = tid % CPR;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = 4 * m + j;
-      r.v[j] = key < st.n ? ld16(Vg + ((int64_t)(st.row + key) * hkv + head) * D + dr * 8)
-                          : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < C::kDmaPerWave; ++i) {
+    const int u = wave * C::kDmaPerWave + i;
+    int row, col;
+    const __bf16* src;
+    if (u < C::kKFrags) {
+      row = (u / (D / 16)) * 32 + (lane & 31);
+      col = 16 * (u % (D / 16)) + 8 * (lane >> 5);
+      src = Kg;
+    } else {
+      const int byte = (u - C::kKFrags) * 1024 + 16 * lane;
+      const int q = byte / C::kQuadBytes, w = byte % C::kQuadBytes;
+      row = 4 * q + (w & 127) / 32;
+      col = 16 * (w / 128) + 8 * ((w & 31) / 16);
+      src = Vg;
     }
-  }
-}
-
-__device__ __forceinline__ uint32_t half_of(const uint4& u, int e) {
-  const uint32_t word = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
-  return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
-}
-
-template <int D>
-__device__ __forceinline__ void store_step(const StepRegs<D>& r, __bf16* buf, int tid) {
-  using L = Bf16Lds<D>;
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int i = 0; i < StepRegs<D>::NK; ++i) {
-    const int c = tid + i * kThreads;
-    const int row = c / CPR, col = (c % CPR) * 8;
-    *reinterpret_cast<uint4*>(buf + row * L::kPitch + col) = r.k[i];
-  }
-  if (tid < (kTileK / 4) * CPR) {
-    const int m = tid / CPR, dr = tid % CPR;
-    // keys 4m..4m+3 land at a permuted position inside their 16-key group:
-    // sub-group 0,1,2,3 -> offset 0,8,4,12 (matches the S^T accumulator)
-    const int pos = 16 * (m >> 2) + ((m & 1) ? 8 : 0) + ((m & 2) ? 4 : 0);
-    __bf16* vt = buf + L::kElems;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint2 w;
-      w.x = half_of(r.v[0], e) | (half_of(r.v[1], e) << 16);
-      w.y = half_of(r.v[2], e) | (half_of(r.v[3], e) << 16);
-      *reinterpret_cast<uint2*>(vt + (dr * 8 + e) * L::vPitch + pos) = w;
-    }
+    const int grow = min(row, st.n - 1);
+    dma16(src + ((int64_t)(st.row + grow) * hkv + head) * D + col, stage + u * 1024);
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
-  using L = Bf16Lds<D>;
-  extern __shared__ __align__(16) char smem_raw[];
-  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
+__global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
+  using C = FwdCfg<D>;
+  extern __shared__ __align__(16) char smem[];
   const int32_t* S = a.sched;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h32 = lane >> 5, l32 = lane & 31;
   const int G = S[H_G], hq = S[H_HQ], hkv = S[H_HKV], nb = S[H_NB];
   const int nq = nb * kBlock, rows_per_head = nq * G;
@@ -132,6 +168,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   const int qbeg = S[S[H_OFF_QOFF] + blockIdx.x], qend = S[S[H_OFF_QOFF] + blockIdx.x + 1];
   const float c = a.scale * kLog2e;
   const __bf16* Qg = static_cast<const __bf16*>(a.Q);
+  const uint32_t lds0 = lds_addr(smem);
+  // per-lane LDS byte offsets inside a stage: K fragment lane slot, and the
+  // transposed V read (16-lane group G reads quad ... + G / 2, block
+  // 2 db + G % 2, 8 bytes per lane)
+  const uint32_t koff = 16 * lane;
+  const uint32_t voff = C::kTileBytes + (lane >> 5) * C::kQuadBytes + ((lane >> 4) & 1) * 128 +
+                        8 * (lane & 15);
 
   for (int qi = qbeg; qi < qend; ++qi) {
     const int32_t* it = items + queue[qi] * I_WORDS;
@@ -141,162 +184,133 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
     const int n_draft = (flags & kItemDraft) ? (sp.dtok1 - sp.dtok0 + kTileK - 1) / kTileK : 0;
     const int n_steps = n_draft + (t1 - t0);
 
-    int rloc[kQB], tok[kQB], qh[kQB], blk[kQB], lo_[kQB], an[kQB];
-    bool valid[kQB];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      rloc[qb] = wave * 64 + qb * 32 + l32;
-      const int rho = qt * kQTile + rloc[qb];
-      valid[qb] = rho < rows_per_head;
-      tok[qb] = valid[qb] ? rho / G : 0;
-      qh[qb] = head * G + (valid[qb] ? rho % G : 0);
-      blk[qb] = tok[qb] / kBlock;
-      lo_[qb] = valid[qb] ? los[blk[qb]] : 0;
-      an[qb] = valid[qb] ? anchors[blk[qb]] : 0;
-    }
-    bf16x8 qf[kQB][D / 16];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const __bf16* qrow = Qg + ((int64_t)tok[qb] * hq + qh[qb]) * D + 8 * h32;
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        uint4 u = valid[qb] ? ld16(qrow + 16 * t) : make_uint4(0, 0, 0, 0);
-        qf[qb][t] = __builtin_bit_cast(bf16x8, u);
-      }
-    }
-    f32x16 o[kQB][D / 32];
-    float m_used[kQB], l[kQB];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      m_used[qb] = kNegInf;
-      l[qb] = 0.f;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
-    }
+    const int rloc = wave * 32 + l32;
+    const int rho = qt * kQTile + rloc;
+    const bool valid = rho < rows_per_head;
+    const int tok = valid ? rho / G : 0;
+    const int qh = head * G + (valid ? rho % G : 0);
+    const int blk = tok / kBlock;
+    const int lo_ = valid ? los[blk] : 0, an = valid ? anchors[blk] : 0;
+    const int64_t qrow = (int64_t)tok * hq + qh;
 
-    StepRegs<D> regs;
-    if (n_steps > 0) {
-      const Step st = item_step(tiles, 0, n_draft, t0, sp);
+    auto issue = [&](int s) {
+      const Step st = item_step(tiles, s, n_draft, t0, sp);
       const __bf16* Kg = static_cast<const __bf16*>(st.draft ? a.Kd : a.K);
       const __bf16* Vg = static_cast<const __bf16*>(st.draft ? a.Vd : a.V);
-      load_step<D>(regs, Kg, Vg, st, head, hkv, tid);
-      store_step<D>(regs, smem, tid);
-    }
-    __syncthreads();
-    for (int s = 0; s < n_steps; ++s) {
-      const Step st = item_step(tiles, s, n_draft, t0, sp);
-      if (s + 1 < n_steps) {
-        const Step nx = item_step(tiles, s + 1, n_draft, t0, sp);
-        const __bf16* Kg = static_cast<const __bf16*>(nx.draft ? a.Kd : a.K);
-        const __bf16* Vg = static_cast<const __bf16*>(nx.draft ? a.Vd : a.V);
-        load_step<D>(regs, Kg, Vg, nx, head, hkv, tid);
-      }
-      const __bf16* Kl = smem + (s & 1) * L::bufElems;
-      const __bf16* Vl = Kl + L::kElems;
-      int klo[kQB], khi[kQB];
-      bool lane_full = true, lane_any = false;
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        if (valid[qb]) {
-          step_bounds(st, lo_[qb], an[qb], blk[qb], klo[qb], khi[qb]);
-          lane_full = lane_full && klo[qb] <= 0 && khi[qb] >= kTileK;
-          lane_any = lane_any || klo[qb] < khi[qb];
-        } else {
-          klo[qb] = 0;
-          khi[qb] = kTileK;
-        }
-      }
-      if (__any(lane_any)) {
-        const bool wave_full = __all(lane_full);
-        f32x16 sacc[kKB][kQB];
-#pragma unroll
-        for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-          for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][qb][r] = 0.f;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-#pragma unroll
-          for (int kb = 0; kb < kKB; ++kb) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-                Kl + (kb * 32 + l32) * L::kPitch + 16 * t + 8 * h32);
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb)
-              sacc[kb][qb] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][t], sacc[kb][qb], 0, 0, 0);
-          }
-        }
-        if (!wave_full) {
-#pragma unroll
-          for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int kappa = 32 * kb + 8 * (r >> 2) + 4 * h32 + (r & 3);
-#pragma unroll
-              for (int qb = 0; qb < kQB; ++qb)
-                if (kappa < klo[qb] || kappa >= khi[qb]) sacc[kb][qb][r] = kNegInf;
-            }
-        }
-        bf16x8 pf[kQB][kKB][2];
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-          float mx = kNegInf;
-#pragma unroll
-          for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float mt = mx * c;
-          const bool need = mt > m_used[qb] + 8.0f;
-          if (__any(need)) {
-            const float alpha = need ? exp2_fast(m_used[qb] - mt) : 1.0f;
-            l[qb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) o[qb][db] *= alpha;
-            if (need) m_used[qb] = mt;
-          }
-          const float msub = m_used[qb] == kNegInf ? 0.f : m_used[qb];
-          float ls = 0.f;
-#pragma unroll
-          for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float p = exp2_fast(fmaf(sacc[kb][qb][r], c, -msub));
-              ls += p;
-              pf[qb][kb][r >> 3][r & 7] = f32_to_bf16(p);
-            }
-          l[qb] += ls;
-        }
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-              const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-                  Vl + (db * 32 + l32) * L::vPitch + kb * 32 + t2 * 16 + 8 * h32);
-#pragma unroll
-              for (int qb = 0; qb < kQB; ++qb)
-                o[qb][db] =
-                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][t2], o[qb][db], 0, 0, 0);
-            }
-      }
-      if (s + 1 < n_steps) store_step<D>(regs, smem + ((s + 1) & 1) * L::bufElems, tid);
-      __syncthreads();
-    }
+      issue_step<D>(Kg, Vg, st, head, hkv, lds0 + (s % C::kStages) * C::kStageBytes, wave, lane);
+    };
+    // the first two steps go out before the Q loads so they overlap
+    if (n_steps > 0) issue(0);
+    if (n_steps > 1) issue(1);
 
-    // Epilogue: normalise, write O and the natural-log LSE (or a partial).
+    bf16x8 qf[D / 16];
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const float lt = l[qb] + __shfl_xor(l[qb], 32);
-      if (!valid[qb]) continue;
+    for (int t = 0; t < D / 16; ++t) {
+      const uint4 u = valid ? *reinterpret_cast<const uint4*>(Qg + qrow * D + 16 * t + 8 * h32)
+                            : make_uint4(0, 0, 0, 0);
+      qf[t] = __builtin_bit_cast(bf16x8, u);
+    }
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    float m_used = kNegInf, l = 0.f;
+
+    for (int s = 0; s < n_steps; ++s) {
+      // this wave's loads for step s are done once at most the next step's
+      // are outstanding; the barrier then makes every wave's loads visible
+      // and guarantees every wave finished step s-1 (whose stage is reused)
+      if (s + 1 < n_steps) wait_vmcnt<C::kDmaPerWave>();
+      else wait_vmcnt<0>();
+      block_barrier();
+      if (s + 2 < n_steps) issue(s + 2);
+
+      const Step st = item_step(tiles, s, n_draft, t0, sp);
+      const uint32_t stage = lds0 + (s % C::kStages) * C::kStageBytes;
+      int klo = 0, khi = kTileK;
+      bool lane_any = false, lane_full = true;
+      if (valid) {
+        step_bounds(st, lo_, an, blk, klo, khi);
+        lane_any = klo < khi;
+        lane_full = klo <= 0 && khi >= kTileK;
+      }
+      if (!__any(lane_any)) continue;
+      const bool wave_full = __all(lane_full);
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      const uint32_t kbase = opaque(stage + koff);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 kf = lds_read16(kbase + (kb * (D / 16) + t) * 1024);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], sacc[kb], 0, 0, 0);
+        }
+      if (!wave_full) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kappa = 32 * kb + 8 * (r >> 2) + 4 * h32 + (r & 3);
+            if (kappa < klo || kappa >= khi) sacc[kb][r] = kNegInf;
+          }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mt = mx * c;
+      const bool need = mt > m_used + 8.0f;
+      if (__any(need)) {
+        const float alpha = need ? exp2_fast(m_used - mt) : 1.0f;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+        if (need) m_used = mt;
+      }
+      const float msub = m_used == kNegInf ? 0.f : m_used;
+      bf16x8 pf[2][2];
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_fast(fmaf(sacc[kb][r], c, -msub));
+          ls += p;
+          pf[kb][r >> 3][r & 7] = f32_to_bf16(p);
+        }
+      l += ls;
+      const uint32_t vbase = opaque(stage + voff);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          // keys 32 kb + 16 t2 + {4 h32 + 0..3}, then {8 + 4 h32 + 0..3}
+          const uint32_t q0 = vbase + (8 * kb + 4 * t2) * C::kQuadBytes;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const short4v lo4 = ds_read_tr(q0 + db * 256);
+            const short4v hi4 = ds_read_tr(q0 + 2 * C::kQuadBytes + db * 256);
+            const bf16x8 vf = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][t2], o[db], 0, 0, 0);
+          }
+        }
+    }
+    // all waves are done with the ring before the next item's DMA reuses it
+    block_barrier();
+
+    const float lt = l + __shfl_xor(l, 32);
+    if (valid) {
       const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-      const float lse = lt > 0.f ? (m_used[qb] + log2f(lt)) * kLn2 : kNegInf;
+      const float lse = lt > 0.f ? (m_used + log2f(lt)) * kLn2 : kNegInf;
       if (slot < 0) {
-        const int64_t row = (int64_t)tok[qb] * hq + qh[qb];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -305,18 +319,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
             if (a.o_bf16) {
               bf16x4 w;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16(o[qb][db][4 * j + i] * inv);
-              *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.O) + row * D + d0) = w;
+              for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16(o[db][4 * j + i] * inv);
+              *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.O) + qrow * D + d0) = w;
             } else {
               f32x4 w;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) w[i] = o[qb][db][4 * j + i] * inv;
-              *reinterpret_cast<f32x4*>(static_cast<float*>(a.O) + row * D + d0) = w;
+              for (int i = 0; i < 4; ++i) w[i] = o[db][4 * j + i] * inv;
+              *reinterpret_cast<f32x4*>(static_cast<float*>(a.O) + qrow * D + d0) = w;
             }
           }
-        if (h32 == 0) a.LSE[row] = lse;
+        if (h32 == 0) a.LSE[qrow] = lse;
       } else {
-        const int64_t prow = (int64_t)slot * kQTile + rloc[qb];
+        const int64_t prow = (int64_t)slot * kQTile + rloc;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -324,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
             const int d0 = 32 * db + 8 * j + 4 * h32;
             f32x4 w;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = o[qb][db][4 * j + i] * inv;
+            for (int i = 0; i < 4; ++i) w[i] = o[db][4 * j + i] * inv;
             *reinterpret_cast<f32x4*>(a.ws_O + prow * D + d0) = w;
           }
         if (h32 == 0) a.ws_LSE[prow] = lse;
@@ -527,11 +541,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
 template <int D>
 hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   if (a.dtype_bf16) {
-    constexpr int bytes = Bf16Lds<D>::bytes;
+    constexpr int bytes = FwdCfg<D>::kLdsBytes;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_kernel<D>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
-    SKV_LAUNCH("fwd_bf16", fwd_bf16_kernel<D>, dim3(a.n_wg), dim3(kThreads), bytes, stream, a);
+    SKV_LAUNCH("fwd_bf16", fwd_bf16_kernel<D>, dim3(a.n_wg), dim3(FwdCfg<D>::kThreads), bytes,
+               stream, a);
   } else {
     constexpr int bytes = F32Lds<D>::bytes;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_f32_kernel<D>),
