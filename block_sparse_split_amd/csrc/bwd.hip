@@ -12,17 +12,20 @@
 //   dK = scale dS^T Q,  dV = P^T dO   (query heads of a kv head summed)
 //
 // Kernels (no atomics, deterministic):
-//   pre   D for every query row;
-//   dq    query-stationary, same work items and LPT queues as the forward:
-//         per 64-key step, S^T = K Q^T and dP^T = V dO^T (lanes own query
-//         columns), dS^T in registers, dQ^T += K^T dS^T with K^T staged in
-//         LDS in the permuted transposed layout; split query tiles write
-//         partial slots that a reduction kernel sums;
-//   dkdv  key-stationary: a wave owns 32 keys (K^T, V^T as B operands in
+//   pre   D and LSE*log2(e) for every query row, stored per kv head in the
+//         row order of the query tiles (so both can be DMA'd as rows);
+//   dq    query-stationary, the forward's work items and LPT queues, eight
+//         waves of 32 rows: per 64-key step S^T = K Q^T and dP^T = V dO^T
+//         (lanes own query columns), dS^T in registers, dQ^T += K^T dS^T;
+//         K (one rotated fragment-major copy serves both the natural and
+//         the transposed read) and V arrive by DMA in a 3-stage ring; split
+//         query tiles write partial slots that a reduction kernel sums;
+//   dkdv  key-stationary: a wave owns 32 keys (K^T, V^T B operands in
 //         registers) and walks 64-row tiles of the query rows that may see
 //         them: S = Q K^T and dP = dO V^T (lanes own key columns), then
-//         dV^T += dO^T P and dK^T += Q^T dS with Q^T / dO^T staged
-//         transposed; each key's gradients are written once.
+//         dV^T += dO^T P and dK^T += Q^T dS; Q and dO tiles (rotated
+//         fragment-major) and the row statistics arrive by DMA in a 3-stage
+//         ring; each key's gradients are written once.
 #include "launch.h"
 #include "tile_stage.h"
 #include "timing.h"
@@ -30,17 +33,22 @@
 namespace skv {
 namespace {
 
-// ---------------------------------------------------------------- D = rowsum
+// ---------------------------------------------------------------- pre
+// Row r (token, q-head h) of a kv head g = h / G has per-head index
+// rho = token * G + h % G.  Writes D and LSE * log2(e) (+inf for a row that
+// sees no key) at [g * Nq * G + rho].
 template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* O, const __bf16* dO, float* Dv,
-                                                      int64_t rows) {
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* O, const __bf16* dO,
+                                                      const float* LSE, float* Drm, float* L2rm,
+                                                      int64_t rows, int hq, int G) {
   constexpr int TPR = D / 8;
   constexpr int RPB = 256 / TPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int c = (threadIdx.x % TPR) * 8;
   float s = 0.f;
   if (row < rows) {
-    const uint4 a = ld16(O + row * D + c), b = ld16(dO + row * D + c);
+    const uint4 a = *reinterpret_cast<const uint4*>(O + row * D + c);
+    const uint4 b = *reinterpret_cast<const uint4*>(dO + row * D + c);
     const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -50,27 +58,55 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* O, const __b
   }
 #pragma unroll
   for (int o = TPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-  if (row < rows && c == 0) Dv[row] = s;
+  if (row < rows && c == 0) {
+    const int64_t token = row / hq;
+    const int h = (int)(row % hq);
+    const int64_t nqG = rows / hq * G;
+    const int64_t idx = (int64_t)(h / G) * nqG + token * G + h % G;
+    const float L = LSE[row];
+    Drm[idx] = s;
+    L2rm[idx] = L == kNegInf ? __builtin_inff() : L * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------- dQ
-constexpr int kQWaves = 8;
-constexpr int kQThreads = kQWaves * 64;
-
 template <int D>
-struct DqLds {
-  static constexpr int buf = 2 * Stage<D>::natElems + Stage<D>::trElems;  // K, V nat; K^T
-  static constexpr int bytes = 2 * buf * 2;
+struct DqCfg {
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = kWaves * 64;
+  // K (rotated fragment-major: natural and transposed reads), V (fragment-major)
+  static constexpr int kVOff = RTile<D>::kBytes;
+  static constexpr int kStageBytes = kVOff + Tile<D>::kBytes;
+  static constexpr int kStages = 3;
+  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kDmaPerWave = 2 * Tile<D>::kBlocks / kWaves;
 };
 
 template <int D>
-__global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
-  using St = Stage<D>;
-  using L = DqLds<D>;
-  extern __shared__ __align__(16) char smem_raw[];
-  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
+__device__ __forceinline__ void dq_issue(const __bf16* Kg, const __bf16* Vg, const Step& st,
+                                         int head, int hkv, uint32_t stage, int wave, int lane) {
+  using C = DqCfg<D>;
+  constexpr int B = Tile<D>::kBlocks;
+#pragma unroll
+  for (int i = 0; i < C::kDmaPerWave; ++i) {
+    const int u = wave * C::kDmaPerWave + i;
+    const bool isv = u >= B;
+    int row, col;
+    if (isv) frag_major_rc<D>(u - B, lane, row, col);
+    else rot_major_rc<D>(u, lane, row, col);
+    const int grow = min(row, st.n - 1);
+    dma16((isv ? Vg : Kg) + ((int64_t)(st.row + grow) * hkv + head) * D + col,
+          stage + (isv ? C::kVOff + (u - B) * 1024 : u * RTile<D>::kFragStride));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
+  using C = DqCfg<D>;
+  extern __shared__ __align__(16) char smem[];
   const int32_t* S = a.sched;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h32 = lane >> 5, l32 = lane & 31;
   const int G = S[H_G], hq = S[H_HQ], hkv = S[H_HKV], nb = S[H_NB];
   const int nq = nb * kBlock, rows_per_head = nq * G;
@@ -83,11 +119,10 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const float c = a.scale * kLog2e;
   const __bf16* Qg = static_cast<const __bf16*>(a.Q);
   const __bf16* dOg = static_cast<const __bf16*>(a.dO);
-  // staging roles: threads [0, nQuads) take K quads, the next nQuads V quads
-  const bool k_stager = tid < St::nQuads;
-  const bool v_stager = tid >= St::nQuads && tid < 2 * St::nQuads;
-  const int sq = k_stager ? tid : tid - St::nQuads;
-  const int sm = sq / St::CPR, sdr = sq % St::CPR;
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t knoff = rot_nat_offset(lane);
+  const uint32_t voff = C::kVOff + 16 * lane;
+  const uint32_t taoff = rot_tr_offset_a(lane), tboff = rot_tr_offset_b(lane);
 
   for (int qi = qbeg; qi < qend; ++qi) {
     const int32_t* it = items + queue[qi] * I_WORDS;
@@ -105,58 +140,42 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     const int blk = tok / kBlock;
     const int lo_ = valid ? los[blk] : 0, an = valid ? anchors[blk] : 0;
     const int64_t qrow = (int64_t)tok * hq + qh;
+
+    auto issue = [&](int s) {
+      const Step st = item_step(tiles, s, n_draft, t0, sp);
+      const __bf16* Kg = static_cast<const __bf16*>(st.draft ? a.Kd : a.K);
+      const __bf16* Vg = static_cast<const __bf16*>(st.draft ? a.Vd : a.V);
+      dq_issue<D>(Kg, Vg, st, head, hkv, lds0 + (s % C::kStages) * C::kStageBytes, wave, lane);
+    };
+    if (n_steps > 0) issue(0);
+    if (n_steps > 1) issue(1);
+
     bf16x8 qf[D / 16], df[D / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
-      const uint4 u = valid ? ld16(Qg + qrow * D + 16 * t + 8 * h32) : make_uint4(0, 0, 0, 0);
-      const uint4 v = valid ? ld16(dOg + qrow * D + 16 * t + 8 * h32) : make_uint4(0, 0, 0, 0);
+      const uint4 u = valid ? *reinterpret_cast<const uint4*>(Qg + qrow * D + 16 * t + 8 * h32)
+                            : make_uint4(0, 0, 0, 0);
+      const uint4 v = valid ? *reinterpret_cast<const uint4*>(dOg + qrow * D + 16 * t + 8 * h32)
+                            : make_uint4(0, 0, 0, 0);
       qf[t] = __builtin_bit_cast(bf16x8, u);
       df[t] = __builtin_bit_cast(bf16x8, v);
     }
-    float lse2 = __builtin_inff(), Dq = 0.f;
-    if (valid) {
-      const float L = a.LSE[qrow];
-      lse2 = L == kNegInf ? __builtin_inff() : L * kLog2e;
-      Dq = a.ws_D[qrow];
-    }
+    const int64_t srow = (int64_t)head * rows_per_head + rho;
+    const float lse2 = valid ? a.ws_L2[srow] : __builtin_inff();
+    const float Dq = valid ? a.ws_D[srow] : 0.f;
     f32x16 dq[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
 
-    Quad qd;
-    auto load = [&](int s) {
-      const Step st = item_step(tiles, s, n_draft, t0, sp);
-      const __bf16* src = static_cast<const __bf16*>(
-          k_stager ? (st.draft ? a.Kd : a.K) : (st.draft ? a.Vd : a.V));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 4 * sm + j;
-        qd.v[j] = row < st.n ? ld16(src + ((int64_t)(st.row + row) * hkv + head) * D + sdr * 8)
-                             : make_uint4(0, 0, 0, 0);
-      }
-    };
-    auto store = [&](int s) {
-      __bf16* buf = smem + (s & 1) * L::buf;
-      if (k_stager) {
-        store_nat<D>(buf, sm, sdr, qd);
-        store_tr<D>(buf + 2 * St::natElems, sm, sdr, qd);
-      } else if (v_stager) {
-        store_nat<D>(buf + St::natElems, sm, sdr, qd);
-      }
-    };
-    if (n_steps > 0 && (k_stager || v_stager)) {
-      load(0);
-      store(0);
-    }
-    __syncthreads();
     for (int s = 0; s < n_steps; ++s) {
+      if (s + 1 < n_steps) wait_vmcnt<C::kDmaPerWave>();
+      else wait_vmcnt<0>();
+      block_barrier();
+      if (s + 2 < n_steps) issue(s + 2);
       const Step st = item_step(tiles, s, n_draft, t0, sp);
-      if (s + 1 < n_steps && (k_stager || v_stager)) load(s + 1);
-      const __bf16* Kn = smem + (s & 1) * L::buf;
-      const __bf16* Vn = Kn + St::natElems;
-      const __bf16* Kt = Kn + 2 * St::natElems;
+      const uint32_t stage = lds0 + (s % C::kStages) * C::kStageBytes;
       int klo = 0, khi = kTileK;
       bool lane_any = false, lane_full = true;
       if (valid) {
@@ -164,44 +183,48 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
         lane_any = klo < khi;
         lane_full = klo <= 0 && khi >= kTileK;
       }
-      if (__any(lane_any)) {
-        f32x16 sacc[2], dp[2];
+      if (!__any(lane_any)) continue;
+      const bool full = __all(lane_full);
+      const int klo4 = klo - 4 * h32, khi4 = khi - 4 * h32;
+      const uint32_t kbase = opaque(stage + knoff);
+      const uint32_t vbase = opaque(stage + voff);
+      bf16x8 ds[2][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        // one 32-key block at a time keeps S, dP of a single block live
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 sacc, dp;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][r] = dp[kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) sacc[r] = dp[r] = 0.f;
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t)
+        for (int t = 0; t < D / 16; ++t) {
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rot_frag_nat<D>(kbase, kb, t), qf[t],
+                                                         sacc, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_nat<D>(vbase, kb, t), df[t], dp, 0,
+                                                       0, 0);
+        }
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_nat<D>(Kn, kb * 32, l32, h32, t),
-                                                               qf[t], sacc[kb], 0, 0, 0);
-            dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_nat<D>(Vn, kb * 32, l32, h32, t),
-                                                             df[t], dp[kb], 0, 0, 0);
-          }
-        const bool full = __all(lane_full);
-        bf16x8 ds[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kappa = 32 * kb + 8 * (r >> 2) + 4 * h32 + (r & 3);
-            float p = exp2_fast(fmaf(sacc[kb][r], c, -lse2));
-            if (!full && (kappa < klo || kappa >= khi)) p = 0.f;
-            ds[kb][r >> 3][r & 7] = f32_to_bf16(p * (dp[kb][r] - Dq));
-          }
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2)
-              dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  frag_tr<D>(Kt, db * 32, l32, h32, kb, t2), ds[kb][t2], dq[db], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) {
+          // key 32 kb + 8 (r / 4) + 4 h32 + r % 4 against bounds shifted by 4 h32
+          const int kc = 32 * kb + 8 * (r >> 2) + (r & 3);
+          float p = exp2_fast(fmaf(sacc[r], c, -lse2));
+          if (!full && (kc < klo4 || kc >= khi4)) p = 0.f;
+          ds[kb][r >> 3][r & 7] = f32_to_bf16(p * (dp[r] - Dq));
+        }
       }
-      if (s + 1 < n_steps) store(s + 1);
-      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t ta = opaque(stage + taoff);
+      const uint32_t tb = opaque(stage + tboff);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rot_frag_tr<D>(ta, tb, db, kb, t2),
+                                                             ds[kb][t2], dq[db], 0, 0, 0);
     }
+    block_barrier();
     if (valid) {
       float* dst = slot < 0 ? a.dQ + qrow * D : a.ws_dQ + ((int64_t)slot * kQTile + rloc) * D;
 #pragma unroll
@@ -244,27 +267,33 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const int32_t* S, const 
 }
 
 // ---------------------------------------------------------------- dK, dV
-constexpr int kKWaves = 4;
-constexpr int kKThreads = kKWaves * 64;
-
 template <int D>
-struct KvLds {
-  // Q nat, dO nat, Q^T, dO^T, then lse2[64] and D[64] (fp32)
-  static constexpr int bufElems = 2 * Stage<D>::natElems + 2 * Stage<D>::trElems + 2 * 64 * 2;
-  static constexpr int bytes = 2 * bufElems * 2;
+struct KvCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = kWaves * 64;
+  // Q, dO (rotated fragment-major), then 1 KB of row statistics
+  static constexpr int kOOff = RTile<D>::kBytes;
+  static constexpr int kStatOff = 2 * RTile<D>::kBytes;
+  static constexpr int kStageBytes = kStatOff + 1024;
+  static constexpr int kStages = 3;
+  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kDmaPerWave = 2 * RTile<D>::kFrags / kWaves;
 };
 
 template <int D>
-__global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  using St = Stage<D>;
-  using L = KvLds<D>;
-  extern __shared__ __align__(16) char smem_raw[];
-  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
+__global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using C = KvCfg<D>;
+  constexpr int B = Tile<D>::kBlocks;
+  extern __shared__ __align__(16) char smem[];
   const int32_t* S = a.sched;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h32 = lane >> 5, l32 = lane & 31;
   const int G = S[H_G], hq = S[H_HQ], hkv = S[H_HKV], nb = S[H_NB];
   const int rows_per_block = kBlock * G;
+  const int rows_per_head = nb * rows_per_block;
+  // G is a power of two: row -> (token, head) and row -> block are shifts
+  const int lgG = __builtin_ctz(G), lgR = 4 + lgG;
   const int32_t* anchors = S + S[H_OFF_ANCHORS];
   const int32_t* los = S + S[H_OFF_LO];
   const int32_t* tiles = S + S[H_OFF_TILES];
@@ -274,8 +303,9 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const float c = a.scale * kLog2e;
   const __bf16* Qg = static_cast<const __bf16*>(a.Q);
   const __bf16* dOg = static_cast<const __bf16*>(a.dO);
-  const bool stager = tid < St::nQuads;
-  const int sm = tid / St::CPR, sdr = tid % St::CPR;
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t noff = rot_nat_offset(lane);
+  const uint32_t taoff = rot_tr_offset_a(lane), tboff = rot_tr_offset_b(lane);
 
   for (int qi = qbeg; qi < qend; ++qi) {
     const int32_t* it = kvs + queue[qi] * K_WORDS;
@@ -296,14 +326,45 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
     const bool kvalid = l32 < nk;
     const int mypos = kpos + l32;
+    const int kp0 = kpos, kp1 = kpos + nk;
+    const int r_begin = b0 * rows_per_block, r_end = b1 * rows_per_block;
+    const int n_rt = (r_end - r_begin + kTileK - 1) / kTileK;
+
+    auto issue = [&](int rt) {
+      const uint32_t stage = lds0 + (rt % C::kStages) * C::kStageBytes;
+      const int rho0 = r_begin + kTileK * rt;
+#pragma unroll
+      for (int i = 0; i < C::kDmaPerWave; ++i) {
+        const int u = wave * C::kDmaPerWave + i;
+        const bool iso = u >= RTile<D>::kFrags;  // dO after Q
+        const int f = iso ? u - RTile<D>::kFrags : u;
+        int row, col;
+        rot_major_rc<D>(f, lane, row, col);
+        const int rho = min(rho0 + row, r_end - 1);
+        const int64_t grow = (int64_t)(rho >> lgG) * hq + head * G + (rho & (G - 1));
+        dma16((iso ? dOg : Qg) + grow * D + col,
+              stage + (iso ? C::kOOff : 0) + f * RTile<D>::kFragStride);
+      }
+      if (wave == 0) {
+        // lanes 0-15: LSE*log2e of rows rho0 .. +63; 16-31: D; the rest pad
+        const float* srcs = (lane >> 4) & 1 ? a.ws_D : a.ws_L2;
+        const int r = min(rho0 + 4 * (lane & 15), rows_per_head - 4);
+        dma16(srcs + (int64_t)head * rows_per_head + r, stage + C::kStatOff);
+      }
+    };
+    if (n_rt > 0) issue(0);
+    if (n_rt > 1) issue(1);
+
     const __bf16* Ksrc = static_cast<const __bf16*>(draft ? a.Kd : a.K);
     const __bf16* Vsrc = static_cast<const __bf16*>(draft ? a.Vd : a.V);
-    const int64_t kaddr = ((int64_t)(krow + l32) * hkv + head) * D;
+    const int64_t kaddr = ((int64_t)(krow + (kvalid ? l32 : 0)) * hkv + head) * D;
     bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
-      const uint4 u = kvalid ? ld16(Ksrc + kaddr + 16 * t + 8 * h32) : make_uint4(0, 0, 0, 0);
-      const uint4 v = kvalid ? ld16(Vsrc + kaddr + 16 * t + 8 * h32) : make_uint4(0, 0, 0, 0);
+      const uint4 u = kvalid ? *reinterpret_cast<const uint4*>(Ksrc + kaddr + 16 * t + 8 * h32)
+                             : make_uint4(0, 0, 0, 0);
+      const uint4 v = kvalid ? *reinterpret_cast<const uint4*>(Vsrc + kaddr + 16 * t + 8 * h32)
+                             : make_uint4(0, 0, 0, 0);
       kf[t] = __builtin_bit_cast(bf16x8, u);
       vf[t] = __builtin_bit_cast(bf16x8, v);
     }
@@ -312,119 +373,79 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) dk[db][r] = dv[db][r] = 0.f;
-    // wave-uniform key interval for skipping row tiles
-    const int kp0 = kpos, kp1 = kpos + nk;
 
-    const int r_begin = b0 * rows_per_block, r_end = b1 * rows_per_block;
-    const int n_rt = (r_end - r_begin + 63) / 64;
-    Quad qq, qo;
-    auto load = [&](int rt) {
-      if (!stager) return;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rho = r_begin + 64 * rt + 4 * sm + j;
-        if (rho < r_end) {
-          const int64_t row = (int64_t)(rho / G) * hq + head * G + rho % G;
-          qq.v[j] = ld16(Qg + row * D + sdr * 8);
-          qo.v[j] = ld16(dOg + row * D + sdr * 8);
-        } else {
-          qq.v[j] = qo.v[j] = make_uint4(0, 0, 0, 0);
-        }
-      }
-    };
-    auto store = [&](int rt) {
-      __bf16* buf = smem + (rt & 1) * L::bufElems;
-      if (stager) {
-        store_nat<D>(buf, sm, sdr, qq);
-        store_nat<D>(buf + St::natElems, sm, sdr, qo);
-        store_tr<D>(buf + 2 * St::natElems, sm, sdr, qq);
-        store_tr<D>(buf + 2 * St::natElems + St::trElems, sm, sdr, qo);
-      }
-      if (tid < 64) {
-        float* f = reinterpret_cast<float*>(buf + 2 * St::natElems + 2 * St::trElems);
-        const int rho = r_begin + 64 * rt + tid;
-        float l2 = __builtin_inff(), dd = 0.f;
-        if (rho < r_end) {
-          const int64_t row = (int64_t)(rho / G) * hq + head * G + rho % G;
-          const float Lr = a.LSE[row];
-          l2 = Lr == kNegInf ? __builtin_inff() : Lr * kLog2e;
-          dd = a.ws_D[row];
-        }
-        f[tid] = l2;
-        f[64 + tid] = dd;
-      }
-    };
-    if (n_rt > 0) {
-      load(0);
-      store(0);
-    }
-    __syncthreads();
     for (int rt = 0; rt < n_rt; ++rt) {
-      if (rt + 1 < n_rt) load(rt + 1);
-      const __bf16* buf = smem + (rt & 1) * L::bufElems;
-      const __bf16* Qn = buf;
-      const __bf16* On = buf + St::natElems;
-      const __bf16* Qt = buf + 2 * St::natElems;
-      const __bf16* Ot = Qt + St::trElems;
-      const float* lse2s = reinterpret_cast<const float*>(Ot + St::trElems);
-      const float* Ds = lse2s + 64;
-      const int rho0 = r_begin + 64 * rt;
+      // this wave's DMA for tile rt is done once at most tile rt+1's is out
+      if (rt + 1 < n_rt) {
+        if (wave == 0) wait_vmcnt<C::kDmaPerWave + 1>();
+        else wait_vmcnt<C::kDmaPerWave>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      block_barrier();
+      if (rt + 2 < n_rt) issue(rt + 2);
+      const int rho0 = r_begin + kTileK * rt;
       // does any row of this tile see any of this wave's keys?
-      const int bA = rho0 / rows_per_block;
-      const int bB = min(b1, (rho0 + 63) / rows_per_block + 1);
+      const int bA = rho0 >> lgR;
+      const int bB = min(b1, ((rho0 + kTileK - 1) >> lgR) + 1);
       bool any = false;
       for (int b = bA; b < bB && nk > 0; ++b) {
         if (draft) any = any || (b * kBlock < kp1 && (b + 1) * kBlock > kp0);
         else any = any || (max(los[b], kp0) < min(anchors[b], kp1));
       }
-      if (any) {
-        bf16x8 pb[2][2], dsb[2][2];
+      if (!any) continue;
+      const uint32_t stage = lds0 + (rt % C::kStages) * C::kStageBytes;
+      const uint32_t qfb = opaque(stage + noff);
+      const uint32_t ofb = qfb + C::kOOff;
+      const uint32_t stat = stage + C::kStatOff;
+      bf16x8 pb[2][2], dsb[2][2];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          f32x16 sacc, dp;
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 sacc, dp;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[r] = dp[r] = 0.f;
+        for (int r = 0; r < 16; ++r) sacc[r] = dp[r] = 0.f;
 #pragma unroll
-          for (int t = 0; t < D / 16; ++t) {
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_nat<D>(Qn, qb * 32, l32, h32, t),
-                                                           kf[t], sacc, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_nat<D>(On, qb * 32, l32, h32, t),
-                                                         vf[t], dp, 0, 0, 0);
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r8 = qb * 32 + 8 * j;              // first of 8 rows, same block
-            const int bj = (rho0 + r8) / rows_per_block;
-            bool vis;
-            if (draft) vis = kvalid && (mypos / kBlock) == bj;
-            else vis = kvalid && bj < nb && mypos >= los[min(bj, nb - 1)] &&
-                       mypos < anchors[min(bj, nb - 1)];
-            const f32x4 l2 = *reinterpret_cast<const f32x4*>(lse2s + r8 + 4 * h32);
-            const f32x4 dd = *reinterpret_cast<const f32x4*>(Ds + r8 + 4 * h32);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 4 * j + i;
-              const float p = vis ? exp2_fast(fmaf(sacc[r], c, -l2[i])) : 0.f;
-              pb[qb][r >> 3][r & 7] = f32_to_bf16(p);
-              dsb[qb][r >> 3][r & 7] = f32_to_bf16(p * (dp[r] - dd[i]));
-            }
-          }
+        for (int t = 0; t < D / 16; ++t) {
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rot_frag_nat<D>(qfb, qb, t), kf[t],
+                                                         sacc, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rot_frag_nat<D>(ofb, qb, t), vf[t], dp, 0,
+                                                       0, 0);
         }
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int j = 0; j < 4; ++j) {
+          const int r8 = qb * 32 + 8 * j;  // first of 8 rows, all in one block
+          const int rr = rho0 + r8;
+          const int bj = min(rr >> lgR, nb - 1);
+          bool vis;
+          if (draft) vis = (mypos / kBlock) == bj;
+          else vis = mypos >= los[bj] && mypos < anchors[bj];
+          vis = vis && kvalid && rr < r_end;
+          const f32x4 l2 = lds_read_f4(stat + 4 * (r8 + 4 * h32));
+          const f32x4 dd = lds_read_f4(stat + 256 + 4 * (r8 + 4 * h32));
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-              dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  frag_tr<D>(Ot, db * 32, l32, h32, qb, t2), pb[qb][t2], dv[db], 0, 0, 0);
-              dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  frag_tr<D>(Qt, db * 32, l32, h32, qb, t2), dsb[qb][t2], dk[db], 0, 0, 0);
-            }
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * j + i;
+            const float p = vis ? exp2_fast(fmaf(sacc[r], c, -l2[i])) : 0.f;
+            pb[qb][r >> 3][r & 7] = f32_to_bf16(p);
+            dsb[qb][r >> 3][r & 7] = f32_to_bf16(p * (dp[r] - dd[i]));
+          }
+        }
       }
-      if (rt + 1 < n_rt) store(rt + 1);
-      __syncthreads();
+      const uint32_t qta = opaque(stage + taoff), qtb = opaque(stage + tboff);
+      const uint32_t ota = qta + C::kOOff, otb = qtb + C::kOOff;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rot_frag_tr<D>(ota, otb, db, qb, t2),
+                                                             pb[qb][t2], dv[db], 0, 0, 0);
+            dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rot_frag_tr<D>(qta, qtb, db, qb, t2),
+                                                             dsb[qb][t2], dk[db], 0, 0, 0);
+          }
     }
+    block_barrier();
     if (kvalid) {
       const int64_t orow = (int64_t)(krow + l32) * hkv + head;
       void* dKp = draft ? a.dKd : a.dK;
@@ -463,24 +484,26 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.nb * kBlock * a.hq;
   constexpr int RPB = 256 / (D / 8);
   SKV_LAUNCH("bwd_pre", bwd_pre_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256), 0, s,
-                     static_cast<const __bf16*>(a.O), static_cast<const __bf16*>(a.dO), a.ws_D,
-                     rows);
+             static_cast<const __bf16*>(a.O), static_cast<const __bf16*>(a.dO), a.LSE, a.ws_D,
+             a.ws_L2, rows, a.hq, a.hq / a.hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_kernel<D>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, DqLds<D>::bytes);
+                          hipFuncAttributeMaxDynamicSharedMemorySize, DqCfg<D>::kLdsBytes);
   if (e != hipSuccess) return e;
-  SKV_LAUNCH("bwd_dq", bwd_dq_kernel<D>, dim3(a.n_wg), dim3(kQThreads), DqLds<D>::bytes, s, a);
+  SKV_LAUNCH("bwd_dq", bwd_dq_kernel<D>, dim3(a.n_wg), dim3(DqCfg<D>::kThreads),
+             DqCfg<D>::kLdsBytes, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.n_split > 0) {
-    SKV_LAUNCH("dq_reduce", dq_reduce_kernel<D>, dim3(a.n_split * (kQTile / RPB)), dim3(256), 0, s,
-                       a.sched, a.ws_dQ, a.dQ);
+    SKV_LAUNCH("dq_reduce", dq_reduce_kernel<D>, dim3(a.n_split * (kQTile / RPB)), dim3(256), 0,
+               s, a.sched, a.ws_dQ, a.dQ);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, KvLds<D>::bytes);
+                          hipFuncAttributeMaxDynamicSharedMemorySize, KvCfg<D>::kLdsBytes);
   if (e != hipSuccess) return e;
-  SKV_LAUNCH("bwd_dkdv", bwd_dkdv_kernel<D>, dim3(a.n_wg), dim3(kKThreads), KvLds<D>::bytes, s, a);
+  SKV_LAUNCH("bwd_dkdv", bwd_dkdv_kernel<D>, dim3(a.n_wg), dim3(KvCfg<D>::kThreads),
+             KvCfg<D>::kLdsBytes, s, a);
   return hipGetLastError();
 }
 

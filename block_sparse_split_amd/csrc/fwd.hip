@@ -28,8 +28,8 @@
 // the current step computes.  Tiles that straddle an anchor bound are masked
 // per element; fully visible tiles skip the mask, invisible ones skip the
 // MFMAs.
-#include "device_common.h"
 #include "launch.h"
+#include "tile_stage.h"
 #include "timing.h"
 
 namespace skv {
@@ -58,72 +58,16 @@ template <int D>
 struct FwdCfg {
   static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kTileBytes = kTileK * D * 2;        // 16 KB (d=128) / 8 KB
+  static constexpr int kTileBytes = Tile<D>::kBytes;       // 16 KB (d=128) / 8 KB
   static constexpr int kStageBytes = 2 * kTileBytes;       // K then V
-  static constexpr int kStages = 3;
+  static constexpr int kStages = 4;
   static constexpr int kLdsBytes = kStages * kStageBytes;
-  static constexpr int kKFrags = 2 * (D / 16);             // 1 KB K fragments per tile
-  static constexpr int kQuadBytes = 4 * D * 2;             // one 4-key quad of V
   static constexpr int kDmaPerWave = 2 * (kTileBytes / 1024) / kWaves;
 };
 
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// 16 bytes per lane from global memory straight into LDS at
-// lds_base + 16 * lane (lds_base wave-uniform).  Issued as inline asm so the
-// compiler neither serialises it against LDS reads nor waits on it; the
-// kernel waits with explicit vmcnt counts before its barriers.
-__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gsrc), "s"(lds_base) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// s_waitcnt vmcnt(n) (n < 16) leaving lgkmcnt/expcnt alone.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef const __attribute__((address_space(3))) char* lds_cptr;
-
-// An LDS byte address the optimiser cannot see through: per-step bases are
-// laundered so that each read becomes `base + immediate offset` instead of
-// one loop-invariant address register per read.
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
-__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-      static_cast<uintptr_t>(addr));
-}
-
-__device__ __forceinline__ short4v ds_read_tr(uint32_t addr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) short4v*)(static_cast<uintptr_t>(addr)));
-}
-
-// Issue this wave's share of the DMA for one step into `stage` (LDS bytes).
-// DMA block u < kKFrags is K fragment (kb, t) = (u / (D/16), u % (D/16)):
-// lane i loads row 32 kb + i % 32, d = 16 t + 8 (i / 32).  The other blocks
-// are V: byte 16 i of block j lies in quad q = (1024 j + 16 i) / quadBytes at
-// offset w, holding row 4 q + (w % 128) / 32 and d = 16 (w / 128) + 8 ((w % 32) / 16).
-// Rows past the end of a ragged step repeat the last valid row (their keys are
-// masked, the values stay finite).
+// Issue this wave's share of the DMA for one step into `stage` (LDS bytes):
+// K fragment-major, then V block-major.  Rows past the end of a ragged step
+// repeat the last valid row (their keys are masked, the values stay finite).
 template <int D>
 __device__ __forceinline__ void issue_step(const __bf16* Kg, const __bf16* Vg, const Step& st,
                                            int head, int hkv, uint32_t stage, int wave,
@@ -133,23 +77,24 @@ __device__ __forceinline__ void issue_step(const __bf16* Kg, const __bf16* Vg, c
   for (int i = 0; i < C::kDmaPerWave; ++i) {
     const int u = wave * C::kDmaPerWave + i;
     int row, col;
-    const __bf16* src;
-    if (u < C::kKFrags) {
-      row = (u / (D / 16)) * 32 + (lane & 31);
-      col = 16 * (u % (D / 16)) + 8 * (lane >> 5);
-      src = Kg;
-    } else {
-      const int byte = (u - C::kKFrags) * 1024 + 16 * lane;
-      const int q = byte / C::kQuadBytes, w = byte % C::kQuadBytes;
-      row = 4 * q + (w & 127) / 32;
-      col = 16 * (w / 128) + 8 * ((w & 31) / 16);
-      src = Vg;
-    }
+    const bool isv = u >= Tile<D>::kBlocks;
+    if (isv) block_major_rc<D>(u - Tile<D>::kBlocks, lane, row, col);
+    else frag_major_rc<D>(u, lane, row, col);
     const int grow = min(row, st.n - 1);
-    dma16(src + ((int64_t)(st.row + grow) * hkv + head) * D + col, stage + u * 1024);
+    dma16((isv ? Vg : Kg) + ((int64_t)(st.row + grow) * hkv + head) * D + col, stage + u * 1024);
   }
 }
 
+// Two groups of four waves (waves w and w + 4 share a SIMD) run the same
+// per-step work -- QK (MFMA), softmax (VALU), PV (MFMA) -- half a step apart.
+// Every half step ends in a workgroup barrier; within a half step one group
+// issues PV of its previous step and QK of its next step while the other
+// group runs the softmax, so each SIMD always has one wave feeding the matrix
+// cores and one feeding the vector ALU.  Half step k (k = -1 .. 2n):
+//   group A (waves 0-3): k odd  -> PV(s-1), QK(s) with s = (k+1)/2;  k even -> softmax(k/2)
+//   group B (waves 4-7): k even -> PV(s-1), QK(s) with s = k/2;      k odd  -> softmax((k-1)/2)
+// Tile s is read in half steps 2s-1 .. 2s+2; a 4-stage ring re-fills the
+// stage of tile j with tile j+4 at the start of half step 2j+3.
 template <int D>
 __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
@@ -157,6 +102,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
   const int32_t* S = a.sched;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool groupA = wave < 4;
   const int h32 = lane >> 5, l32 = lane & 31;
   const int G = S[H_G], hq = S[H_HQ], hkv = S[H_HKV], nb = S[H_NB];
   const int nq = nb * kBlock, rows_per_head = nq * G;
@@ -169,12 +115,10 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
   const float c = a.scale * kLog2e;
   const __bf16* Qg = static_cast<const __bf16*>(a.Q);
   const uint32_t lds0 = lds_addr(smem);
-  // per-lane LDS byte offsets inside a stage: K fragment lane slot, and the
-  // transposed V read (16-lane group G reads quad ... + G / 2, block
-  // 2 db + G % 2, 8 bytes per lane)
+  // per-lane LDS byte offsets inside a stage: K fragment lane slot and the
+  // transposed V read
   const uint32_t koff = 16 * lane;
-  const uint32_t voff = C::kTileBytes + (lane >> 5) * C::kQuadBytes + ((lane >> 4) & 1) * 128 +
-                        8 * (lane & 15);
+  const uint32_t voff = C::kTileBytes + tr_lane_offset<D>(lane);
 
   for (int qi = qbeg; qi < qend; ++qi) {
     const int32_t* it = items + queue[qi] * I_WORDS;
@@ -193,15 +137,17 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
     const int lo_ = valid ? los[blk] : 0, an = valid ? anchors[blk] : 0;
     const int64_t qrow = (int64_t)tok * hq + qh;
 
+    auto stage_of = [&](int s) { return lds0 + (s & (C::kStages - 1)) * C::kStageBytes; };
     auto issue = [&](int s) {
       const Step st = item_step(tiles, s, n_draft, t0, sp);
       const __bf16* Kg = static_cast<const __bf16*>(st.draft ? a.Kd : a.K);
       const __bf16* Vg = static_cast<const __bf16*>(st.draft ? a.Vd : a.V);
-      issue_step<D>(Kg, Vg, st, head, hkv, lds0 + (s % C::kStages) * C::kStageBytes, wave, lane);
+      issue_step<D>(Kg, Vg, st, head, hkv, stage_of(s), wave, lane);
     };
-    // the first two steps go out before the Q loads so they overlap
-    if (n_steps > 0) issue(0);
-    if (n_steps > 1) issue(1);
+    // fill the ring before the Q loads so they overlap
+#pragma unroll
+    for (int s = 0; s < C::kStages; ++s)
+      if (s < n_steps) issue(s);
 
     bf16x8 qf[D / 16];
 #pragma unroll
@@ -216,18 +162,52 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
     float m_used = kNegInf, l = 0.f;
+    // P of the step whose softmax ran last, carried to the next MFMA phase
+    bf16x8 pf[2][2];
+    bool p_act = false;
 
-    for (int s = 0; s < n_steps; ++s) {
-      // this wave's loads for step s are done once at most the next step's
-      // are outstanding; the barrier then makes every wave's loads visible
-      // and guarantees every wave finished step s-1 (whose stage is reused)
-      if (s + 1 < n_steps) wait_vmcnt<C::kDmaPerWave>();
-      else wait_vmcnt<0>();
+    // Barrier of half step k, with the ring bookkeeping of odd half steps:
+    // before it, wait for this wave's share of tile (k+1)/2 (at most the
+    // following tile's loads may still be in flight); after it, re-fill the
+    // stage that tile (k-3)/2 has left with tile (k-3)/2 + kStages.
+    auto half_step = [&](int k) {
+      if ((k & 1) != 0) {
+        const int sn = (k + 1) / 2;
+        if (sn < n_steps) {
+          if (sn + 1 < n_steps) wait_vmcnt<C::kDmaPerWave>();
+          else wait_vmcnt<0>();
+        }
+      }
       block_barrier();
-      if (s + 2 < n_steps) issue(s + 2);
-
-      const Step st = item_step(tiles, s, n_draft, t0, sp);
-      const uint32_t stage = lds0 + (s % C::kStages) * C::kStageBytes;
+      if ((k & 1) != 0 && k >= 3) {
+        const int sj = (k - 3) / 2 + C::kStages;
+        if (sj < n_steps) issue(sj);
+      }
+    };
+    // MFMA phase p runs in half step 2p - 1 (group A) or 2p (group B), the
+    // softmax of step p in the half step after it.  Group B starts with an
+    // idle half step and skips the (empty) last one, so both groups pass the
+    // same 2 n + 2 barriers.
+    const int k0 = groupA ? -1 : 0;
+    // O^T += V^T P^T for the tile in `stage` (P from the last softmax)
+    auto pv = [&](int s) {
+      const uint32_t vbase = opaque(stage_of(s) + voff);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(vbase, db, kb, t2),
+                                                            pf[kb][t2], o[db], 0, 0, 0);
+    };
+    if (!groupA) half_step(-1);
+    for (int p = 0; p < n_steps; ++p) {
+      half_step(2 * p + k0);
+      if (p_act) pv(p - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // QK of step p
+      const Step st = item_step(tiles, p, n_draft, t0, sp);
       int klo = 0, khi = kTileK;
       bool lane_any = false, lane_full = true;
       if (valid) {
@@ -235,74 +215,70 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
         lane_any = klo < khi;
         lane_full = klo <= 0 && khi >= kTileK;
       }
-      if (!__any(lane_any)) continue;
-      const bool wave_full = __all(lane_full);
+      const bool s_act = __any(lane_any);
+      const bool s_full = __all(lane_full);
       f32x16 sacc[2];
+      if (s_act) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-      const uint32_t kbase = opaque(stage + koff);
+          for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+        const uint32_t kbase = opaque(stage_of(p) + koff);
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t)
+        for (int t = 0; t < D / 16; ++t)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 kf = lds_read16(kbase + (kb * (D / 16) + t) * 1024);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], sacc[kb], 0, 0, 0);
+          for (int kb = 0; kb < 2; ++kb)
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_nat<D>(kbase, kb, t), qf[t],
+                                                               sacc[kb], 0, 0, 0);
+      }
+      half_step(2 * p + k0 + 1);
+      // softmax of step p
+      p_act = s_act;
+      if (s_act) {
+        if (!s_full) {
+          // key kappa = 32 kb + 8 (r / 4) + 4 h32 + r % 4: fold the lane
+          // part into the bounds so the per-element index is a constant
+          const int lo4 = klo - 4 * h32, hi4 = khi - 4 * h32;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kc = 32 * kb + 8 * (r >> 2) + (r & 3);
+              if (kc < lo4 || kc >= hi4) sacc[kb][r] = kNegInf;
+            }
         }
-      if (!wave_full) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mt = mx * c;
+        const bool need = mt > m_used + 8.0f;
+        if (__any(need)) {
+          const float alpha = need ? exp2_fast(m_used - mt) : 1.0f;
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+          if (need) m_used = mt;
+        }
+        const float msub = m_used == kNegInf ? 0.f : m_used;
+        float ls = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int kappa = 32 * kb + 8 * (r >> 2) + 4 * h32 + (r & 3);
-            if (kappa < klo || kappa >= khi) sacc[kb][r] = kNegInf;
+            const float pv_ = exp2_fast(fmaf(sacc[kb][r], c, -msub));
+            ls += pv_;
+            pf[kb][r >> 3][r & 7] = f32_to_bf16(pv_);
           }
+        l += ls;
       }
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mt = mx * c;
-      const bool need = mt > m_used + 8.0f;
-      if (__any(need)) {
-        const float alpha = need ? exp2_fast(m_used - mt) : 1.0f;
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-        if (need) m_used = mt;
-      }
-      const float msub = m_used == kNegInf ? 0.f : m_used;
-      bf16x8 pf[2][2];
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(fmaf(sacc[kb][r], c, -msub));
-          ls += p;
-          pf[kb][r >> 3][r & 7] = f32_to_bf16(p);
-        }
-      l += ls;
-      const uint32_t vbase = opaque(stage + voff);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          // keys 32 kb + 16 t2 + {4 h32 + 0..3}, then {8 + 4 h32 + 0..3}
-          const uint32_t q0 = vbase + (8 * kb + 4 * t2) * C::kQuadBytes;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const short4v lo4 = ds_read_tr(q0 + db * 256);
-            const short4v hi4 = ds_read_tr(q0 + 2 * C::kQuadBytes + db * 256);
-            const bf16x8 vf = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][t2], o[db], 0, 0, 0);
-          }
-        }
     }
+    // last MFMA phase: PV of the last step only
+    half_step(2 * n_steps + k0);
+    if (p_act) pv(n_steps - 1);
+    if (groupA) half_step(2 * n_steps + k0 + 1);
     // all waves are done with the ring before the next item's DMA reuses it
     block_barrier();
 

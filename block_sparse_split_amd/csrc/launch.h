@@ -37,7 +37,8 @@ struct BwdArgs {
   void* dV;
   void* dKd;                // [Nq, hkv, d]
   void* dVd;
-  float* ws_D;              // [Nq, hq] rowsum(dO * O)
+  float* ws_D;              // rowsum(dO * O), [hkv][Nq * G] in query-tile row order
+  float* ws_L2;             // LSE * log2(e) (+inf: no key), same layout
   float* ws_dQ;             // partial slots [n_slots, 256, d]
   int32_t grad_bf16, dtype_bf16;
   int32_t hq, hkv, d, nb, n_local;

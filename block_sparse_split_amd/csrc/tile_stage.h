@@ -1,84 +1,182 @@
-// Staging of 64-row bf16 tiles from HBM into LDS (gfx950 kernels).
+// Direct-to-LDS tile staging and LDS fragment reads (gfx950 kernels).
 //
-// A thread owns a "quad": rows 4m .. 4m+3 of a 64-row tile at columns
-// 8*dr .. 8*dr+7 (four 16-byte loads; consecutive threads take consecutive
-// column groups of the same rows, so a wave reads whole 256-byte rows).  The
-// quad is written to LDS in one or both of two layouts:
-//   natural     [row][col]            row pitch D + 8 elements;
-//   transposed  [col][row-permuted]   row pitch 64 + 8 elements, where rows
-//     4m..4m+3 of each 16-row group are stored at offset 0, 8, 4, 12 for
-//     m % 4 = 0, 1, 2, 3.
-// The permutation makes the 8 bf16 that one lane of a 32x32x16 MFMA needs as
-// its A operand contiguous when the matching B operand comes straight out of
-// a 32x32 accumulator (whose lanes hold rows 8j + 4*(lane/32) + i).  The
-// pitches add 16 bytes per row so that 16 lanes reading 16 bytes each at
-// the same column of consecutive rows hit distinct LDS banks.
+// Tiles of 64 rows x D bf16 (rows are keys or query rows) are copied from
+// HBM into LDS with global_load_lds_dwordx4: every lane of a wave moves 16
+// bytes and writes them at lds_base + 16 * lane.  Because each lane chooses
+// its own global address, a tile can be written directly in the order the
+// MFMAs consume it, in one of two layouts (both 64 x D x 2 bytes):
+//
+//   fragment-major  1 KB block (kb, t), kb in {0,1}, t < D/16, holds the A
+//                   operand of a 32x32x16 MFMA with lane = row: lane L's 16
+//                   bytes are row 32 kb + L % 32, columns 16 t + 8 (L / 32).
+//   block-major     4-row quads (8 D bytes each) of 4 x 16 blocks (128 bytes,
+//                   row-major inside).  A 16-lane ds_read_b64_tr_b16 over one
+//                   block returns, in lane i, column i of its 4 rows; two such
+//                   reads form the A operand with lane = column and the 8
+//                   rows {4h + 0..3, 8 + 4h + 0..3} that a 32x32 accumulator
+//                   lane (half h) holds, so results feed MFMAs without any
+//                   register transpose.
+//
+// Reads are contiguous per instruction (no bank conflicts) and use one base
+// register plus an immediate offset.  The DMA is issued as inline asm so the
+// compiler neither waits on it nor serialises it against LDS reads; kernels
+// wait with explicit vmcnt counts and a bare s_barrier.
 #pragma once
 #include "device_common.h"
 
 namespace skv {
 
+typedef short short4v __attribute__((ext_vector_type(4)));
+
 template <int D>
-struct Stage {
-  static constexpr int natPitch = D + 8;
-  static constexpr int trPitch = kTileK + 8;
-  static constexpr int natElems = kTileK * natPitch;
-  static constexpr int trElems = D * trPitch;
-  static constexpr int CPR = D / 8;                 // 16-byte column groups
-  static constexpr int nQuads = (kTileK / 4) * CPR;  // quads per 64-row tile
+struct Tile {
+  static constexpr int kBytes = kTileK * D * 2;   // 16 KB for d = 128
+  static constexpr int kBlocks = kBytes / 1024;   // DMA blocks per tile
+  static constexpr int kFragsPerKb = D / 16;      // fragment-major: t range
+  static constexpr int kQuadBytes = 4 * D * 2;    // block-major: one 4-row quad
 };
 
-struct Quad {
-  uint4 v[4];
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane;
+// lds_base must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gsrc), "s"(lds_base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// s_waitcnt vmcnt(n) (n < 16), leaving lgkmcnt/expcnt alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// An LDS byte address the optimiser cannot see through, so that each read
+// becomes `base + immediate` rather than one hoisted address register per read.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+      static_cast<uintptr_t>(addr));
+}
+
+__device__ __forceinline__ f32x4 lds_read_f4(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+      static_cast<uintptr_t>(addr));
+}
+
+__device__ __forceinline__ short4v ds_read_tr(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4v*)(static_cast<uintptr_t>(addr)));
+}
+
+// Row and column that byte 16*lane of DMA block u carries, per layout.
+template <int D>
+__device__ __forceinline__ void frag_major_rc(int u, int lane, int& row, int& col) {
+  row = (u / Tile<D>::kFragsPerKb) * 32 + (lane & 31);
+  col = 16 * (u % Tile<D>::kFragsPerKb) + 8 * (lane >> 5);
+}
+template <int D>
+__device__ __forceinline__ void block_major_rc(int u, int lane, int& row, int& col) {
+  const int byte = u * 1024 + 16 * lane;
+  const int q = byte / Tile<D>::kQuadBytes, w = byte % Tile<D>::kQuadBytes;
+  row = 4 * q + (w & 127) / 32;
+  col = 16 * (w / 128) + 8 * ((w & 31) / 16);
+}
+
+// Per-lane byte offset of the transposed read within a block-major tile: the
+// 16-lane group G = lane / 16 reads quad (base + G / 2), block (2 db + G % 2).
+template <int D>
+__device__ __forceinline__ uint32_t tr_lane_offset(int lane) {
+  return (lane >> 5) * Tile<D>::kQuadBytes + ((lane >> 4) & 1) * 128 + 8 * (lane & 15);
+}
+
+// A operand (lane = column d = 32 db + lane % 32) for rows
+// 32 rb + 16 t2 + {4h + 0..3, 8 + 4h + 0..3} of a block-major tile at `base`
+// (base already includes tr_lane_offset).
+template <int D>
+__device__ __forceinline__ bf16x8 frag_tr(uint32_t base, int db, int rb, int t2) {
+  const uint32_t q0 = base + (8 * rb + 4 * t2) * Tile<D>::kQuadBytes + db * 256;
+  const short4v lo4 = ds_read_tr(q0);
+  const short4v hi4 = ds_read_tr(q0 + 2 * Tile<D>::kQuadBytes);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// A operand (lane = row 32 kb + lane % 32) of d-step t of a fragment-major
+// tile at `base` (base already includes 16 * lane).
+template <int D>
+__device__ __forceinline__ bf16x8 frag_nat(uint32_t base, int kb, int t) {
+  return lds_read16(base + (kb * Tile<D>::kFragsPerKb + t) * 1024);
+}
+
+// ---------------------------------------------------------------------------
+// Rotated fragment-major tile: one copy that serves both the natural A
+// operand (lane = row) and the transposed one (lane = column).  Fragment
+// (kb, t) sits at (kb * D/16 + t) * 1088 bytes; slot s < 32 holds row
+// 32 kb + s, columns 16 t .. +7; slot s >= 32 holds row 32 kb + ((s - 24) & 31),
+// columns 16 t + 8 .. +15 (the second half rotated by 8 rows).  The rotation
+// puts the two column halves of a row 128 bytes apart modulo the 256-byte
+// bank window and the 64-byte fragment skew separates neighbouring fragments,
+// so 32 lanes of a transposed read touch 256 distinct bytes.
+template <int D>
+struct RTile {
+  static constexpr int kFragStride = 1088;
+  static constexpr int kFrags = 2 * (D / 16);
+  static constexpr int kBytes = kFrags * kFragStride;
 };
 
-__device__ __forceinline__ uint4 ld16(const __bf16* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
-
-__device__ __forceinline__ uint32_t half_of(const uint4& u, int e) {
-  const uint32_t word = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
-  return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
-}
-
-__device__ __forceinline__ int quad_perm(int m) {
-  return 16 * (m >> 2) + ((m & 1) ? 8 : 0) + ((m & 2) ? 4 : 0);
-}
-
+// Row/column of DMA lane `lane` for fragment u (written at u * kFragStride).
 template <int D>
-__device__ __forceinline__ void store_nat(__bf16* buf, int m, int dr, const Quad& q) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    *reinterpret_cast<uint4*>(buf + (4 * m + j) * Stage<D>::natPitch + dr * 8) = q.v[j];
+__device__ __forceinline__ void rot_major_rc(int u, int lane, int& row, int& col) {
+  row = (u / (D / 16)) * 32 + (lane < 32 ? lane : ((lane - 24) & 31));
+  col = 16 * (u % (D / 16)) + 8 * (lane >> 5);
 }
 
+// Natural read: lane L's 16 bytes of fragment (kb, t) are at
+// base + (kb * D/16 + t) * 1088 with base = tile + rot_nat_offset(L).
+__device__ __forceinline__ uint32_t rot_nat_offset(int lane) {
+  return 16 * (lane < 32 ? lane : 32 + ((lane - 40) & 31));
+}
 template <int D>
-__device__ __forceinline__ void store_tr(__bf16* buf, int m, int dr, const Quad& q) {
-  const int pos = quad_perm(m);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint2 w;
-    w.x = half_of(q.v[0], e) | (half_of(q.v[1], e) << 16);
-    w.y = half_of(q.v[2], e) | (half_of(q.v[3], e) << 16);
-    *reinterpret_cast<uint2*>(buf + (dr * 8 + e) * Stage<D>::trPitch + pos) = w;
-  }
+__device__ __forceinline__ bf16x8 rot_frag_nat(uint32_t base, int kb, int t) {
+  return lds_read16(base + (kb * (D / 16) + t) * RTile<D>::kFragStride);
 }
 
-// A-operand fragment of a 32x32x16 MFMA from a natural-layout tile:
-// lane (row = r0 + l32, half h32) gets columns 16*t + 8*h32 .. +7.
-template <int D>
-__device__ __forceinline__ bf16x8 frag_nat(const __bf16* buf, int r0, int l32, int h32, int t) {
-  return *reinterpret_cast<const bf16x8*>(buf + (r0 + l32) * Stage<D>::natPitch + 16 * t +
-                                          8 * h32);
+// Transposed read (lane = column 32 db + lane % 32, rows of 32-row block rb
+// at k-step t2).  Source lane j = lane % 16 supplies row 4h + j / 4 (+16 t2,
+// +8 for the second read) and columns 4 (j % 4) .. +3 of its 16-column group.
+// Rows 0..7 of a block wrap in the rotated half, so the first read of t2 = 0
+// uses its own lane offset (A); every other read uses offset B.
+__device__ __forceinline__ uint32_t rot_tr_offset_a(int lane) {
+  const int j = lane & 15, m = j >> 2, q = j & 3, half = q >> 1;
+  return 16 * (56 * half + 4 * (lane >> 5) + m) + 8 * (q & 1) + 1088 * ((lane >> 4) & 1);
 }
-
-// A-operand fragment from a transposed tile: lane (column = c0 + l32) gets
-// the 8 permuted rows of k-step (kb, t2) for its half.
+__device__ __forceinline__ uint32_t rot_tr_offset_b(int lane) {
+  const int j = lane & 15, m = j >> 2, q = j & 3, half = q >> 1;
+  return 16 * (24 * half + 4 * (lane >> 5) + m) + 8 * (q & 1) + 1088 * ((lane >> 4) & 1);
+}
 template <int D>
-__device__ __forceinline__ bf16x8 frag_tr(const __bf16* buf, int c0, int l32, int h32, int kb,
-                                          int t2) {
-  return *reinterpret_cast<const bf16x8*>(buf + (c0 + l32) * Stage<D>::trPitch + kb * 32 +
-                                          t2 * 16 + 8 * h32);
+__device__ __forceinline__ bf16x8 rot_frag_tr(uint32_t base_a, uint32_t base_b, int db, int rb,
+                                              int t2) {
+  const uint32_t f = (rb * (D / 16) + 2 * db) * RTile<D>::kFragStride;
+  const short4v lo4 = t2 == 0 ? ds_read_tr(base_a + f) : ds_read_tr(base_b + f + 256 * t2);
+  const short4v hi4 = ds_read_tr(base_b + f + 256 * t2 + 128);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 }  // namespace skv
