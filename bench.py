@@ -123,6 +123,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time the forward alone (diagnostic; not the benchmark step)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the benchmark, run a plain elementwise copy of this many "
+                         "MiB (read once, written once) three times; used to calibrate HBM "
+                         "byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -137,6 +141,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
+                          "launches": 3}), flush=True)
+        return
     skv.lib()  # fail loudly if the HIP library is not built
 
     w, g, t = wl.make(args.workload, args.seed, with_grad=True)

@@ -1,0 +1,136 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept with the
+sources.
+
+  kernels  -- per-kernel call count / average / share from a
+              `rocprofv3 --kernel-trace --stats --output-format csv` run
+  traffic  -- HBM bytes per launch of one kernel from two `--pmc` runs
+              (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by
+              what the same counter reads for a plain elementwise copy of a
+              known number of bytes
+
+Usage:
+  python -m block_sparse_split_amd.rocprof_summary kernels STATS_CSV \\
+      --command "..." [--out FILE]
+  python -m block_sparse_split_amd.rocprof_summary traffic KERNEL \\
+      --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV \\
+      --copy-bytes N --workload NAME --command "..." [--out FILE]
+"""
+import argparse
+import csv
+import hashlib
+import os
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# short names used by the library's own launch timing
+SHORT = {
+    "fwd_bf16_kernel": "fwd_bf16", "fwd_f32_kernel": "fwd_f32",
+    "merge_split_kernel": "merge_split", "merge_kernel": "merge",
+    "bwd_pre_kernel": "bwd_pre", "bwd_dq_kernel": "bwd_dq",
+    "dq_reduce_kernel": "dq_reduce", "bwd_dkdv_kernel": "bwd_dkdv",
+}
+
+
+def short_name(kernel_name):
+    for key, short in SHORT.items():
+        if key in kernel_name:
+            return short
+    return None
+
+
+def kernel_source_hash():
+    """sha256 over the kernel sources (csrc/*.hip, csrc/*.h, sorted by name)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_split_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def counter_per_dispatch(path, counter, match):
+    """Mean over dispatches of `counter` (summed over its per-dimension rows)
+    for kernels whose name satisfies `match`."""
+    per_dispatch = defaultdict(float)
+    for row in csv.DictReader(open(path)):
+        if row["Counter_Name"] != counter or not match(row["Kernel_Name"]):
+            continue
+        per_dispatch[row["Dispatch_Id"]] += float(row["Counter_Value"])
+    if not per_dispatch:
+        raise SystemExit(f"{path}: no {counter} rows for the requested kernel")
+    vals = list(per_dispatch.values())
+    return sum(vals) / len(vals), len(vals)
+
+
+def cmd_kernels(a):
+    rows = list(csv.DictReader(open(a.stats)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    out = [f"# rocprofv3 kernel statistics", f"command: {a.command}", "",
+           f"{'kernel':<14} {'calls':>6} {'avg_ms':>9} {'min_ms':>9} {'max_ms':>9} {'share':>7}"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = short_name(r["Name"]) or ("torch_elementwise" if "at::native" in r["Name"] else r["Name"][:40])
+        out.append(f"{name:<14} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e6:>9.4f} "
+                   f"{float(r['MinNs']) / 1e6:>9.4f} {float(r['MaxNs']) / 1e6:>9.4f} "
+                   f"{100 * float(r['TotalDurationNs']) / total:>6.2f}%")
+    emit("\n".join(out) + "\n", a.out)
+
+
+def cmd_traffic(a):
+    is_k = lambda n: short_name(n) == a.kernel
+    is_copy = lambda n: "neg_kernel" in n
+    f_kib, nf = counter_per_dispatch(a.fetch, "FETCH_SIZE", is_k)
+    w_kib, nw = counter_per_dispatch(a.write, "WRITE_SIZE", is_k)
+    cf_kib, _ = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", is_copy)
+    cw_kib, _ = counter_per_dispatch(a.copy_write, "WRITE_SIZE", is_copy)
+    f_scale = a.copy_bytes / (cf_kib * 1024.0)
+    w_scale = a.copy_bytes / (cw_kib * 1024.0)
+    lines = [
+        f"# HBM traffic of {a.kernel} on workload {a.workload}",
+        f"command: {a.command}",
+        f"kernel: {a.kernel}",
+        f"workload: {a.workload}",
+        f"kernel_source_sha256: {kernel_source_hash()}",
+        f"dispatches_fetch: {nf}",
+        f"dispatches_write: {nw}",
+        f"fetch_kib_per_dispatch_raw: {f_kib:.1f}",
+        f"write_kib_per_dispatch_raw: {w_kib:.1f}",
+        f"copy_probe_bytes: {a.copy_bytes}",
+        f"copy_fetch_kib_raw: {cf_kib:.1f}",
+        f"copy_write_kib_raw: {cw_kib:.1f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"fetch_bytes_per_launch: {f_kib * 1024.0 * f_scale:.0f}",
+        f"write_bytes_per_launch: {w_kib * 1024.0 * w_scale:.0f}",
+    ]
+    emit("\n".join(lines) + "\n", a.out)
+
+
+def emit(text, out):
+    if out:
+        with open(out, "w") as f:
+            f.write(text)
+    else:
+        sys.stdout.write(text)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    k = sub.add_parser("kernels")
+    k.add_argument("stats")
+    k.add_argument("--command", required=True)
+    k.add_argument("--out")
+    t = sub.add_parser("traffic")
+    t.add_argument("kernel")
+    for opt in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--workload", "--command"):
+        t.add_argument(opt, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--out")
+    a = ap.parse_args(argv)
+    {"kernels": cmd_kernels, "traffic": cmd_traffic}[a.what](a)
+
+
+if __name__ == "__main__":
+    main()
