@@ -104,17 +104,17 @@ template <int D>
 __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<D>;
   extern __shared__ __align__(16) char smem[];
-  const int32_t* S = a.sched;
+  const sched_t S = sched_const(a.sched);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h32 = lane >> 5, l32 = lane & 31;
   const int G = S[H_G], hq = S[H_HQ], hkv = S[H_HKV], nb = S[H_NB];
   const int nq = nb * kBlock, rows_per_head = nq * G;
-  const int32_t* anchors = S + S[H_OFF_ANCHORS];
-  const int32_t* los = S + S[H_OFF_LO];
-  const int32_t* tiles = S + S[H_OFF_TILES];
-  const int32_t* items = S + S[H_OFF_ITEMS];
-  const int32_t* queue = S + S[H_OFF_QUEUE];
+  const sched_t anchors = S + S[H_OFF_ANCHORS];
+  const sched_t los = S + S[H_OFF_LO];
+  const sched_t tiles = S + S[H_OFF_TILES];
+  const sched_t items = S + S[H_OFF_ITEMS];
+  const sched_t queue = S + S[H_OFF_QUEUE];
   const int qbeg = S[S[H_OFF_QOFF] + blockIdx.x], qend = S[S[H_OFF_QOFF] + blockIdx.x + 1];
   const float c = a.scale * kLog2e;
   const __bf16* Qg = static_cast<const __bf16*>(a.Q);
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
   const uint32_t taoff = rot_tr_offset_a(lane), tboff = rot_tr_offset_b(lane);
 
   for (int qi = qbeg; qi < qend; ++qi) {
-    const int32_t* it = items + queue[qi] * I_WORDS;
+    const sched_t it = items + queue[qi] * I_WORDS;
     const int head = it[I_HEAD], qt = it[I_QT], t0 = it[I_T0], t1 = it[I_T1];
     const int slot = it[I_SLOT], flags = it[I_FLAGS];
     const QTileSpan sp = qtile_span(qt, G, nq);
@@ -147,9 +147,6 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
       const __bf16* Vg = static_cast<const __bf16*>(st.draft ? a.Vd : a.V);
       dq_issue<D>(Kg, Vg, st, head, hkv, lds0 + (s % C::kStages) * C::kStageBytes, wave, lane);
     };
-    if (n_steps > 0) issue(0);
-    if (n_steps > 1) issue(1);
-
     bf16x8 qf[D / 16], df[D / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
@@ -163,6 +160,11 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
     const int64_t srow = (int64_t)head * rows_per_head + rho;
     const float lse2 = valid ? a.ws_L2[srow] : __builtin_inff();
     const float Dq = valid ? a.ws_D[srow] : 0.f;
+    // settle the per-row loads while no tile DMA is in flight, so that no
+    // wait for them lands inside the step loop (vmcnt also counts the DMA)
+    wait_vmcnt<0>();
+    if (n_steps > 0) issue(0);
+    if (n_steps > 1) issue(1);
     f32x16 dq[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkdv_kernel(BwdArgs
   using C = KvCfg<D>;
   constexpr int B = Tile<D>::kBlocks;
   extern __shared__ __align__(16) char smem[];
-  const int32_t* S = a.sched;
+  const sched_t S = sched_const(a.sched);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h32 = lane >> 5, l32 = lane & 31;
@@ -294,11 +296,11 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkdv_kernel(BwdArgs
   const int rows_per_head = nb * rows_per_block;
   // G is a power of two: row -> (token, head) and row -> block are shifts
   const int lgG = __builtin_ctz(G), lgR = 4 + lgG;
-  const int32_t* anchors = S + S[H_OFF_ANCHORS];
-  const int32_t* los = S + S[H_OFF_LO];
-  const int32_t* tiles = S + S[H_OFF_TILES];
-  const int32_t* kvs = S + S[H_OFF_KV];
-  const int32_t* queue = S + S[H_OFF_KVQUEUE];
+  const sched_t anchors = S + S[H_OFF_ANCHORS];
+  const sched_t los = S + S[H_OFF_LO];
+  const sched_t tiles = S + S[H_OFF_TILES];
+  const sched_t kvs = S + S[H_OFF_KV];
+  const sched_t queue = S + S[H_OFF_KVQUEUE];
   const int qbeg = S[S[H_OFF_KVQOFF] + blockIdx.x], qend = S[S[H_OFF_KVQOFF] + blockIdx.x + 1];
   const float c = a.scale * kLog2e;
   const __bf16* Qg = static_cast<const __bf16*>(a.Q);
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkdv_kernel(BwdArgs
   const uint32_t taoff = rot_tr_offset_a(lane), tboff = rot_tr_offset_b(lane);
 
   for (int qi = qbeg; qi < qend; ++qi) {
-    const int32_t* it = kvs + queue[qi] * K_WORDS;
+    const sched_t it = kvs + queue[qi] * K_WORDS;
     const int head = it[K_HEAD], t0 = it[K_T0], nt = it[K_NT];
     const int dtok0 = it[K_DTOK0], nd = it[K_NDRAFT], b0 = it[K_B0], b1 = it[K_B1];
     const bool draft = nd > 0;
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkdv_kernel(BwdArgs
       kpos = krow;
       nk = max(0, min(32, nd - 32 * wave));
     } else if ((wave >> 1) < nt) {
-      const int32_t* tl = tiles + (t0 + (wave >> 1)) * T_WORDS;
+      const sched_t tl = tiles + (t0 + (wave >> 1)) * T_WORDS;
       krow = tl[T_ROW] + 32 * (wave & 1);
       kpos = tl[T_POS] + 32 * (wave & 1);
       nk = max(0, min(32, tl[T_LEN] - 32 * (wave & 1)));

@@ -27,6 +27,16 @@ __device__ __forceinline__ __bf16 f32_to_bf16(float x) { return static_cast<__bf
 
 __device__ __forceinline__ uint16_t bf16_bits(__bf16 b) { return __builtin_bit_cast(uint16_t, b); }
 
+// The schedule image is read-only for the whole launch.  Reading it through
+// the constant address space lets wave-uniform reads become scalar loads:
+// a vector load would make the compiler wait on vmcnt, which also counts the
+// tile DMA in flight, and drain the staging ring.
+typedef const __attribute__((address_space(4))) int32_t* sched_t;
+
+__device__ __forceinline__ sched_t sched_const(const int32_t* p) {
+  return reinterpret_cast<sched_t>(reinterpret_cast<uintptr_t>(p));
+}
+
 // Draft-key rows a query tile may see: tokens [dtok0, dtok1) of Kd/Vd.
 struct QTileSpan {
   int32_t tok0, tok1;    // tokens of the tile (rows / G), clipped to Nq
@@ -51,7 +61,7 @@ struct Step {
   int32_t draft;   // 1 for draft keys
 };
 
-__device__ __forceinline__ Step item_step(const int32_t* tiles, int32_t s, int32_t n_draft,
+__device__ __forceinline__ Step item_step(sched_t tiles, int32_t s, int32_t n_draft,
                                           int32_t t0, const QTileSpan& sp) {
   Step st;
   if (s < n_draft) {
@@ -60,7 +70,7 @@ __device__ __forceinline__ Step item_step(const int32_t* tiles, int32_t s, int32
     st.n = min(kTileK, sp.dtok1 - st.row);
     st.draft = 1;
   } else {
-    const int32_t* t = tiles + (t0 + s - n_draft) * T_WORDS;
+    const sched_t t = tiles + (t0 + s - n_draft) * T_WORDS;
     st.row = t[T_ROW];
     st.base = t[T_POS];
     st.n = t[T_LEN];

@@ -99,18 +99,18 @@ template <int D>
 __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   extern __shared__ __align__(16) char smem[];
-  const int32_t* S = a.sched;
+  const sched_t S = sched_const(a.sched);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool groupA = wave < 4;
   const int h32 = lane >> 5, l32 = lane & 31;
   const int G = S[H_G], hq = S[H_HQ], hkv = S[H_HKV], nb = S[H_NB];
   const int nq = nb * kBlock, rows_per_head = nq * G;
-  const int32_t* anchors = S + S[H_OFF_ANCHORS];
-  const int32_t* los = S + S[H_OFF_LO];
-  const int32_t* tiles = S + S[H_OFF_TILES];
-  const int32_t* items = S + S[H_OFF_ITEMS];
-  const int32_t* queue = S + S[H_OFF_QUEUE];
+  const sched_t anchors = S + S[H_OFF_ANCHORS];
+  const sched_t los = S + S[H_OFF_LO];
+  const sched_t tiles = S + S[H_OFF_TILES];
+  const sched_t items = S + S[H_OFF_ITEMS];
+  const sched_t queue = S + S[H_OFF_QUEUE];
   const int qbeg = S[S[H_OFF_QOFF] + blockIdx.x], qend = S[S[H_OFF_QOFF] + blockIdx.x + 1];
   const float c = a.scale * kLog2e;
   const __bf16* Qg = static_cast<const __bf16*>(a.Q);
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
   const uint32_t voff = C::kTileBytes + tr_lane_offset<D>(lane);
 
   for (int qi = qbeg; qi < qend; ++qi) {
-    const int32_t* it = items + queue[qi] * I_WORDS;
+    const sched_t it = items + queue[qi] * I_WORDS;
     const int head = it[I_HEAD], qt = it[I_QT], t0 = it[I_T0], t1 = it[I_T1];
     const int slot = it[I_SLOT], flags = it[I_FLAGS];
     const QTileSpan sp = qtile_span(qt, G, nq);
@@ -144,11 +144,6 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
       const __bf16* Vg = static_cast<const __bf16*>(st.draft ? a.Vd : a.V);
       issue_step<D>(Kg, Vg, st, head, hkv, stage_of(s), wave, lane);
     };
-    // fill the ring before the Q loads so they overlap
-#pragma unroll
-    for (int s = 0; s < C::kStages; ++s)
-      if (s < n_steps) issue(s);
-
     bf16x8 qf[D / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
@@ -156,6 +151,12 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
                             : make_uint4(0, 0, 0, 0);
       qf[t] = __builtin_bit_cast(bf16x8, u);
     }
+    // settle the per-row loads while no tile DMA is in flight, so that no
+    // wait for them lands inside the step loop (vmcnt also counts the DMA)
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int s = 0; s < C::kStages; ++s)
+      if (s < n_steps) issue(s);
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -341,22 +342,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
   extern __shared__ __align__(16) char smem_raw[];
   float* Kl = reinterpret_cast<float*>(smem_raw);
   float* Vl = Kl + L::elems;
-  const int32_t* S = a.sched;
+  const sched_t S = sched_const(a.sched);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h32 = lane >> 5, l32 = lane & 31;
   const int G = S[H_G], hq = S[H_HQ], hkv = S[H_HKV], nb = S[H_NB];
   const int nq = nb * kBlock, rows_per_head = nq * G;
-  const int32_t* anchors = S + S[H_OFF_ANCHORS];
-  const int32_t* los = S + S[H_OFF_LO];
-  const int32_t* tiles = S + S[H_OFF_TILES];
-  const int32_t* items = S + S[H_OFF_ITEMS];
-  const int32_t* queue = S + S[H_OFF_QUEUE];
+  const sched_t anchors = S + S[H_OFF_ANCHORS];
+  const sched_t los = S + S[H_OFF_LO];
+  const sched_t tiles = S + S[H_OFF_TILES];
+  const sched_t items = S + S[H_OFF_ITEMS];
+  const sched_t queue = S + S[H_OFF_QUEUE];
   const int qbeg = S[S[H_OFF_QOFF] + blockIdx.x], qend = S[S[H_OFF_QOFF] + blockIdx.x + 1];
   const float c = a.scale * kLog2e;
   const float* Qg = static_cast<const float*>(a.Q);
 
   for (int qi = qbeg; qi < qend; ++qi) {
-    const int32_t* it = items + queue[qi] * I_WORDS;
+    const sched_t it = items + queue[qi] * I_WORDS;
     const int head = it[I_HEAD], qt = it[I_QT], t0 = it[I_T0], t1 = it[I_T1];
     const int slot = it[I_SLOT], flags = it[I_FLAGS];
     const QTileSpan sp = qtile_span(qt, G, nq);
