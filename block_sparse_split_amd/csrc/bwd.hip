@@ -35,16 +35,31 @@ namespace {
 
 // ---------------------------------------------------------------- pre
 // Row r (token, q-head h) of a kv head g = h / G has per-head index
-// rho = token * G + h % G.  Writes D and LSE * log2(e) (+inf for a row that
-// sees no key) at [g * Nq * G + rho].
+// rho = token * G + h % G.  Writes, at [g * Nq * G + rho]: D, LSE * log2(e)
+// (+inf for a row that sees no key) and the row's visible context interval
+// [lo, anchor) of its anchor block.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* O, const __bf16* dO,
-                                                      const float* LSE, float* Drm, float* L2rm,
-                                                      int64_t rows, int hq, int G) {
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const int32_t* sched, const __bf16* O,
+                                                      const __bf16* dO, const float* LSE,
+                                                      float* Drm, float* L2rm, int32_t* LOrm,
+                                                      int32_t* HIrm, int64_t rows, int hq, int G) {
   constexpr int TPR = D / 8;
   constexpr int RPB = 256 / TPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int c = (threadIdx.x % TPR) * 8;
+  {
+    // padding rows after each kv head's rows: no visible key
+    const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int hkv = hq / G;
+    if (gt < (int64_t)hkv * kStatPad) {
+      const int64_t idx = (gt / kStatPad) * (rows / hq * G + kStatPad) + rows / hq * G +
+                          gt % kStatPad;
+      Drm[idx] = 0.f;
+      L2rm[idx] = __builtin_inff();
+      LOrm[idx] = 0;
+      HIrm[idx] = 0;
+    }
+  }
   float s = 0.f;
   if (row < rows) {
     const uint4 a = *reinterpret_cast<const uint4*>(O + row * D + c);
@@ -62,10 +77,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* O, const __b
     const int64_t token = row / hq;
     const int h = (int)(row % hq);
     const int64_t nqG = rows / hq * G;
-    const int64_t idx = (int64_t)(h / G) * nqG + token * G + h % G;
+    const int64_t idx = (int64_t)(h / G) * (nqG + kStatPad) + token * G + h % G;
     const float L = LSE[row];
+    const int blk = (int)(token / kBlock);
     Drm[idx] = s;
     L2rm[idx] = L == kNegInf ? __builtin_inff() : L * kLog2e;
+    LOrm[idx] = sched[sched[H_OFF_LO] + blk];
+    HIrm[idx] = sched[sched[H_OFF_ANCHORS] + blk];
   }
 }
 
@@ -157,7 +175,7 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
       qf[t] = __builtin_bit_cast(bf16x8, u);
       df[t] = __builtin_bit_cast(bf16x8, v);
     }
-    const int64_t srow = (int64_t)head * rows_per_head + rho;
+    const int64_t srow = (int64_t)head * (rows_per_head + kStatPad) + rho;
     const float lse2 = valid ? a.ws_L2[srow] : __builtin_inff();
     const float Dq = valid ? a.ws_D[srow] : 0.f;
     // settle the per-row loads while no tile DMA is in flight, so that no
@@ -269,35 +287,59 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const int32_t* S, const 
 }
 
 // ---------------------------------------------------------------- dK, dV
+// Key-stationary.  Eight waves in four pairs; the waves of a pair share a
+// SIMD (waves w and w + 4) and own the same 32 keys of the item:
+//   P wave  (w < 4):  S = Q K^T, P = exp2(c S - L2) on visible pairs,
+//                     dV^T += dO^T P;
+//   dS wave (w >= 4): dP = dO V^T, dS = P (dP - D) with P taken from the P
+//                     wave through LDS, dK^T += Q^T dS.
+// Each holds one stationary operand (K or V of its keys) and one gradient,
+// so a wave needs half the registers of one doing both, two waves fit per
+// SIMD and one hides the other's LDS latency.  A 64-row query tile takes two
+// half steps: S/P and dP (P goes to the exchange buffer), barrier, then dV
+// and dK.  Q and dO tiles (rotated fragment-major: natural reads for S and
+// dP, transposed reads for dV and dK) and the per-row statistics (L2, D and
+// the row's visible interval) arrive by DMA in a 3-stage ring.  Every key's
+// gradients are written once.
 template <int D>
 struct KvCfg {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
-  // Q, dO (rotated fragment-major), then 1 KB of row statistics
+  // Q, dO (rotated fragment-major), then 1 KB of row statistics:
+  // D [0, 256), L2 [256, 512), lo [512, 768), anchor [768, 1024)
   static constexpr int kOOff = RTile<D>::kBytes;
   static constexpr int kStatOff = 2 * RTile<D>::kBytes;
   static constexpr int kStageBytes = kStatOff + 1024;
   static constexpr int kStages = 3;
-  static constexpr int kLdsBytes = kStages * kStageBytes;
+  // P exchange: per pair 64 rows x 32 keys of bf16, in MFMA B-operand order
+  static constexpr int kXOff = kStages * kStageBytes;
+  static constexpr int kLdsBytes = kXOff + 4 * 4096;
   static constexpr int kDmaPerWave = 2 * RTile<D>::kFrags / kWaves;
+  static constexpr int kPrefetchNat = 6;
+  static constexpr int kPrefetchTr = 4;
 };
 
-template <int D>
-__global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+// The two roles run separate copies of the whole item loop, so that the
+// compiler never keeps one role's loop state live in the other's.
+template <int D, bool PW>
+__device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
   using C = KvCfg<D>;
-  constexpr int B = Tile<D>::kBlocks;
+  // distinct (empty) markers keep the optimiser from merging the two roles'
+  // code back into one path with selects
+  if constexpr (PW) asm volatile("; dkdv role P" ::: "memory");
+  else asm volatile("; dkdv role dS" ::: "memory");
+  constexpr int NDB = D / 32;
   extern __shared__ __align__(16) char smem[];
   const sched_t S = sched_const(a.sched);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & 3;
+  constexpr bool pwave = PW;
   const int h32 = lane >> 5, l32 = lane & 31;
   const int G = S[H_G], hq = S[H_HQ], hkv = S[H_HKV], nb = S[H_NB];
-  const int rows_per_block = kBlock * G;
-  const int rows_per_head = nb * rows_per_block;
+  const int rows_per_head = nb * kBlock * G;
   // G is a power of two: row -> (token, head) and row -> block are shifts
   const int lgG = __builtin_ctz(G), lgR = 4 + lgG;
-  const sched_t anchors = S + S[H_OFF_ANCHORS];
-  const sched_t los = S + S[H_OFF_LO];
   const sched_t tiles = S + S[H_OFF_TILES];
   const sched_t kvs = S + S[H_OFF_KV];
   const sched_t queue = S + S[H_OFF_KVQUEUE];
@@ -308,32 +350,35 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkdv_kernel(BwdArgs
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t noff = rot_nat_offset(lane);
   const uint32_t taoff = rot_tr_offset_a(lane), tboff = rot_tr_offset_b(lane);
+  const uint32_t xslot = lds0 + C::kXOff + pair * 4096 + 16 * lane;
 
   for (int qi = qbeg; qi < qend; ++qi) {
     const sched_t it = kvs + queue[qi] * K_WORDS;
     const int head = it[K_HEAD], t0 = it[K_T0], nt = it[K_NT];
     const int dtok0 = it[K_DTOK0], nd = it[K_NDRAFT], b0 = it[K_B0], b1 = it[K_B1];
     const bool draft = nd > 0;
-    // this wave's 32 keys
+    // the pair's 32 keys: rows of K/V (or Kd/Vd) and absolute positions
+    // (draft keys: their draft token)
     int krow = 0, kpos = 0, nk = 0;
     if (draft) {
-      krow = dtok0 + 32 * wave;
+      krow = dtok0 + 32 * pair;
       kpos = krow;
-      nk = max(0, min(32, nd - 32 * wave));
-    } else if ((wave >> 1) < nt) {
-      const sched_t tl = tiles + (t0 + (wave >> 1)) * T_WORDS;
-      krow = tl[T_ROW] + 32 * (wave & 1);
-      kpos = tl[T_POS] + 32 * (wave & 1);
-      nk = max(0, min(32, tl[T_LEN] - 32 * (wave & 1)));
+      nk = max(0, min(32, nd - 32 * pair));
+    } else if ((pair >> 1) < nt) {
+      const sched_t tl = tiles + (t0 + (pair >> 1)) * T_WORDS;
+      krow = tl[T_ROW] + 32 * (pair & 1);
+      kpos = tl[T_POS] + 32 * (pair & 1);
+      nk = max(0, min(32, tl[T_LEN] - 32 * (pair & 1)));
     }
     const bool kvalid = l32 < nk;
     const int mypos = kpos + l32;
     const int kp0 = kpos, kp1 = kpos + nk;
-    const int r_begin = b0 * rows_per_block, r_end = b1 * rows_per_block;
+    const int r_begin = b0 * kBlock * G, r_end = b1 * kBlock * G;
     const int n_rt = (r_end - r_begin + kTileK - 1) / kTileK;
 
+    auto stage_of = [&](int rt) { return lds0 + (rt % C::kStages) * C::kStageBytes; };
     auto issue = [&](int rt) {
-      const uint32_t stage = lds0 + (rt % C::kStages) * C::kStageBytes;
+      const uint32_t stage = stage_of(rt);
       const int rho0 = r_begin + kTileK * rt;
 #pragma unroll
       for (int i = 0; i < C::kDmaPerWave; ++i) {
@@ -348,36 +393,40 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkdv_kernel(BwdArgs
               stage + (iso ? C::kOOff : 0) + f * RTile<D>::kFragStride);
       }
       if (wave == 0) {
-        // lanes 0-15: LSE*log2e of rows rho0 .. +63; 16-31: D; the rest pad
-        const float* srcs = (lane >> 4) & 1 ? a.ws_D : a.ws_L2;
-        const int r = min(rho0 + 4 * (lane & 15), rows_per_head - 4);
-        dma16(srcs + (int64_t)head * rows_per_head + r, stage + C::kStatOff);
+        // 16 lanes per statistic (D, L2, lo, anchor: consecutive arrays of
+        // stat_words each), 4 rows per lane; a tile ends at most 63 rows
+        // past the head's rows, inside its padding
+        dma16(reinterpret_cast<const int32_t*>(a.ws_D) + (int64_t)(lane >> 4) * a.stat_words +
+                  (int64_t)head * (rows_per_head + kStatPad) + rho0 + 4 * (lane & 15),
+              stage + C::kStatOff);
       }
     };
-    if (n_rt > 0) issue(0);
-    if (n_rt > 1) issue(1);
-
-    const __bf16* Ksrc = static_cast<const __bf16*>(draft ? a.Kd : a.K);
-    const __bf16* Vsrc = static_cast<const __bf16*>(draft ? a.Vd : a.V);
+    // this wave's stationary B operand: K (P wave) or V (dS wave) of its keys
+    const void* ksrc = pwave ? (draft ? a.Kd : a.K) : (draft ? a.Vd : a.V);
     const int64_t kaddr = ((int64_t)(krow + (kvalid ? l32 : 0)) * hkv + head) * D;
-    bf16x8 kf[D / 16], vf[D / 16];
+    bf16x8 kv[D / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
-      const uint4 u = kvalid ? *reinterpret_cast<const uint4*>(Ksrc + kaddr + 16 * t + 8 * h32)
+      const uint4 u = kvalid ? *reinterpret_cast<const uint4*>(
+                                   static_cast<const __bf16*>(ksrc) + kaddr + 16 * t + 8 * h32)
                              : make_uint4(0, 0, 0, 0);
-      const uint4 v = kvalid ? *reinterpret_cast<const uint4*>(Vsrc + kaddr + 16 * t + 8 * h32)
-                             : make_uint4(0, 0, 0, 0);
-      kf[t] = __builtin_bit_cast(bf16x8, u);
-      vf[t] = __builtin_bit_cast(bf16x8, v);
+      kv[t] = __builtin_bit_cast(bf16x8, u);
     }
-    f32x16 dk[D / 32], dv[D / 32];
+    // settle the per-item loads before any tile DMA is in flight
+    wait_vmcnt<0>();
+    if (n_rt > 0) issue(0);
+    if (n_rt > 1) issue(1);
+    f32x16 acc[NDB];  // dV^T (P wave) or dK^T (dS wave) of the pair's keys
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dk[db][r] = dv[db][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-    for (int rt = 0; rt < n_rt; ++rt) {
-      // this wave's DMA for tile rt is done once at most tile rt+1's is out
+    // Opening barrier of tile rt: this wave's share of tile rt has landed
+    // once at most tile rt+1's loads are in flight; after the barrier the
+    // stage of tile rt-1 takes tile rt+2.  Returns whether any row of the
+    // tile sees any of the pair's keys, and whether all rows see all of them.
+    auto open_tile = [&](int rt, bool& full) {
       if (rt + 1 < n_rt) {
         if (wave == 0) wait_vmcnt<C::kDmaPerWave + 1>();
         else wait_vmcnt<C::kDmaPerWave>();
@@ -386,95 +435,167 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkdv_kernel(BwdArgs
       }
       block_barrier();
       if (rt + 2 < n_rt) issue(rt + 2);
-      const int rho0 = r_begin + kTileK * rt;
-      // does any row of this tile see any of this wave's keys?
-      const int bA = rho0 >> lgR;
-      const int bB = min(b1, ((rho0 + kTileK - 1) >> lgR) + 1);
-      bool any = false;
-      for (int b = bA; b < bB && nk > 0; ++b) {
-        if (draft) any = any || (b * kBlock < kp1 && (b + 1) * kBlock > kp0);
-        else any = any || (max(los[b], kp0) < min(anchors[b], kp1));
+      // Rows past r_end belong to blocks that see none of the item's keys
+      // (their statistics, or the padding rows, say so), so every row's own
+      // interval decides; draft keys: the row's block.
+      const uint32_t stat = stage_of(rt) + C::kStatOff;
+      const int row = r_begin + kTileK * rt + lane;
+      int lo, hi;
+      if (draft) {
+        lo = (row >> lgR) * kBlock;
+        hi = lo + kBlock;
+      } else {
+        lo = lds_read_i32(stat + 512 + 4 * lane);
+        hi = lds_read_i32(stat + 768 + 4 * lane);
       }
-      if (!any) continue;
-      const uint32_t stage = lds0 + (rt % C::kStages) * C::kStageBytes;
-      const uint32_t qfb = opaque(stage + noff);
-      const uint32_t ofb = qfb + C::kOOff;
-      const uint32_t stat = stage + C::kStatOff;
-      bf16x8 pb[2][2], dsb[2][2];
+      full = __all(lo <= kp0 && hi >= kp1);
+      return __any(max(lo, kp0) < min(hi, kp1));
+    };
+    if constexpr (PW) {
+      for (int rt = 0; rt < n_rt; ++rt) {
+        bool full;
+        const bool any = open_tile(rt, full);
+        const uint32_t stage = stage_of(rt);
+        const uint32_t stat = stage + C::kStatOff;
+        const int rho0 = r_begin + kTileK * rt;
+        bf16x8 pb[2][2];
+        if (any) {
+          f32x16 sacc[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 sacc, dp;
+          for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = dp[r] = 0.f;
+            for (int r = 0; r < 16; ++r) sacc[qb][r] = 0.f;
+          const uint32_t qfb = opaque(stage + noff);
+          // MFMA i: query block qb = i % 2, d-step t = i / 2
+          lds_pipelined<2 * (D / 16), C::kPrefetchNat>(
+              [&](int i) { return rot_frag_nat<D>(qfb, i % 2, i / 2); },
+              [&](int i, const bf16x8& q) {
+                sacc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q, kv[i / 2], sacc[i % 2],
+                                                                      0, 0, 0);
+              });
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rot_frag_nat<D>(qfb, qb, t), kf[t],
-                                                         sacc, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rot_frag_nat<D>(ofb, qb, t), vf[t], dp, 0,
-                                                       0, 0);
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int r8 = qb * 32 + 8 * j;
+              const int rr = r8 + 4 * h32;  // rows rr .. rr+3 of the tile
+              const f32x4 l2 = lds_read_f4(stat + 256 + 4 * rr);
+              if (!full) {
+                // key visible to row i iff lo_i <= pos < hi_i
+                i32x4 lo, hi;
+                if (draft) {
+                  const int b = ((rho0 + rr) >> lgR) * kBlock;  // the 4 rows share a block
+                  lo = i32x4{b, b, b, b};
+                  hi = lo + kBlock;
+                } else {
+                  lo = lds_read_i4(stat + 512 + 4 * rr);
+                  hi = lds_read_i4(stat + 768 + 4 * rr);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if ((uint32_t)(mypos - lo[i]) >= (uint32_t)(hi[i] - lo[i]))
+                    sacc[qb][4 * j + i] = kNegInf;
+              }
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int r = 4 * j + i;
+                pb[qb][r >> 3][r & 7] = f32_to_bf16(exp2_fast(fmaf(sacc[qb][r], c, -l2[i])));
+              }
+            }
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) lds_write16(xslot + (2 * qb + t2) * 1024, pb[qb][t2]);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r8 = qb * 32 + 8 * j;  // first of 8 rows, all in one block
-          const int rr = rho0 + r8;
-          const int bj = min(rr >> lgR, nb - 1);
-          bool vis;
-          if (draft) vis = (mypos / kBlock) == bj;
-          else vis = mypos >= los[bj] && mypos < anchors[bj];
-          vis = vis && kvalid && rr < r_end;
-          const f32x4 l2 = lds_read_f4(stat + 4 * (r8 + 4 * h32));
-          const f32x4 dd = lds_read_f4(stat + 256 + 4 * (r8 + 4 * h32));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * j + i;
-            const float p = vis ? exp2_fast(fmaf(sacc[r], c, -l2[i])) : 0.f;
-            pb[qb][r >> 3][r & 7] = f32_to_bf16(p);
-            dsb[qb][r >> 3][r & 7] = f32_to_bf16(p * (dp[r] - dd[i]));
-          }
+        wait_lgkmcnt0();
+        block_barrier();
+        if (any) {
+          const uint32_t ota = opaque(stage + taoff + C::kOOff);
+          const uint32_t otb = opaque(stage + tboff + C::kOOff);
+          // MFMA i: query block qb, k-half t2, output block db
+          lds_pipelined<4 * NDB, C::kPrefetchTr>(
+              [&](int i) {
+                return rot_frag_tr<D>(ota, otb, i % NDB, i / (2 * NDB), (i / NDB) % 2);
+              },
+              [&](int i, const bf16x8& o) {
+                acc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    o, pb[i / (2 * NDB)][(i / NDB) % 2], acc[i % NDB], 0, 0, 0);
+              });
         }
       }
-      const uint32_t qta = opaque(stage + taoff), qtb = opaque(stage + tboff);
-      const uint32_t ota = qta + C::kOOff, otb = qtb + C::kOOff;
+    } else {
+      for (int rt = 0; rt < n_rt; ++rt) {
+        bool full;
+        const bool any = open_tile(rt, full);
+        const uint32_t stage = stage_of(rt);
+        const uint32_t stat = stage + C::kStatOff;
+        f32x16 dp[2];
+        if (any) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+          for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
+            for (int r = 0; r < 16; ++r) dp[qb][r] = 0.f;
+          const uint32_t ofb = opaque(stage + noff + C::kOOff);
+          lds_pipelined<2 * (D / 16), C::kPrefetchNat>(
+              [&](int i) { return rot_frag_nat<D>(ofb, i % 2, i / 2); },
+              [&](int i, const bf16x8& o) {
+                dp[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, kv[i / 2], dp[i % 2], 0,
+                                                                    0, 0);
+              });
+        }
+        block_barrier();
+        if (any) {
+          bf16x8 dsb[2][2];
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rot_frag_tr<D>(ota, otb, db, qb, t2),
-                                                             pb[qb][t2], dv[db], 0, 0, 0);
-            dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rot_frag_tr<D>(qta, qtb, db, qb, t2),
-                                                             dsb[qb][t2], dk[db], 0, 0, 0);
-          }
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+              const bf16x8 pr = lds_read16(xslot + (2 * qb + t2) * 1024);
+#pragma unroll
+              for (int jj = 0; jj < 2; ++jj) {
+                // rows 8 (2 t2 + jj) + 4 h32 + 0..3 of query block qb
+                const f32x4 dd = lds_read_f4(stat + 4 * (qb * 32 + 8 * (2 * t2 + jj) + 4 * h32));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int e = 4 * jj + i;
+                  const int r = 8 * t2 + e;
+                  dsb[qb][t2][e] = f32_to_bf16(static_cast<float>(pr[e]) * (dp[qb][r] - dd[i]));
+                }
+              }
+            }
+          const uint32_t qta = opaque(stage + taoff), qtb = opaque(stage + tboff);
+          lds_pipelined<4 * NDB, C::kPrefetchTr>(
+              [&](int i) {
+                return rot_frag_tr<D>(qta, qtb, i % NDB, i / (2 * NDB), (i / NDB) % 2);
+              },
+              [&](int i, const bf16x8& q) {
+                acc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    q, dsb[i / (2 * NDB)][(i / NDB) % 2], acc[i % NDB], 0, 0, 0);
+              });
+        }
+      }
     }
+    // the ring and the exchange buffer are free before the next item's DMA
     block_barrier();
     if (kvalid) {
       const int64_t orow = (int64_t)(krow + l32) * hkv + head;
-      void* dKp = draft ? a.dKd : a.dK;
-      void* dVp = draft ? a.dVd : a.dV;
+      void* dst = pwave ? (draft ? a.dVd : a.dV) : (draft ? a.dKd : a.dK);
+      const float mul = pwave ? 1.0f : a.scale;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d0 = 32 * db + 8 * j + 4 * h32;
           if (a.grad_bf16) {
-            bf16x4 wk, wv;
+            bf16x4 w;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              wk[i] = f32_to_bf16(dk[db][4 * j + i] * a.scale);
-              wv[i] = f32_to_bf16(dv[db][4 * j + i]);
-            }
-            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(dKp) + orow * D + d0) = wk;
-            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(dVp) + orow * D + d0) = wv;
+            for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16(acc[db][4 * j + i] * mul);
+            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(dst) + orow * D + d0) = w;
           } else {
-            f32x4 wk, wv;
+            f32x4 w;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              wk[i] = dk[db][4 * j + i] * a.scale;
-              wv[i] = dv[db][4 * j + i];
-            }
-            *reinterpret_cast<f32x4*>(static_cast<float*>(dKp) + orow * D + d0) = wk;
-            *reinterpret_cast<f32x4*>(static_cast<float*>(dVp) + orow * D + d0) = wv;
+            for (int i = 0; i < 4; ++i) w[i] = acc[db][4 * j + i] * mul;
+            *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + orow * D + d0) = w;
           }
         }
     }
@@ -482,12 +603,18 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkdv_kernel(BwdArgs
 }
 
 template <int D>
+__global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  if (threadIdx.x < 256) dkdv_role<D, true>(a);
+  else dkdv_role<D, false>(a);
+}
+
+template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.nb * kBlock * a.hq;
   constexpr int RPB = 256 / (D / 8);
   SKV_LAUNCH("bwd_pre", bwd_pre_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256), 0, s,
-             static_cast<const __bf16*>(a.O), static_cast<const __bf16*>(a.dO), a.LSE, a.ws_D,
-             a.ws_L2, rows, a.hq, a.hq / a.hkv);
+             a.sched, static_cast<const __bf16*>(a.O), static_cast<const __bf16*>(a.dO), a.LSE,
+             a.ws_D, a.ws_L2, a.ws_LO, a.ws_HI, rows, a.hq, a.hq / a.hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_kernel<D>),

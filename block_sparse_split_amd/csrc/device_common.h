@@ -93,6 +93,20 @@ __device__ __forceinline__ void step_bounds(const Step& st, int32_t lo, int32_t 
   khi = min(khi, st.n);
 }
 
+// max / sum of x over lanes l and l ^ 32.  v_permlane32_swap exchanges the
+// two 32-lane halves in registers (no LDS round trip); the sum adds the lower
+// half's value first in both halves, so both get bit-identical results.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -63,6 +63,10 @@ struct FwdCfg {
   static constexpr int kStages = 4;
   static constexpr int kLdsBytes = kStages * kStageBytes;
   static constexpr int kDmaPerWave = 2 * (kTileBytes / 1024) / kWaves;
+  // LDS operand reads kept in flight ahead of the MFMAs (K: one read per
+  // fragment, V: two transposed reads per fragment)
+  static constexpr int kPrefetchK = 6;
+  static constexpr int kPrefetchV = 4;
 };
 
 // Issue this wave's share of the DMA for one step into `stage` (LDS bytes):
@@ -193,14 +197,14 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
     // O^T += V^T P^T for the tile in `stage` (P from the last softmax)
     auto pv = [&](int s) {
       const uint32_t vbase = opaque(stage_of(s) + voff);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(vbase, db, kb, t2),
-                                                            pf[kb][t2], o[db], 0, 0, 0);
+      constexpr int NDB = D / 32;
+      // MFMA i: key block kb, k-half t2, output block db
+      lds_pipelined<4 * NDB, C::kPrefetchV>(
+          [&](int i) { return frag_tr<D>(vbase, i % NDB, i / (2 * NDB), (i / NDB) % 2); },
+          [&](int i, const bf16x8& v) {
+            o[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                v, pf[i / (2 * NDB)][(i / NDB) % 2], o[i % NDB], 0, 0, 0);
+          });
     };
     if (!groupA) half_step(-1);
     for (int p = 0; p < n_steps; ++p) {
@@ -225,12 +229,13 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
 #pragma unroll
           for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
         const uint32_t kbase = opaque(stage_of(p) + koff);
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_nat<D>(kbase, kb, t), qf[t],
-                                                               sacc[kb], 0, 0, 0);
+        // MFMA i: d-step t = i / 2, key block kb = i % 2
+        lds_pipelined<2 * (D / 16), C::kPrefetchK>(
+            [&](int i) { return frag_nat<D>(kbase, i % 2, i / 2); },
+            [&](int i, const bf16x8& k) {
+              sacc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[i / 2], sacc[i % 2], 0,
+                                                                    0, 0);
+            });
       }
       half_step(2 * p + k0 + 1);
       // softmax of step p
@@ -253,7 +258,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_xor32(mx);
         const float mt = mx * c;
         const bool need = mt > m_used + 8.0f;
         if (__any(need)) {
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
     // all waves are done with the ring before the next item's DMA reuses it
     block_barrier();
 
-    const float lt = l + __shfl_xor(l, 32);
+    const float lt = sum_xor32(l);
     if (valid) {
       const float inv = lt > 0.f ? 1.0f / lt : 0.f;
       const float lse = lt > 0.f ? (m_used + log2f(lt)) * kLn2 : kNegInf;
@@ -450,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
         for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_xor32(mx);
         const float mt = mx * c;
         const bool need = mt > m_used[qb] + 8.0f;
         if (__any(need)) {

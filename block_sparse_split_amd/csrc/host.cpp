@@ -453,7 +453,8 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
   const int64_t rows_slot = skv::kQTile;
   const int64_t fwd_ws = align_up(int64_t(n_slots) * rows_slot * g.d * 4, 256) +
                          align_up(int64_t(n_slots) * rows_slot * 4, 256);
-  const int64_t bwd_ws = 2 * align_up(int64_t(g.nq) * g.hq * 4, 256) +
+  // per-row statistics: per kv head, its rows plus kStatPad padding rows
+  const int64_t bwd_ws = 4 * align_up(int64_t(g.hkv) * (g.rows_per_head + skv::kStatPad) * 4, 256) +
                          align_up(int64_t(n_slots) * rows_slot * g.d * 4, 256);
   std::memset(info, 0, sizeof(*info));
   info->words = words;
@@ -711,10 +712,14 @@ skv_status skv_attn_bwd(const skv_problem* p, const skv_schedule_info* info,
     a.n_split = info->n_split_qtiles;
     a.n_slots = info->n_partial_slots;
     a.with_draft = p->with_draft;
-    const int64_t stat_bytes = align_up(int64_t(p->nb) * 16 * p->hq * 4, 256);
+    const int64_t stat_bytes = align_up(
+        int64_t(p->hkv) * (int64_t(p->nb) * 16 * (p->hq / p->hkv) + skv::kStatPad) * 4, 256);
     a.ws_D = static_cast<float*>(workspace);
     a.ws_L2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + stat_bytes);
-    a.ws_dQ = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * stat_bytes);
+    a.ws_LO = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 2 * stat_bytes);
+    a.ws_HI = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 3 * stat_bytes);
+    a.ws_dQ = reinterpret_cast<float*>(static_cast<char*>(workspace) + 4 * stat_bytes);
+    a.stat_words = stat_bytes / 4;
     check_hip(skv::launch_bwd(a, static_cast<hipStream_t>(stream)), "backward launch");
   });
 }

@@ -18,6 +18,7 @@ constexpr int kBlock = 16;      // draft tokens per anchor block
 constexpr int kTileK = 64;      // keys per key tile
 constexpr int kQTile = 256;     // query rows (token x head of one kv head) per tile
 constexpr int kKvGroup = 128;   // keys per dK/dV item (two 64-key tiles)
+constexpr int kStatPad = 64;    // padding rows after each kv head's row statistics
 
 // Header word indices.
 enum Hdr : int {

@@ -75,6 +75,25 @@ __device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
       static_cast<uintptr_t>(addr));
 }
 
+__device__ __forceinline__ void lds_write16(uint32_t addr, const bf16x8& v) {
+  *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(static_cast<uintptr_t>(addr)) = v;
+}
+
+__device__ __forceinline__ int32_t lds_read_i32(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) int32_t*>(
+      static_cast<uintptr_t>(addr));
+}
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 lds_read_i4(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
+      static_cast<uintptr_t>(addr));
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS writes have completed (before a
+// barrier that publishes them to other waves).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 __device__ __forceinline__ f32x4 lds_read_f4(uint32_t addr) {
   return *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
       static_cast<uintptr_t>(addr));
@@ -177,6 +196,26 @@ __device__ __forceinline__ bf16x8 rot_frag_tr(uint32_t base_a, uint32_t base_b, 
   const short4v lo4 = t2 == 0 ? ds_read_tr(base_a + f) : ds_read_tr(base_b + f + 256 * t2);
   const short4v hi4 = ds_read_tr(base_b + f + 256 * t2 + 128);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// N MFMAs whose A operands come from LDS, with P reads kept in flight:
+// read(i) returns operand i (i is a compile-time constant after unrolling),
+// mfma(i, a) issues MFMA i.  A scheduling barrier before every MFMA stops
+// the compiler from moving each read next to its consumer, so the read
+// latency hides behind the P MFMAs issued in between.
+template <int N, int P, class Read, class Mfma>
+__device__ __forceinline__ void lds_pipelined(Read read, Mfma mfma) {
+  bf16x8 buf[P];
+#pragma unroll
+  for (int i = 0; i < P && i < N; ++i) buf[i] = read(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8 a = buf[i % P];
+    if (i + P < N) buf[i % P] = read(i + P);
+    mfma(i, a);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 }  // namespace skv
