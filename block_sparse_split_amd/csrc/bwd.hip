@@ -98,6 +98,8 @@ struct DqCfg {
   static constexpr int kStages = 3;
   static constexpr int kLdsBytes = kStages * kStageBytes;
   static constexpr int kDmaPerWave = 2 * Tile<D>::kBlocks / kWaves;
+  static constexpr int kPrefetchNat = 6;
+  static constexpr int kPrefetchTr = 4;
 };
 
 template <int D>
@@ -216,13 +218,18 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
         f32x16 sacc, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = dp[r] = 0.f;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rot_frag_nat<D>(kbase, kb, t), qf[t],
-                                                         sacc, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_nat<D>(vbase, kb, t), df[t], dp, 0,
-                                                       0, 0);
-        }
+        // MFMA i: d-step t = i / 2; even i: S^T (K), odd i: dP^T (V)
+        lds_pipelined<2 * (D / 16), C::kPrefetchNat>(
+            [&](int i) {
+              return i % 2 == 0 ? rot_frag_nat<D>(kbase, kb, i / 2)
+                                : frag_nat<D>(vbase, kb, i / 2);
+            },
+            [&](int i, const bf16x8& x) {
+              if (i % 2 == 0)
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, qf[i / 2], sacc, 0, 0, 0);
+              else
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, df[i / 2], dp, 0, 0, 0);
+            });
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           // key 32 kb + 8 (r / 4) + 4 h32 + r % 4 against bounds shifted by 4 h32
@@ -235,14 +242,14 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
       __builtin_amdgcn_sched_barrier(0);
       const uint32_t ta = opaque(stage + taoff);
       const uint32_t tb = opaque(stage + tboff);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-            dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rot_frag_tr<D>(ta, tb, db, kb, t2),
-                                                             ds[kb][t2], dq[db], 0, 0, 0);
+      constexpr int NDB = D / 32;
+      // MFMA i: key block kb, k-half t2, output block db
+      lds_pipelined<4 * NDB, C::kPrefetchTr>(
+          [&](int i) { return rot_frag_tr<D>(ta, tb, i % NDB, i / (2 * NDB), (i / NDB) % 2); },
+          [&](int i, const bf16x8& k) {
+            dq[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                k, ds[i / (2 * NDB)][(i / NDB) % 2], dq[i % NDB], 0, 0, 0);
+          });
     }
     block_barrier();
     if (valid) {

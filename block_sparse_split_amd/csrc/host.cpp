@@ -210,13 +210,6 @@ std::vector<Tile> build_tiles(const skv_problem* p) {
   return tiles;
 }
 
-int32_t env_int(const char* name, int32_t dflt, int32_t lo, int32_t hi) {
-  const char* s = std::getenv(name);
-  if (!s || !*s) return dflt;
-  long v = std::strtol(s, nullptr, 10);
-  return int32_t(std::min<long>(hi, std::max<long>(lo, v)));
-}
-
 struct Item {
   int32_t head, qt, t0, t1, slot, flags;
   int64_t cost;
@@ -296,99 +289,119 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
     }
     if (p->with_draft) total += int64_t(b1 - b0) * g.hkv;
   }
-  // Cut each query tile's visible tiles into runs of consecutive tile
-  // indices, then each run into pieces of `piece` cost (the last piece of a
-  // run keeps the remainder).  The remainders, of varied sizes, are what LPT
-  // places last, so they fill the bins evenly.  Several piece sizes (the
-  // per-workgroup mean load divided by r) are tried and the one with the
-  // smallest LPT makespan is kept (ties: fewer items).
-  struct Piece {
-    int32_t t0, t1;
-    int64_t cost;
+  // Forward / dQ items.  Units are runs of consecutive visible tiles of one
+  // (kv head, query tile); the first run of a query tile also carries its
+  // draft keys (one pair per anchor block).  Per XCD class, units are placed
+  // LPT-first (largest remaining cost first, ties: lowest unit, then lowest
+  // bin) on the least-loaded workgroup; a unit that would push that
+  // workgroup past the class's target load T = ceil(class cost / bins) is
+  // cut at a tile boundary: the prefix that fits stays, the rest goes back to
+  // the pending set.  Work units are divisible (their partials merge exactly),
+  // so every bin ends at most one tile above T, with at most one cut per bin.
+  struct Unit {
+    int32_t head, qt, k0, k1;  // tiles qt_vis[qt][k0 .. k1-1]
+    int64_t draft_cost;        // cost of the draft step (first run only)
   };
-  auto cut = [&](int64_t piece) {
-    std::vector<std::vector<Piece>> out(g.qt_per_head);
+  std::vector<Unit> units;
+  for (int32_t h = 0; h < g.hkv; ++h) {
     for (int32_t qt = 0; qt < g.qt_per_head; ++qt) {
+      const int32_t b0 = qt * tok_per_qt / skv::kBlock;
+      const int32_t b1 =
+          std::min(g.nb, ((qt + 1) * tok_per_qt + skv::kBlock - 1) / skv::kBlock);
+      const int64_t dcost = p->with_draft ? int64_t(b1 - b0) : 0;
       const auto& vis = qt_vis[qt];
-      const auto& cst = qt_cost[qt];
-      size_t i = 0;
-      while (i < vis.size()) {
+      if (vis.empty()) {  // still one item: it writes O = 0, LSE = -inf (or the draft part)
+        units.push_back({h, qt, 0, 0, dcost});
+        continue;
+      }
+      bool first = true;
+      for (size_t i = 0; i < vis.size();) {
         size_t j = i + 1;
         while (j < vis.size() && vis[j] == vis[j - 1] + 1) ++j;
-        size_t start = i;
-        int64_t acc = 0;
-        for (size_t k = i; k < j; ++k) {
-          acc += cst[k];
-          if (acc >= piece || k + 1 == j) {
-            out[qt].push_back({vis[start], vis[k] + 1, acc});
-            start = k + 1;
-            acc = 0;
-          }
-        }
+        units.push_back({h, qt, int32_t(i), int32_t(j), first ? dcost : 0});
+        first = false;
         i = j;
       }
     }
-    return out;
-  };
+  }
   const int32_t n_cls_fwd = xcd_classes(g.hkv, n_wg);
-  auto make_items = [&](const std::vector<std::vector<Piece>>& pieces, std::vector<Item>& out,
-                        std::vector<int32_t>& split, int32_t& slots) {
-    out.clear();
-    split.clear();
-    slots = 0;
-    for (int32_t h = 0; h < g.hkv; ++h) {
-      for (int32_t qt = 0; qt < g.qt_per_head; ++qt) {
-        const int32_t b0 = qt * tok_per_qt / skv::kBlock;
-        const int32_t b1 =
-            std::min(g.nb, ((qt + 1) * tok_per_qt + skv::kBlock - 1) / skv::kBlock);
-        std::vector<Piece> ps = pieces[qt];
-        if (ps.empty()) ps.push_back({0, 0, 0});
-        const int32_t n = int32_t(ps.size());
-        const int32_t slot0 = n > 1 ? slots : -1;
-        if (n > 1) {
-          split.insert(split.end(), {h, qt, slot0, n});
-          slots += n;
-        }
-        for (int32_t k = 0; k < n; ++k) {
-          Item it{h, qt, ps[k].t0, ps[k].t1, n > 1 ? slot0 + k : -1, 0, ps[k].cost};
-          if (k == 0 && p->with_draft) {
-            it.flags |= skv::kItemDraft;
-            it.cost += b1 - b0;
-          }
-          out.push_back(it);
+  const int32_t per_cls = n_wg / n_cls_fwd;
+  std::vector<std::vector<int32_t>> q(n_wg);
+  std::vector<int64_t> wg_load(n_wg, 0);
+  auto piece_cost = [&](const Unit& u, int32_t k0, int32_t k1) {
+    int64_t c = k0 == u.k0 ? u.draft_cost : 0;
+    for (int32_t k = k0; k < k1; ++k) c += qt_cost[u.qt][k];
+    return c;
+  };
+  for (int32_t cls = 0; cls < n_cls_fwd; ++cls) {
+    // pending pieces: (cost, unit, first tile) -- largest cost first
+    struct Pending {
+      int64_t cost;
+      int32_t unit, k0;
+      bool operator<(const Pending& o) const {  // priority_queue: top = largest
+        if (cost != o.cost) return cost < o.cost;
+        if (unit != o.unit) return unit > o.unit;
+        return k0 > o.k0;
+      }
+    };
+    std::priority_queue<Pending> pend;
+    int64_t cls_total = 0;
+    for (int32_t ui = 0; ui < int32_t(units.size()); ++ui) {
+      const Unit& u = units[ui];
+      if (u.head % n_cls_fwd != cls) continue;
+      const int64_t c = piece_cost(u, u.k0, u.k1);
+      cls_total += c;
+      pend.push({c, ui, u.k0});
+    }
+    const int64_t target = (cls_total + per_cls - 1) / per_cls;
+    using Bin = std::pair<int64_t, int32_t>;  // (load, bin)
+    std::priority_queue<Bin, std::vector<Bin>, std::greater<Bin>> bins;
+    for (int32_t b = 0; b < per_cls; ++b) bins.push({0, b});
+    while (!pend.empty()) {
+      const Pending pc = pend.top();
+      pend.pop();
+      const Unit& u = units[pc.unit];
+      Bin bin = bins.top();
+      bins.pop();
+      int32_t k_end = u.k1;
+      int64_t placed = pc.cost;
+      if (bin.first + pc.cost > target && u.k1 - pc.k0 > 1) {
+        // cut: the longest prefix that fits (at least one tile)
+        const int64_t room = target - bin.first;
+        int64_t acc = pc.k0 == u.k0 ? u.draft_cost : 0;
+        int32_t k = pc.k0;
+        while (k < u.k1 && acc + qt_cost[u.qt][k] <= room) acc += qt_cost[u.qt][k++];
+        if (k == pc.k0) acc += qt_cost[u.qt][k++];
+        if (k < u.k1) {
+          k_end = k;
+          placed = acc;
+          pend.push({pc.cost - acc, pc.unit, k});
         }
       }
+      const auto& vis = qt_vis[u.qt];
+      Item it{u.head, u.qt, u.k1 > u.k0 ? vis[pc.k0] : 0, u.k1 > u.k0 ? vis[k_end - 1] + 1 : 0,
+              -1, 0, placed};
+      if (pc.k0 == u.k0 && p->with_draft && u.draft_cost > 0) it.flags |= skv::kItemDraft;
+      const int32_t wg = cls + bin.second * n_cls_fwd;
+      q[wg].push_back(int32_t(items.size()));
+      items.push_back(it);
+      bin.first += placed;
+      wg_load[wg] = bin.first;
+      bins.push(bin);
     }
-  };
-  const int32_t forced = env_int("SKV_PIECE_DIV", 0, 0, 64);
-  const int32_t divs_all[] = {1, 2, 3, 4, 5, 6, 8, 12, 16};
-  std::vector<int32_t> divs;
-  if (forced) divs.push_back(forced); else divs.assign(std::begin(divs_all), std::end(divs_all));
-  // Each partial slot costs a write and a read of 256 rows of fp32 O + LSE
-  // at chip bandwidth, while one (block, tile) pair costs its MFMA work on one
-  // of n_wg workgroups.  With the bf16 MFMA peak (~2.5 PFLOP/s, ~60% of it
-  // reached) and 8 TB/s, one slot weighs `slot_w` pairs of makespan.
-  const double pair_flops = double(skv::kBlock) * g.G * skv::kTileK * g.d * 4.0;
-  const double slot_bytes = double(skv::kQTile) * (g.d + 1) * 4.0 * 2.0;
-  const double slot_w = (slot_bytes / 8e12) / (pair_flops * n_wg / 1.5e15);
+  }
+  // query tiles with several items write partial slots, merged afterwards
   std::vector<int32_t> split_rec;  // S_WORDS per split query tile
   int32_t n_slots = 0;
-  double best_obj = -1.0;
-  for (int32_t r : divs) {
-    const int64_t piece = std::max<int64_t>(1, total / (int64_t(n_wg) * r));
-    std::vector<Item> cand;
-    std::vector<int32_t> cand_split;
-    int32_t cand_slots = 0;
-    make_items(cut(piece), cand, cand_split, cand_slots);
-    int64_t mb = 0;
-    place(int32_t(cand.size()), n_wg, n_cls_fwd, [&](int32_t i) { return cand[i].cost; },
-          [&](int32_t i) { return cand[i].head; }, &mb);
-    const double obj = double(mb) + slot_w * cand_slots;
-    if (best_obj < 0 || obj < best_obj) {
-      best_obj = obj;
-      items.swap(cand);
-      split_rec.swap(cand_split);
-      n_slots = cand_slots;
+  {
+    std::vector<std::vector<int32_t>> of(int64_t(g.hkv) * g.qt_per_head);
+    for (int32_t i = 0; i < int32_t(items.size()); ++i)
+      of[int64_t(items[i].head) * g.qt_per_head + items[i].qt].push_back(i);
+    for (int64_t k = 0; k < int64_t(of.size()); ++k) {
+      if (of[k].size() < 2) continue;
+      split_rec.insert(split_rec.end(), {int32_t(k / g.qt_per_head), int32_t(k % g.qt_per_head),
+                                         n_slots, int32_t(of[k].size())});
+      for (int32_t i : of[k]) items[i].slot = n_slots++;
     }
   }
   // dK/dV items: two consecutive tiles per item (one if a lone tile is
@@ -421,11 +434,9 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
       }
     }
   }
-  const int32_t n_cls = xcd_classes(g.hkv, n_wg);
+  const int32_t n_cls = n_cls_fwd;
   int64_t max_bin = 0, kv_max_bin = 0;
-  auto q = place(int32_t(items.size()), n_wg, n_cls,
-                 [&](int32_t i) { return items[i].cost; },
-                 [&](int32_t i) { return items[i].head; }, &max_bin);
+  for (int64_t l : wg_load) max_bin = std::max(max_bin, l);
   auto kq = place(int32_t(kv.size()), n_wg, n_cls,
                   [&](int32_t i) { return kv[i].cost; },
                   [&](int32_t i) { return kv[i].head; }, &kv_max_bin);
