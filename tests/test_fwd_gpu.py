@@ -227,3 +227,64 @@ def test_full_varlen_fwd_sampled_rows():
                               wl.softmax_scale(w.d), blocks=blocks)
     rows = block_rows(blocks)
     compare(O[rows], L[rows], Oo, Lo, "bf16", "varlen sampled")
+
+
+def test_full_ctx1m_64_shards_then_64way_merge():
+    """1M context, 8192 queries, 4096 chunks of 256 over 64 LPT shards: all
+    64 partials on the GPU (draft keys on shard 0), then one 64-way LSE merge;
+    the two anchor blocks with the smallest anchors (their ~260K visible keys
+    lie in chunks spread over all 64 shards) against fp64 attention over the
+    keys they see.  Each shard's K/V are drawn in fp32 and rounded to bf16 on
+    the device (round to nearest even, as the host rounding does); the oracle
+    gets the host-rounded rows."""
+    w, g, _ = wl.make("ctx1m_merge64", 4, tensors=False)
+    w32 = wl.scaled(w, dtype="f32")
+    ids, _, _, load = shards.lpt_shards(w, g, w.n_shards)
+    assert load.max() / load.mean() - 1 < 0.01
+    t = wl.draw_tensors(w, g, 4, chunk_ids=[])
+    Q = to_dev(t.Q, "bf16")
+    Kd, Vd = to_dev(t.Kd, "bf16"), to_dev(t.Vd, "bf16")
+    Op = torch.empty((w.n_shards, w.nq, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+    Lp = torch.empty((w.n_shards, w.nq, w.hq), dtype=torch.float32, device="cuda")
+    for r in range(w.n_shards):
+        if r % 8 == 0:
+            announce("ctx1m shard", r)
+        prob = shards.shard_problem(w, g, ids[r], r == 0)
+        sh = skv.Shard(prob)
+        K = to_dev(wl.draw_kv_chunks(w32, g, 4, ids[r], "K"), "bf16")
+        V = to_dev(wl.draw_kv_chunks(w32, g, 4, ids[r], "V"), "bf16")
+        sh.fwd(Q, K, V, Kd if r == 0 else None, Vd if r == 0 else None, Op[r], Lp[r])
+        torch.cuda.synchronize()
+        del K, V, sh
+    Om = torch.empty((w.nq, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+    Lm = torch.empty((w.nq, w.hq), dtype=torch.float32, device="cuda")
+    announce("ctx1m: 64-way merge")
+    skv.skv_merge_lse(Op, Lp, Om, Lm)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        skv.skv_merge_lse(Op, Lp, Om, Lm)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    nbytes = (Op.numel() * 2 + Lp.numel() * 4) + (Om.numel() * 2 + Lm.numel() * 4)
+    print(f"[ctx1m] 64-way merge {ms:.3f} ms, {nbytes / ms / 1e6:.0f} GB/s", flush=True)
+    assert torch.all(torch.isfinite(Lm))
+    blocks = [0, 1]
+    need = np.nonzero(g.chunk_pos < g.anchors[blocks].max())[0]
+    assert len(np.unique(ids_of(ids, need))) == w.n_shards
+    announce("ctx1m: oracle on blocks", blocks, "over", len(need), "chunks")
+    Ko = wl.draw_kv_chunks(w, g, 4, need, "K")
+    Vo = wl.draw_kv_chunks(w, g, 4, need, "V")
+    pos = shards.shard_rows(g, need)
+    Oo, Lo = oracle.attention_partial(t.Q, Ko, Vo, pos, g.anchors, g.lo, wl.softmax_scale(w.d),
+                                      t.Kd, t.Vd, blocks=blocks)
+    rows = block_rows(blocks)
+    compare(Om[rows], Lm[rows], Oo, Lo, "bf16", "ctx1m merged sampled")
+
+
+def ids_of(ids, chunks):
+    """Shard of each chunk."""
+    owner = {int(c): r for r, cs in enumerate(ids) for c in cs}
+    return [owner[int(c)] for c in chunks]
