@@ -321,7 +321,8 @@ struct KvCfg {
   // P exchange: per pair 64 rows x 32 keys of bf16, in MFMA B-operand order
   static constexpr int kXOff = kStages * kStageBytes;
   static constexpr int kLdsBytes = kXOff + 4 * 4096;
-  static constexpr int kDmaPerWave = 2 * RTile<D>::kFrags / kWaves;
+  // the four P waves issue all tile DMA (the dS waves issue none)
+  static constexpr int kDmaPerWave = 2 * RTile<D>::kFrags / 4;
   static constexpr int kPrefetchNat = 6;
   static constexpr int kPrefetchTr = 4;
 };
@@ -384,6 +385,8 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
     const int n_rt = (r_end - r_begin + kTileK - 1) / kTileK;
 
     auto stage_of = [&](int rt) { return lds0 + (rt % C::kStages) * C::kStageBytes; };
+    // P waves only: this wave's share of tile rt (Q and dO fragments; wave 0
+    // also the row statistics)
     auto issue = [&](int rt) {
       const uint32_t stage = stage_of(rt);
       const int rho0 = r_begin + kTileK * rt;
@@ -421,27 +424,32 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
     }
     // settle the per-item loads before any tile DMA is in flight
     wait_vmcnt<0>();
-    if (n_rt > 0) issue(0);
-    if (n_rt > 1) issue(1);
+    if (pwave) {
+      if (n_rt > 0) issue(0);
+      if (n_rt > 1) issue(1);
+    }
     f32x16 acc[NDB];  // dV^T (P wave) or dK^T (dS wave) of the pair's keys
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-    // Opening barrier of tile rt: this wave's share of tile rt has landed
-    // once at most tile rt+1's loads are in flight; after the barrier the
-    // stage of tile rt-1 takes tile rt+2.  Returns whether any row of the
-    // tile sees any of the pair's keys, and whether all rows see all of them.
+    // Opening barrier of tile rt: a P wave's share of tile rt has landed
+    // once at most tile rt+1's loads are in flight.  Tile rt+2 goes into the
+    // stage of tile rt-1, free after this barrier; the P waves issue it at
+    // the end of step rt, where they would otherwise wait for the dS waves.
+    // Returns whether any row of the tile sees any of the pair's keys, and
+    // whether all rows see all of them.
     auto open_tile = [&](int rt, bool& full) {
-      if (rt + 1 < n_rt) {
-        if (wave == 0) wait_vmcnt<C::kDmaPerWave + 1>();
-        else wait_vmcnt<C::kDmaPerWave>();
-      } else {
-        wait_vmcnt<0>();
+      if (pwave) {
+        if (rt + 1 < n_rt) {
+          if (wave == 0) wait_vmcnt<C::kDmaPerWave + 1>();
+          else wait_vmcnt<C::kDmaPerWave>();
+        } else {
+          wait_vmcnt<0>();
+        }
       }
       block_barrier();
-      if (rt + 2 < n_rt) issue(rt + 2);
       // Rows past r_end belong to blocks that see none of the item's keys
       // (their statistics, or the padding rows, say so), so every row's own
       // interval decides; draft keys: the row's block.
@@ -529,6 +537,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
                     o, pb[i / (2 * NDB)][(i / NDB) % 2], acc[i % NDB], 0, 0, 0);
               });
         }
+        if (rt + 2 < n_rt) issue(rt + 2);
       }
     } else {
       for (int rt = 0; rt < n_rt; ++rt) {
