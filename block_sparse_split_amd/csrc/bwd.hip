@@ -17,14 +17,14 @@
 //   dq    query-stationary, the forward's work items and LPT queues, eight
 //         waves of 32 rows: per 64-key step S^T = K Q^T and dP^T = V dO^T
 //         (lanes own query columns), dS^T in registers, dQ^T += K^T dS^T;
-//         K (one rotated fragment-major copy serves both the natural and
-//         the transposed read) and V arrive by DMA in a 3-stage ring; split
-//         query tiles write partial slots that a reduction kernel sums;
+//         K (read naturally for S^T and transposed for dQ^T) and V arrive by
+//         DMA in a 3-stage ring; split query tiles write partial slots that
+//         a reduction kernel sums;
 //   dkdv  key-stationary: a wave owns 32 keys (K^T, V^T B operands in
 //         registers) and walks 64-row tiles of the query rows that may see
 //         them: S = Q K^T and dP = dO V^T (lanes own key columns), then
-//         dV^T += dO^T P and dK^T += Q^T dS; Q and dO tiles (rotated
-//         fragment-major) and the row statistics arrive by DMA in a 3-stage
+//         dV^T += dO^T P and dK^T += Q^T dS; Q and dO tiles and
+//         the row statistics arrive by DMA in a 3-stage
 //         ring; each key's gradients are written once.
 #include "launch.h"
 #include "tile_stage.h"
@@ -92,12 +92,12 @@ template <int D>
 struct DqCfg {
   static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
-  // K (rotated fragment-major: natural and transposed reads), V (fragment-major)
-  static constexpr int kVOff = RTile<D>::kBytes;
-  static constexpr int kStageBytes = kVOff + Tile<D>::kBytes;
+  // K (natural and transposed reads), then V (natural reads)
+  static constexpr int kVOff = ITile<D>::kBytes;
+  static constexpr int kStageBytes = 2 * ITile<D>::kBytes;
   static constexpr int kStages = 3;
   static constexpr int kLdsBytes = kStages * kStageBytes;
-  static constexpr int kDmaPerWave = 2 * Tile<D>::kBlocks / kWaves;
+  static constexpr int kDmaPerWave = 2 * ITile<D>::kBlocks / kWaves;
   static constexpr int kPrefetchNat = 6;
   static constexpr int kPrefetchTr = 4;
 };
@@ -106,17 +106,17 @@ template <int D>
 __device__ __forceinline__ void dq_issue(const __bf16* Kg, const __bf16* Vg, const Step& st,
                                          int head, int hkv, uint32_t stage, int wave, int lane) {
   using C = DqCfg<D>;
-  constexpr int B = Tile<D>::kBlocks;
+  constexpr int B = ITile<D>::kBlocks;
 #pragma unroll
   for (int i = 0; i < C::kDmaPerWave; ++i) {
     const int u = wave * C::kDmaPerWave + i;
     const bool isv = u >= B;
+    const int g = isv ? u - B : u;
     int row, col;
-    if (isv) frag_major_rc<D>(u - B, lane, row, col);
-    else rot_major_rc<D>(u, lane, row, col);
+    itile_rc<D>(g, lane, row, col);
     const int grow = min(row, st.n - 1);
     dma16((isv ? Vg : Kg) + ((int64_t)(st.row + grow) * hkv + head) * D + col,
-          stage + (isv ? C::kVOff + (u - B) * 1024 : u * RTile<D>::kFragStride));
+          stage + (isv ? C::kVOff : 0) + g * ITile<D>::kBlockStride);
   }
 }
 
@@ -140,9 +140,9 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
   const __bf16* Qg = static_cast<const __bf16*>(a.Q);
   const __bf16* dOg = static_cast<const __bf16*>(a.dO);
   const uint32_t lds0 = lds_addr(smem);
-  const uint32_t knoff = rot_nat_offset(lane);
-  const uint32_t voff = C::kVOff + 16 * lane;
-  const uint32_t taoff = rot_tr_offset_a(lane), tboff = rot_tr_offset_b(lane);
+  const uint32_t knoff = itile_nat_offset<D>(lane);
+  const uint32_t voff = C::kVOff + itile_nat_offset<D>(lane);
+  const uint32_t troff = itile_tr_offset<D>(lane);
 
   for (int qi = qbeg; qi < qend; ++qi) {
     const sched_t it = items + queue[qi] * I_WORDS;
@@ -221,8 +221,8 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
         // MFMA i: d-step t = i / 2; even i: S^T (K), odd i: dP^T (V)
         lds_pipelined<2 * (D / 16), C::kPrefetchNat>(
             [&](int i) {
-              return i % 2 == 0 ? rot_frag_nat<D>(kbase, kb, i / 2)
-                                : frag_nat<D>(vbase, kb, i / 2);
+              return i % 2 == 0 ? itile_nat<D>(kbase, kb, i / 2)
+                                : itile_nat<D>(vbase, kb, i / 2);
             },
             [&](int i, const bf16x8& x) {
               if (i % 2 == 0)
@@ -240,12 +240,11 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      const uint32_t ta = opaque(stage + taoff);
-      const uint32_t tb = opaque(stage + tboff);
+      const uint32_t tbase = opaque(stage + troff);
       constexpr int NDB = D / 32;
       // MFMA i: key block kb, k-half t2, output block db
       lds_pipelined<4 * NDB, C::kPrefetchTr>(
-          [&](int i) { return rot_frag_tr<D>(ta, tb, i % NDB, i / (2 * NDB), (i / NDB) % 2); },
+          [&](int i) { return itile_tr<D>(tbase, i % NDB, i / (2 * NDB), (i / NDB) % 2); },
           [&](int i, const bf16x8& k) {
             dq[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 k, ds[i / (2 * NDB)][(i / NDB) % 2], dq[i % NDB], 0, 0, 0);
@@ -304,25 +303,25 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const int32_t* S, const 
 // so a wave needs half the registers of one doing both, two waves fit per
 // SIMD and one hides the other's LDS latency.  A 64-row query tile takes two
 // half steps: S/P and dP (P goes to the exchange buffer), barrier, then dV
-// and dK.  Q and dO tiles (rotated fragment-major: natural reads for S and
-// dP, transposed reads for dV and dK) and the per-row statistics (L2, D and
-// the row's visible interval) arrive by DMA in a 3-stage ring.  Every key's
-// gradients are written once.
+// and dK.  Q and dO tiles (natural reads for S and dP, transposed reads for
+// dV and dK) and the per-row statistics (D, L2 and the row's visible
+// interval) arrive by DMA in a 3-stage ring.  Every key's gradients are
+// written once.
 template <int D>
 struct KvCfg {
   static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
-  // Q, dO (rotated fragment-major), then 1 KB of row statistics:
+  // Q, dO (interleaved row tiles), then 1 KB of row statistics:
   // D [0, 256), L2 [256, 512), lo [512, 768), anchor [768, 1024)
-  static constexpr int kOOff = RTile<D>::kBytes;
-  static constexpr int kStatOff = 2 * RTile<D>::kBytes;
+  static constexpr int kOOff = ITile<D>::kBytes;
+  static constexpr int kStatOff = 2 * ITile<D>::kBytes;
   static constexpr int kStageBytes = kStatOff + 1024;
   static constexpr int kStages = 3;
   // P exchange: per pair 64 rows x 32 keys of bf16, in MFMA B-operand order
   static constexpr int kXOff = kStages * kStageBytes;
   static constexpr int kLdsBytes = kXOff + 4 * 4096;
   // the four P waves issue all tile DMA (the dS waves issue none)
-  static constexpr int kDmaPerWave = 2 * RTile<D>::kFrags / 4;
+  static constexpr int kDmaPerWave = 2 * ITile<D>::kBlocks / 4;
   static constexpr int kPrefetchNat = 6;
   static constexpr int kPrefetchTr = 4;
 };
@@ -356,8 +355,8 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
   const __bf16* Qg = static_cast<const __bf16*>(a.Q);
   const __bf16* dOg = static_cast<const __bf16*>(a.dO);
   const uint32_t lds0 = lds_addr(smem);
-  const uint32_t noff = rot_nat_offset(lane);
-  const uint32_t taoff = rot_tr_offset_a(lane), tboff = rot_tr_offset_b(lane);
+  const uint32_t noff = itile_nat_offset<D>(lane);
+  const uint32_t troff = itile_tr_offset<D>(lane);
   const uint32_t xslot = lds0 + C::kXOff + pair * 4096 + 16 * lane;
 
   for (int qi = qbeg; qi < qend; ++qi) {
@@ -393,14 +392,14 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
 #pragma unroll
       for (int i = 0; i < C::kDmaPerWave; ++i) {
         const int u = wave * C::kDmaPerWave + i;
-        const bool iso = u >= RTile<D>::kFrags;  // dO after Q
-        const int f = iso ? u - RTile<D>::kFrags : u;
+        const bool iso = u >= ITile<D>::kBlocks;  // dO after Q
+        const int g = iso ? u - ITile<D>::kBlocks : u;
         int row, col;
-        rot_major_rc<D>(f, lane, row, col);
+        itile_rc<D>(g, lane, row, col);
         const int rho = min(rho0 + row, r_end - 1);
         const int64_t grow = (int64_t)(rho >> lgG) * hq + head * G + (rho & (G - 1));
         dma16((iso ? dOg : Qg) + grow * D + col,
-              stage + (iso ? C::kOOff : 0) + f * RTile<D>::kFragStride);
+              stage + (iso ? C::kOOff : 0) + g * ITile<D>::kBlockStride);
       }
       if (wave == 0) {
         // 16 lanes per statistic (D, L2, lo, anchor: consecutive arrays of
@@ -483,7 +482,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
           const uint32_t qfb = opaque(stage + noff);
           // MFMA i: query block qb = i % 2, d-step t = i / 2
           lds_pipelined<2 * (D / 16), C::kPrefetchNat>(
-              [&](int i) { return rot_frag_nat<D>(qfb, i % 2, i / 2); },
+              [&](int i) { return itile_nat<D>(qfb, i % 2, i / 2); },
               [&](int i, const bf16x8& q) {
                 sacc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q, kv[i / 2], sacc[i % 2],
                                                                       0, 0, 0);
@@ -525,13 +524,10 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
         wait_lgkmcnt0();
         block_barrier();
         if (any) {
-          const uint32_t ota = opaque(stage + taoff + C::kOOff);
-          const uint32_t otb = opaque(stage + tboff + C::kOOff);
+          const uint32_t otb = opaque(stage + troff + C::kOOff);
           // MFMA i: query block qb, k-half t2, output block db
           lds_pipelined<4 * NDB, C::kPrefetchTr>(
-              [&](int i) {
-                return rot_frag_tr<D>(ota, otb, i % NDB, i / (2 * NDB), (i / NDB) % 2);
-              },
+              [&](int i) { return itile_tr<D>(otb, i % NDB, i / (2 * NDB), (i / NDB) % 2); },
               [&](int i, const bf16x8& o) {
                 acc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     o, pb[i / (2 * NDB)][(i / NDB) % 2], acc[i % NDB], 0, 0, 0);
@@ -553,7 +549,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
             for (int r = 0; r < 16; ++r) dp[qb][r] = 0.f;
           const uint32_t ofb = opaque(stage + noff + C::kOOff);
           lds_pipelined<2 * (D / 16), C::kPrefetchNat>(
-              [&](int i) { return rot_frag_nat<D>(ofb, i % 2, i / 2); },
+              [&](int i) { return itile_nat<D>(ofb, i % 2, i / 2); },
               [&](int i, const bf16x8& o) {
                 dp[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, kv[i / 2], dp[i % 2], 0,
                                                                     0, 0);
@@ -579,11 +575,9 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
                 }
               }
             }
-          const uint32_t qta = opaque(stage + taoff), qtb = opaque(stage + tboff);
+          const uint32_t qtb = opaque(stage + troff);
           lds_pipelined<4 * NDB, C::kPrefetchTr>(
-              [&](int i) {
-                return rot_frag_tr<D>(qta, qtb, i % NDB, i / (2 * NDB), (i / NDB) % 2);
-              },
+              [&](int i) { return itile_tr<D>(qtb, i % NDB, i / (2 * NDB), (i / NDB) % 2); },
               [&](int i, const bf16x8& q) {
                 acc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     q, dsb[i / (2 * NDB)][(i / NDB) % 2], acc[i % NDB], 0, 0, 0);

@@ -18,16 +18,14 @@
 // v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T held in registers),
 // so every lane owns one query column: the softmax max/sum over keys is a
 // per-lane reduction plus one exchange with lane ^ 32.  P^T is rounded to
-// bf16 in place and feeds O^T += V^T P^T directly as the B operand; V is
-// staged transposed in LDS (keys of a 16-key group permuted to match the
-// accumulator layout of S^T), so no register transpose is needed.  The
+// bf16 in place and feeds O^T += V^T P^T directly as the B operand; the V^T
+// operand comes from transposed LDS reads whose key order matches the
+// accumulator layout of S^T, so no register transpose is needed.  The
 // online softmax works in base 2 with the scale folded into one FMA and
 // rescales O only when the running maximum grows by more than 2^8, which is
-// exact (the same maximum is used for O and for the sum).  K/V tiles are
-// double-buffered in LDS: the next step's global loads are in flight while
-// the current step computes.  Tiles that straddle an anchor bound are masked
-// per element; fully visible tiles skip the mask, invisible ones skip the
-// MFMAs.
+// exact (the same maximum is used for O and for the sum).  Tiles that
+// straddle an anchor bound are masked per element; fully visible tiles skip
+// the mask, invisible ones skip the MFMAs.
 #include "launch.h"
 #include "tile_stage.h"
 #include "timing.h"
@@ -41,28 +39,21 @@ constexpr int kQB = 2;             // 32-query column blocks per wave
 constexpr int kKB = kTileK / 32;   // 32-key blocks per step
 
 // ---------------------------------------------------------------------------
-// bf16 path.  Eight waves (two per SIMD, so one wave's MFMAs overlap the
-// other's softmax) each own 32 query rows of the 256-row tile.  K and V tiles
-// reach LDS by direct global->LDS DMA (global_load_lds_dwordx4) into a
-// 3-stage ring, so two steps of loads are in flight while one computes and no
-// registers hold staged data.  Each DMA lane picks its own global address, so
-// the tiles are written in the order they are consumed:
-//   K  fragment-major: the A operand of MFMA (key block kb, d-step t) -- 32
-//      rows x 32 bytes -- is one contiguous 1 KB, lane L at byte 16 L;
-//   V  in blocks of 4 keys x 16 d (128 bytes, row-major inside), grouped per
-//      4-key quad; a 16-lane ds_read_b64_tr_b16 of one block returns, in lane
-//      i, column i of the 4 keys -- half of a V^T A-operand fragment.
-// Every LDS read is then one base register plus an immediate offset, reads
-// are contiguous (no bank conflicts) and V is never transposed in memory.
+// bf16 path.  Eight waves (two per SIMD) each own 32 query rows of the
+// 256-row tile.  K and V tiles reach LDS by direct global->LDS DMA
+// (global_load_lds_dwordx4, whole rows per instruction) into a 4-stage ring
+// of interleaved row tiles, so loads run two steps ahead and no registers
+// hold staged data; K is read as natural MFMA operands, V as transposed ones,
+// each one base register plus an immediate offset, without bank conflicts.
 template <int D>
 struct FwdCfg {
   static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kTileBytes = Tile<D>::kBytes;       // 16 KB (d=128) / 8 KB
+  static constexpr int kTileBytes = ITile<D>::kBytes;     // 17 KB (d=128) / 9 KB
   static constexpr int kStageBytes = 2 * kTileBytes;       // K then V
   static constexpr int kStages = 4;
   static constexpr int kLdsBytes = kStages * kStageBytes;
-  static constexpr int kDmaPerWave = 2 * (kTileBytes / 1024) / kWaves;
+  static constexpr int kDmaPerWave = 2 * ITile<D>::kBlocks / kWaves;
   // LDS operand reads kept in flight ahead of the MFMAs (K: one read per
   // fragment, V: two transposed reads per fragment)
   static constexpr int kPrefetchK = 6;
@@ -70,22 +61,25 @@ struct FwdCfg {
 };
 
 // Issue this wave's share of the DMA for one step into `stage` (LDS bytes):
-// K fragment-major, then V block-major.  Rows past the end of a ragged step
-// repeat the last valid row (their keys are masked, the values stay finite).
+// K blocks, then V blocks, both interleaved row tiles.  Rows past the end of
+// a ragged step repeat the last valid row (their keys are masked, the values
+// stay finite).
 template <int D>
 __device__ __forceinline__ void issue_step(const __bf16* Kg, const __bf16* Vg, const Step& st,
                                            int head, int hkv, uint32_t stage, int wave,
                                            int lane) {
   using C = FwdCfg<D>;
+  constexpr int B = ITile<D>::kBlocks;
 #pragma unroll
   for (int i = 0; i < C::kDmaPerWave; ++i) {
     const int u = wave * C::kDmaPerWave + i;
+    const bool isv = u >= B;
+    const int g = isv ? u - B : u;
     int row, col;
-    const bool isv = u >= Tile<D>::kBlocks;
-    if (isv) block_major_rc<D>(u - Tile<D>::kBlocks, lane, row, col);
-    else frag_major_rc<D>(u, lane, row, col);
+    itile_rc<D>(g, lane, row, col);
     const int grow = min(row, st.n - 1);
-    dma16((isv ? Vg : Kg) + ((int64_t)(st.row + grow) * hkv + head) * D + col, stage + u * 1024);
+    dma16((isv ? Vg : Kg) + ((int64_t)(st.row + grow) * hkv + head) * D + col,
+          stage + (isv ? C::kTileBytes : 0) + g * ITile<D>::kBlockStride);
   }
 }
 
@@ -121,8 +115,8 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
   const uint32_t lds0 = lds_addr(smem);
   // per-lane LDS byte offsets inside a stage: K fragment lane slot and the
   // transposed V read
-  const uint32_t koff = 16 * lane;
-  const uint32_t voff = C::kTileBytes + tr_lane_offset<D>(lane);
+  const uint32_t koff = itile_nat_offset<D>(lane);
+  const uint32_t voff = C::kTileBytes + itile_tr_offset<D>(lane);
 
   for (int qi = qbeg; qi < qend; ++qi) {
     const sched_t it = items + queue[qi] * I_WORDS;
@@ -200,7 +194,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
       constexpr int NDB = D / 32;
       // MFMA i: key block kb, k-half t2, output block db
       lds_pipelined<4 * NDB, C::kPrefetchV>(
-          [&](int i) { return frag_tr<D>(vbase, i % NDB, i / (2 * NDB), (i / NDB) % 2); },
+          [&](int i) { return itile_tr<D>(vbase, i % NDB, i / (2 * NDB), (i / NDB) % 2); },
           [&](int i, const bf16x8& v) {
             o[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 v, pf[i / (2 * NDB)][(i / NDB) % 2], o[i % NDB], 0, 0, 0);
@@ -231,7 +225,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
         const uint32_t kbase = opaque(stage_of(p) + koff);
         // MFMA i: d-step t = i / 2, key block kb = i % 2
         lds_pipelined<2 * (D / 16), C::kPrefetchK>(
-            [&](int i) { return frag_nat<D>(kbase, i % 2, i / 2); },
+            [&](int i) { return itile_nat<D>(kbase, i % 2, i / 2); },
             [&](int i, const bf16x8& k) {
               sacc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[i / 2], sacc[i % 2], 0,
                                                                     0, 0);

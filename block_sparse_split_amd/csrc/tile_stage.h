@@ -1,40 +1,22 @@
-// Direct-to-LDS tile staging and LDS fragment reads (gfx950 kernels).
+// Direct-to-LDS tile staging and LDS operand reads (gfx950 kernels).
 //
 // Tiles of 64 rows x D bf16 (rows are keys or query rows) are copied from
 // HBM into LDS with global_load_lds_dwordx4: every lane of a wave moves 16
-// bytes and writes them at lds_base + 16 * lane.  Because each lane chooses
-// its own global address, a tile can be written directly in the order the
-// MFMAs consume it, in one of two layouts (both 64 x D x 2 bytes):
-//
-//   fragment-major  1 KB block (kb, t), kb in {0,1}, t < D/16, holds the A
-//                   operand of a 32x32x16 MFMA with lane = row: lane L's 16
-//                   bytes are row 32 kb + L % 32, columns 16 t + 8 (L / 32).
-//   block-major     4-row quads (8 D bytes each) of 4 x 16 blocks (128 bytes,
-//                   row-major inside).  A 16-lane ds_read_b64_tr_b16 over one
-//                   block returns, in lane i, column i of its 4 rows; two such
-//                   reads form the A operand with lane = column and the 8
-//                   rows {4h + 0..3, 8 + 4h + 0..3} that a 32x32 accumulator
-//                   lane (half h) holds, so results feed MFMAs without any
-//                   register transpose.
-//
-// Reads are contiguous per instruction (no bank conflicts) and use one base
-// register plus an immediate offset.  The DMA is issued as inline asm so the
-// compiler neither waits on it nor serialises it against LDS reads; kernels
-// wait with explicit vmcnt counts and a bare s_barrier.
+// bytes and writes them at lds_base + 16 * lane, choosing its own global
+// address.  All tiles use one layout (the interleaved row tile below): each
+// DMA instruction moves whole rows, and MFMA operands are read either
+// naturally (lane = row, ds_read_b128) or transposed (lane = column,
+// ds_read_b64_tr_b16) without bank conflicts and without any register
+// transpose.  Reads use one base register plus an immediate offset.  The
+// DMA is issued as inline asm so the compiler neither waits on it nor
+// serialises it against LDS reads; kernels wait with explicit vmcnt counts
+// and a bare s_barrier.
 #pragma once
 #include "device_common.h"
 
 namespace skv {
 
 typedef short short4v __attribute__((ext_vector_type(4)));
-
-template <int D>
-struct Tile {
-  static constexpr int kBytes = kTileK * D * 2;   // 16 KB for d = 128
-  static constexpr int kBlocks = kBytes / 1024;   // DMA blocks per tile
-  static constexpr int kFragsPerKb = D / 16;      // fragment-major: t range
-  static constexpr int kQuadBytes = 4 * D * 2;    // block-major: one 4-row quad
-};
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -104,97 +86,67 @@ __device__ __forceinline__ short4v ds_read_tr(uint32_t addr) {
       (__attribute__((address_space(3))) short4v*)(static_cast<uintptr_t>(addr)));
 }
 
-// Row and column that byte 16*lane of DMA block u carries, per layout.
-template <int D>
-__device__ __forceinline__ void frag_major_rc(int u, int lane, int& row, int& col) {
-  row = (u / Tile<D>::kFragsPerKb) * 32 + (lane & 31);
-  col = 16 * (u % Tile<D>::kFragsPerKb) + 8 * (lane >> 5);
-}
-template <int D>
-__device__ __forceinline__ void block_major_rc(int u, int lane, int& row, int& col) {
-  const int byte = u * 1024 + 16 * lane;
-  const int q = byte / Tile<D>::kQuadBytes, w = byte % Tile<D>::kQuadBytes;
-  row = 4 * q + (w & 127) / 32;
-  col = 16 * (w / 128) + 8 * ((w & 31) / 16);
-}
-
-// Per-lane byte offset of the transposed read within a block-major tile: the
-// 16-lane group G = lane / 16 reads quad (base + G / 2), block (2 db + G % 2).
-template <int D>
-__device__ __forceinline__ uint32_t tr_lane_offset(int lane) {
-  return (lane >> 5) * Tile<D>::kQuadBytes + ((lane >> 4) & 1) * 128 + 8 * (lane & 15);
-}
-
-// A operand (lane = column d = 32 db + lane % 32) for rows
-// 32 rb + 16 t2 + {4h + 0..3, 8 + 4h + 0..3} of a block-major tile at `base`
-// (base already includes tr_lane_offset).
-template <int D>
-__device__ __forceinline__ bf16x8 frag_tr(uint32_t base, int db, int rb, int t2) {
-  const uint32_t q0 = base + (8 * rb + 4 * t2) * Tile<D>::kQuadBytes + db * 256;
-  const short4v lo4 = ds_read_tr(q0);
-  const short4v hi4 = ds_read_tr(q0 + 2 * Tile<D>::kQuadBytes);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// A operand (lane = row 32 kb + lane % 32) of d-step t of a fragment-major
-// tile at `base` (base already includes 16 * lane).
-template <int D>
-__device__ __forceinline__ bf16x8 frag_nat(uint32_t base, int kb, int t) {
-  return lds_read16(base + (kb * Tile<D>::kFragsPerKb + t) * 1024);
-}
-
 // ---------------------------------------------------------------------------
-// Rotated fragment-major tile: one copy that serves both the natural A
-// operand (lane = row) and the transposed one (lane = column).  Fragment
-// (kb, t) sits at (kb * D/16 + t) * 1088 bytes; slot s < 32 holds row
-// 32 kb + s, columns 16 t .. +7; slot s >= 32 holds row 32 kb + ((s - 24) & 31),
-// columns 16 t + 8 .. +15 (the second half rotated by 8 rows).  The rotation
-// puts the two column halves of a row 128 bytes apart modulo the 256-byte
-// bank window and the 64-byte fragment skew separates neighbouring fragments,
-// so 32 lanes of a transposed read touch 256 distinct bytes.
+// Interleaved row tile: the one LDS layout of every K, V, Q and dO tile.
+// A DMA instruction moves whole rows: lane i of block g reads 16 bytes
+// (8 columns) of row g*RB + i % RB, column chunk i / RB, where RB = 1024 /
+// (2 D) rows fill one 1 KB block (RB = 4 for d = 128, 8 for d = 64), so each
+// instruction covers 8 full 128-byte lines of K/V rows.  In LDS, block g
+// sits at g * (1024 + 16 RB): the 16-byte chunk c of row r is at
+//   (r / RB) * (1024 + 16 RB) + (c * RB + r % RB) * 16.
+// The chunk of 16 consecutive rows then falls in 16 distinct 16-byte bank
+// groups (natural reads: lane = row), and 4 rows x 32 columns of a
+// transposed read fall in distinct banks for d = 128.
 template <int D>
-struct RTile {
-  static constexpr int kFragStride = 1088;
-  static constexpr int kFrags = 2 * (D / 16);
-  static constexpr int kBytes = kFrags * kFragStride;
+struct ITile {
+  static constexpr int kRB = 1024 / (2 * D);
+  static constexpr int kBlockStride = 1024 + 16 * kRB;
+  static constexpr int kBlocks = kTileK / kRB;
+  static constexpr int kBytes = kBlocks * kBlockStride;
 };
 
-// Row/column of DMA lane `lane` for fragment u (written at u * kFragStride).
+// Row and column (first of 8) that DMA lane `lane` of block g carries.
 template <int D>
-__device__ __forceinline__ void rot_major_rc(int u, int lane, int& row, int& col) {
-  row = (u / (D / 16)) * 32 + (lane < 32 ? lane : ((lane - 24) & 31));
-  col = 16 * (u % (D / 16)) + 8 * (lane >> 5);
+__device__ __forceinline__ void itile_rc(int g, int lane, int& row, int& col) {
+  row = g * ITile<D>::kRB + lane % ITile<D>::kRB;
+  col = 8 * (lane / ITile<D>::kRB);
 }
 
-// Natural read: lane L's 16 bytes of fragment (kb, t) are at
-// base + (kb * D/16 + t) * 1088 with base = tile + rot_nat_offset(L).
-__device__ __forceinline__ uint32_t rot_nat_offset(int lane) {
-  return 16 * (lane < 32 ? lane : 32 + ((lane - 40) & 31));
-}
 template <int D>
-__device__ __forceinline__ bf16x8 rot_frag_nat(uint32_t base, int kb, int t) {
-  return lds_read16(base + (kb * (D / 16) + t) * RTile<D>::kFragStride);
+__device__ __forceinline__ uint32_t itile_addr(int row, int chunk) {
+  using T = ITile<D>;
+  return (row / T::kRB) * T::kBlockStride + (chunk * T::kRB + row % T::kRB) * 16;
 }
 
-// Transposed read (lane = column 32 db + lane % 32, rows of 32-row block rb
-// at k-step t2).  Source lane j = lane % 16 supplies row 4h + j / 4 (+16 t2,
-// +8 for the second read) and columns 4 (j % 4) .. +3 of its 16-column group.
-// Rows 0..7 of a block wrap in the rotated half, so the first read of t2 = 0
-// uses its own lane offset (A); every other read uses offset B.
-__device__ __forceinline__ uint32_t rot_tr_offset_a(int lane) {
-  const int j = lane & 15, m = j >> 2, q = j & 3, half = q >> 1;
-  return 16 * (56 * half + 4 * (lane >> 5) + m) + 8 * (q & 1) + 1088 * ((lane >> 4) & 1);
-}
-__device__ __forceinline__ uint32_t rot_tr_offset_b(int lane) {
-  const int j = lane & 15, m = j >> 2, q = j & 3, half = q >> 1;
-  return 16 * (24 * half + 4 * (lane >> 5) + m) + 8 * (q & 1) + 1088 * ((lane >> 4) & 1);
+// Natural A operand (lane = row 32 kb + lane % 32, columns 16 t + 8 (lane /
+// 32) .. +7): base = tile + itile_nat_offset(lane).
+template <int D>
+__device__ __forceinline__ uint32_t itile_nat_offset(int lane) {
+  return itile_addr<D>(lane & 31, lane >> 5);
 }
 template <int D>
-__device__ __forceinline__ bf16x8 rot_frag_tr(uint32_t base_a, uint32_t base_b, int db, int rb,
-                                              int t2) {
-  const uint32_t f = (rb * (D / 16) + 2 * db) * RTile<D>::kFragStride;
-  const short4v lo4 = t2 == 0 ? ds_read_tr(base_a + f) : ds_read_tr(base_b + f + 256 * t2);
-  const short4v hi4 = ds_read_tr(base_b + f + 256 * t2 + 128);
+__device__ __forceinline__ bf16x8 itile_nat(uint32_t base, int kb, int t) {
+  using T = ITile<D>;
+  return lds_read16(base + kb * (32 / T::kRB) * T::kBlockStride + t * 2 * T::kRB * 16);
+}
+
+// Transposed A operand (lane = column 32 db + lane % 32; its 8 k values are
+// rows 32 rb + 16 t2 + {4 h + 0..3, 8 + 4 h + 0..3}, h = lane / 32, the row
+// order of a 32x32 accumulator lane): two ds_read_b64_tr_b16, each over 4
+// rows.  Source lane j of 16-lane group G reads row 4 h + j / 4, columns
+// 16 (G % 2) + 4 (j % 4) .. +3.
+template <int D>
+__device__ __forceinline__ uint32_t itile_tr_offset(int lane) {
+  const int j = lane & 15, grp = (lane >> 4) & 1, h = lane >> 5;
+  const int row = 4 * h + j / 4, col = 16 * grp + 4 * (j % 4);
+  return itile_addr<D>(row, col / 8) + ((col % 8) / 4) * 8;
+}
+template <int D>
+__device__ __forceinline__ bf16x8 itile_tr(uint32_t base, int db, int rb, int t2) {
+  using T = ITile<D>;
+  const uint32_t c = ((32 * rb + 16 * t2) / T::kRB) * T::kBlockStride + 4 * db * T::kRB * 16;
+  const short4v lo4 = ds_read_tr(base + c);
+  const short4v hi4 = ds_read_tr(base + c + (8 / T::kRB) * T::kBlockStride);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
