@@ -45,6 +45,16 @@ def visible_elements(g, hq):
     return int(per_block.sum()) * 16 * hq
 
 
+def shard_visible_elements(g, hq, chunk_ids, with_draft):
+    """Visible pairs restricted to the keys of the given chunks (+ draft)."""
+    a = g.anchors.astype(np.int64)[:, None]
+    lo = g.lo.astype(np.int64)[:, None]
+    cp = g.chunk_pos[chunk_ids].astype(np.int64)[None, :]
+    ce = cp + g.chunk_len[chunk_ids].astype(np.int64)[None, :]
+    keys = np.clip(np.minimum(a, ce) - np.maximum(lo, cp), 0, None).sum()
+    return (int(keys) + (16 * len(g.anchors) if with_draft else 0)) * 16 * hq
+
+
 def cpu_baseline(w, g, t, target_s=15.0):
     """The fp64 oracle (as it stands) on a bounded sample of anchor blocks,
     forward + backward, timed on this host's cores."""
@@ -113,6 +123,83 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
+def bench_merge64(args):
+    """1M-context job: the forward partial of each of the 64 LPT shards (draft
+    keys on shard 0) into one partial buffer, then the 64-way LSE merge.
+    value = forward TFLOP/s over the 64 partials; the merge is reported in
+    GB/s against HBM."""
+    import torch
+    from block_sparse_split_amd import splitkv as skv
+    from block_sparse_split_amd import shards
+    from block_sparse_split_amd import workloads as wl
+
+    w, g, _ = wl.make("ctx1m_merge64", args.seed, tensors=False)
+    w32 = wl.scaled(w, dtype="f32")
+    ids, _, _, load = shards.lpt_shards(w, g, w.n_shards)
+    t = wl.draw_tensors(w, g, args.seed, chunk_ids=[])
+    dev = lambda x: torch.from_numpy(x).cuda().to(torch.bfloat16)
+    Q, Kd, Vd = dev(t.Q), dev(t.Kd), dev(t.Vd)
+    Op = torch.empty((w.n_shards, w.nq, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+    Lp = torch.empty((w.n_shards, w.nq, w.hq), dtype=torch.float32, device="cuda")
+    Om = torch.empty((w.nq, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+    Lm = torch.empty((w.nq, w.hq), dtype=torch.float32, device="cuda")
+    fwd_ms = 0.0
+    E = 0
+    for r in range(w.n_shards):
+        if r % 16 == 0:
+            log(f"shard {r}")
+        sh = skv.Shard(shards.shard_problem(w, g, ids[r], r == 0))
+        # K/V drawn in fp32, rounded to bf16 on the device (round to nearest even)
+        K = dev(wl.draw_kv_chunks(w32, g, args.seed, ids[r], "K"))
+        V = dev(wl.draw_kv_chunks(w32, g, args.seed, ids[r], "V"))
+        kd, vd = (Kd, Vd) if r == 0 else (None, None)
+        sh.fwd(Q, K, V, kd, vd, Op[r], Lp[r])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            sh.fwd(Q, K, V, kd, vd, Op[r], Lp[r])
+        e1.record()
+        torch.cuda.synchronize()
+        fwd_ms += e0.elapsed_time(e1) / args.steps
+        E += shard_visible_elements(g, w.hq, ids[r], r == 0)
+        del K, V, sh
+    for _ in range(args.warmup):
+        skv.skv_merge_lse(Op, Lp, Om, Lm)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        skv.skv_merge_lse(Op, Lp, Om, Lm)
+    e1.record()
+    torch.cuda.synchronize()
+    merge_ms = e0.elapsed_time(e1) / args.steps
+    merge_bytes = Op.numel() * 2 + Lp.numel() * 4 + Om.numel() * 2 + Lm.numel() * 4
+    flops = 4.0 * w.d * E
+    ms = fwd_ms + merge_ms
+    out = {
+        "metric": METRIC, "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "context": g.ctx, "draft_queries": w.nq,
+                   "anchor_blocks": w.nb, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d,
+                   "chunk": w.chunk, "shards": w.n_shards, "seed": args.seed,
+                   "step": "64 shard forwards + 64-way merge"},
+        "fwd_ms_all_shards": fwd_ms,
+        "fwd_tflops": flops / (fwd_ms * 1e-3) / 1e12,
+        "merge_ms": merge_ms,
+        "merge_gbs": merge_bytes / (merge_ms * 1e-3) / 1e9,
+        "merge_frac_of_hbm_peak": merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "lpt": {"shard_imbalance_64": float(load.max() / load.mean() - 1)},
+        "roofline": {"bound": "hbm", "achieved": merge_bytes / (merge_ms * 1e-3) / 1e9,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "kernel": "merge", "avg_ms": merge_ms, "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,9 +241,25 @@ def main():
         return
     skv.lib()  # fail loudly if the HIP library is not built
 
-    w, g, t = wl.make(args.workload, args.seed, with_grad=True)
-    log(f"workload {w.name}: ctx {g.ctx}, nb {w.nb}, hq {w.hq}, hkv {w.hkv}, d {w.d}")
-    prob = shards.whole_context_problem(w, g)
+    if args.workload == "ctx1m_merge64":
+        return bench_merge64(args)
+    w, g, _ = wl.make(args.workload, args.seed, tensors=False)
+    # the 512K workload is one rank's share of a 64-way LPT split: its chunks
+    # (no draft keys) against all queries, forward only
+    rank_share = w.n_shards > 1
+    rank_load = None
+    if rank_share:
+        ids_all, _, _, rank_load = shards.lpt_shards(w, g, w.n_shards)
+        chunk_ids = ids_all[0]
+    else:
+        chunk_ids = None
+    t = wl.draw_tensors(w, g, args.seed, with_grad=True, chunk_ids=chunk_ids)
+    if rank_share:
+        args.fwd_only = True
+    log(f"workload {w.name}: ctx {g.ctx}, nb {w.nb}, hq {w.hq}, hkv {w.hkv}, d {w.d}"
+        + (f", rank 0 of {w.n_shards}: {len(chunk_ids)} chunks" if rank_share else ""))
+    prob = (shards.shard_problem(w, g, chunk_ids, False) if rank_share
+            else shards.whole_context_problem(w, g))
     plan_times = []
     for _ in range(5):
         t0 = time.perf_counter()
@@ -201,7 +304,8 @@ def main():
     ms = start.elapsed_time(stop) / args.steps
     log(f"{ms:.3f} ms/step")
 
-    E = visible_elements(g, w.hq)
+    E = (shard_visible_elements(g, w.hq, chunk_ids, False) if rank_share
+         else visible_elements(g, w.hq))
     fwd_flops = 4.0 * w.d * E
     bwd_flops = 10.0 * w.d * E
     step_flops = fwd_flops + (0 if args.fwd_only else bwd_flops)
@@ -262,7 +366,10 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if rank_share:
+        out["config"]["rank"] = f"0 of {w.n_shards} (LPT), {len(chunk_ids)} chunks"
+        out["lpt"]["rank_imbalance"] = float(rank_load.max() / rank_load.mean() - 1)
+    if not args.no_cpu_baseline and not rank_share:
         log("timing the fp64 oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(w, g, t)
     print(json.dumps(out), flush=True)

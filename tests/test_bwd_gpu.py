@@ -169,3 +169,41 @@ def test_bwd_full_ctx32k_sampled():
                               Lo)
     check_grad(dK[keys], gk[1], "dK sampled keys")
     check_grad(dV[keys], gk[2], "dV sampled keys")
+
+
+def test_bwd_full_varlen_sampled():
+    """Varlen batch (8 packed sequences, lognormal lengths, late-skewed
+    anchors) on all CUs: dQ and the draft-key gradients on sampled anchor
+    blocks, dK/dV on sampled key ranges (a sequence start, a late range and a
+    sequence end), against the oracle run on exactly the anchor blocks that
+    see those keys."""
+    w, g, t = wl.make("varlen8_fwdbwd", 5, with_grad=True)
+    allc = np.arange(len(g.chunk_pos))
+    announce("bwd full varlen")
+    O, L, _ = gpu_fwd(w, g, t, allc, True)
+    dQ, dK, dV, dKd, dVd = gpu_bwd(w, g, t, allc, True, O, L)
+    scale = wl.softmax_scale(w.d)
+    s0, l0 = int(g.seq_start[1]), int(g.seq_len[1])
+    s1, l1 = int(g.seq_start[3]), int(g.seq_len[3])
+    keys = np.concatenate([np.arange(s0, s0 + 32),
+                           np.arange(s1 + int(0.92 * l1), s1 + int(0.92 * l1) + 48),
+                           np.arange(s1 + l1 - 32, s1 + l1)])
+    sees = (g.lo[:, None] <= keys[None, :]) & (keys[None, :] < g.anchors[:, None])
+    nb = len(g.anchors)
+    blocks = sorted(set(np.nonzero(sees.any(1))[0].tolist()) | {0, nb // 2, nb - 1})
+    announce("bwd full varlen: oracle on", len(blocks), "blocks")
+    Ob, Lb = oracle.attention(t.Q, t.K, t.V, t.Kd, t.Vd, g.anchors, g.lo, scale, blocks=blocks)
+    rows = block_rows(blocks)
+    Of = np.zeros((w.nq, w.hq, w.d))
+    Lf = np.full((w.nq, w.hq), -np.inf)
+    Of[rows], Lf[rows] = Ob, Lb
+    gq = oracle.attention_bwd(t.Q, t.K, t.V, np.arange(g.ctx), g.anchors, g.lo, scale, Of,
+                              t.dO, Lf, t.Kd, t.Vd, blocks=blocks)
+    check_grad(dQ[rows], gq[0][rows], "varlen dQ sampled rows")
+    check_grad(dKd[rows], gq[3][rows], "varlen dKd sampled rows")
+    check_grad(dVd[rows], gq[4][rows], "varlen dVd sampled rows")
+    # rows outside `blocks` see none of the sampled keys
+    gk = oracle.attention_bwd(t.Q, t.K[keys], t.V[keys], keys, g.anchors, g.lo, scale, Of, t.dO,
+                              Lf)
+    check_grad(dK[keys], gk[1], "varlen dK sampled keys")
+    check_grad(dV[keys], gk[2], "varlen dV sampled keys")
