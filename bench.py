@@ -143,27 +143,39 @@ def bench_merge64(args):
     Lp = torch.empty((w.n_shards, w.nq, w.hq), dtype=torch.float32, device="cuda")
     Om = torch.empty((w.nq, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
     Lm = torch.empty((w.nq, w.hq), dtype=torch.float32, device="cuda")
-    fwd_ms = 0.0
-    E = 0
-    for r in range(w.n_shards):
-        if r % 16 == 0:
-            log(f"shard {r}")
-        sh = skv.Shard(shards.shard_problem(w, g, ids[r], r == 0))
-        # K/V drawn in fp32, rounded to bf16 on the device (round to nearest even)
-        K = dev(wl.draw_kv_chunks(w32, g, args.seed, ids[r], "K"))
-        V = dev(wl.draw_kv_chunks(w32, g, args.seed, ids[r], "V"))
-        kd, vd = (Kd, Vd) if r == 0 else (None, None)
-        sh.fwd(Q, K, V, kd, vd, Op[r], Lp[r])
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
+    def run_shards(plan, label):
+        """Forward partial of every shard of a plan into Op/Lp; per-shard ms."""
+        times = []
+        for r in range(w.n_shards):
+            if r % 16 == 0:
+                log(f"{label} shard {r}")
+            sh = skv.Shard(shards.shard_problem(w, g, plan[r], r == 0))
+            # K/V drawn in fp32, rounded to bf16 on the device (round to nearest even)
+            K = dev(wl.draw_kv_chunks(w32, g, args.seed, plan[r], "K"))
+            V = dev(wl.draw_kv_chunks(w32, g, args.seed, plan[r], "V"))
+            kd, vd = (Kd, Vd) if r == 0 else (None, None)
             sh.fwd(Q, K, V, kd, vd, Op[r], Lp[r])
-        e1.record()
-        torch.cuda.synchronize()
-        fwd_ms += e0.elapsed_time(e1) / args.steps
-        E += shard_visible_elements(g, w.hq, ids[r], r == 0)
-        del K, V, sh
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                sh.fwd(Q, K, V, kd, vd, Op[r], Lp[r])
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / args.steps)
+            del K, V, sh
+        return np.array(times)
+
+    # simulated context-parallel step: every rank runs its share; the
+    # slowest one sets the step time.  Contiguous equal-length split first,
+    # then the LPT plan (whose partials stay in Op/Lp for the merge).
+    n = len(g.chunk_pos)
+    contiguous = [np.arange(r * n // w.n_shards, (r + 1) * n // w.n_shards)
+                  for r in range(w.n_shards)]
+    t_cont = run_shards(contiguous, "contiguous")
+    t_lpt = run_shards(ids, "lpt")
+    fwd_ms = float(t_lpt.sum())
+    E = sum(shard_visible_elements(g, w.hq, ids[r], r == 0) for r in range(w.n_shards))
     for _ in range(args.warmup):
         skv.skv_merge_lse(Op, Lp, Om, Lm)
     torch.cuda.synchronize()
@@ -191,6 +203,11 @@ def bench_merge64(args):
         "merge_gbs": merge_bytes / (merge_ms * 1e-3) / 1e9,
         "merge_frac_of_hbm_peak": merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "lpt": {"shard_imbalance_64": float(load.max() / load.mean() - 1)},
+        "simulated_cp_step": {
+            "ranks": w.n_shards,
+            "lpt_max_ms": float(t_lpt.max()), "lpt_mean_ms": float(t_lpt.mean()),
+            "contiguous_max_ms": float(t_cont.max()), "contiguous_mean_ms": float(t_cont.mean()),
+            "step_gain_from_balancing": float(t_cont.max() / t_lpt.max())},
         "roofline": {"bound": "hbm", "achieved": merge_bytes / (merge_ms * 1e-3) / 1e9,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
