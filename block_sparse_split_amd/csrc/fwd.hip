@@ -53,14 +53,16 @@ struct FwdCfg {
   static constexpr int kStageBytes = 2 * kTileBytes;       // K then V
   static constexpr int kStages = 4;
   static constexpr int kLdsBytes = kStages * kStageBytes;
-  static constexpr int kDmaPerWave = 2 * ITile<D>::kBlocks / kWaves;
+  // group B (waves 4-7) issues all tile DMA, in its softmax half steps, so
+  // the issue latency stays off the MFMA group's path
+  static constexpr int kDmaPerWave = 2 * ITile<D>::kBlocks / 4;
   // LDS operand reads kept in flight ahead of the MFMAs (K: one read per
   // fragment, V: two transposed reads per fragment)
   static constexpr int kPrefetchK = 6;
   static constexpr int kPrefetchV = 4;
 };
 
-// Issue this wave's share of the DMA for one step into `stage` (LDS bytes):
+// Issue this group-B wave's share of the DMA for one step into `stage`:
 // K blocks, then V blocks, both interleaved row tiles.  Rows past the end of
 // a ragged step repeat the last valid row (their keys are masked, the values
 // stay finite).
@@ -72,7 +74,7 @@ __device__ __forceinline__ void issue_step(const __bf16* Kg, const __bf16* Vg, c
   constexpr int B = ITile<D>::kBlocks;
 #pragma unroll
   for (int i = 0; i < C::kDmaPerWave; ++i) {
-    const int u = wave * C::kDmaPerWave + i;
+    const int u = (wave - 4) * C::kDmaPerWave + i;
     const bool isv = u >= B;
     const int g = isv ? u - B : u;
     int row, col;
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
     wait_vmcnt<0>();
 #pragma unroll
     for (int s = 0; s < C::kStages; ++s)
-      if (s < n_steps) issue(s);
+      if (s < n_steps && !groupA) issue(s);
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -165,12 +167,13 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
     bf16x8 pf[2][2];
     bool p_act = false;
 
-    // Barrier of half step k, with the ring bookkeeping of odd half steps:
-    // before it, wait for this wave's share of tile (k+1)/2 (at most the
-    // following tile's loads may still be in flight); after it, re-fill the
-    // stage that tile (k-3)/2 has left with tile (k-3)/2 + kStages.
+    // Barrier of half step k, with the ring bookkeeping of odd half steps
+    // (group B is then in its softmax half): before it, a group-B wave waits
+    // for its share of tile (k+1)/2 (at most the following tile's loads may
+    // still be in flight); after it, group B re-fills the stage that tile
+    // (k-3)/2 has left with tile (k-3)/2 + kStages.
     auto half_step = [&](int k) {
-      if ((k & 1) != 0) {
+      if ((k & 1) != 0 && !groupA) {
         const int sn = (k + 1) / 2;
         if (sn < n_steps) {
           if (sn + 1 < n_steps) wait_vmcnt<C::kDmaPerWave>();
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
         }
       }
       block_barrier();
-      if ((k & 1) != 0 && k >= 3) {
+      if ((k & 1) != 0 && k >= 3 && !groupA) {
         const int sj = (k - 3) / 2 + C::kStages;
         if (sj < n_steps) issue(sj);
       }
