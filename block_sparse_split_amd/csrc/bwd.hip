@@ -35,13 +35,14 @@ namespace {
 
 // ---------------------------------------------------------------- pre
 // Row r (token, q-head h) of a kv head g = h / G has per-head index
-// rho = token * G + h % G.  Writes, at [g * Nq * G + rho]: D, LSE * log2(e)
-// (+inf for a row that sees no key) and the row's visible context interval
+// rho = token * G + h % G.  Writes, at [g * Nq * G + rho]: -D (the dP
+// accumulators start from it, so they end as dP - D), LSE * log2(e) (+inf
+// for a row that sees no key) and the row's visible context interval
 // [lo, anchor) of its anchor block.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const int32_t* sched, const __bf16* O,
                                                       const __bf16* dO, const float* LSE,
-                                                      float* Drm, float* L2rm, int32_t* LOrm,
+                                                      float* nDrm, float* L2rm, int32_t* LOrm,
                                                       int32_t* HIrm, int64_t rows, int hq, int G) {
   constexpr int TPR = D / 8;
   constexpr int RPB = 256 / TPR;
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const int32_t* sched, cons
     if (gt < (int64_t)hkv * kStatPad) {
       const int64_t idx = (gt / kStatPad) * (rows / hq * G + kStatPad) + rows / hq * G +
                           gt % kStatPad;
-      Drm[idx] = 0.f;
+      nDrm[idx] = 0.f;
       L2rm[idx] = __builtin_inff();
       LOrm[idx] = 0;
       HIrm[idx] = 0;
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const int32_t* sched, cons
     const int64_t idx = (int64_t)(h / G) * (nqG + kStatPad) + token * G + h % G;
     const float L = LSE[row];
     const int blk = (int)(token / kBlock);
-    Drm[idx] = s;
+    nDrm[idx] = -s;
     L2rm[idx] = L == kNegInf ? __builtin_inff() : L * kLog2e;
     LOrm[idx] = sched[sched[H_OFF_LO] + blk];
     HIrm[idx] = sched[sched[H_OFF_ANCHORS] + blk];
@@ -179,12 +180,16 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
     }
     const int64_t srow = (int64_t)head * (rows_per_head + kStatPad) + rho;
     const float lse2 = valid ? a.ws_L2[srow] : __builtin_inff();
-    const float Dq = valid ? a.ws_D[srow] : 0.f;
+    const float nDq = valid ? a.ws_nD[srow] : 0.f;
     // settle the per-row loads while no tile DMA is in flight, so that no
     // wait for them lands inside the step loop (vmcnt also counts the DMA)
     wait_vmcnt<0>();
     if (n_steps > 0) issue(0);
     if (n_steps > 1) issue(1);
+    // initial dP^T accumulator: every element of a lane is in the lane's row
+    f32x16 negd;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negd[r] = nDq;
     f32x16 dq[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -215,9 +220,9 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
       for (int kb = 0; kb < 2; ++kb) {
         // one 32-key block at a time keeps S, dP of a single block live
         __builtin_amdgcn_sched_barrier(0);
-        f32x16 sacc, dp;
+        f32x16 sacc, dp = negd;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = dp[r] = 0.f;
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
         // MFMA i: d-step t = i / 2; even i: S^T (K), odd i: dP^T (V)
         lds_pipelined<2 * (D / 16), C::kPrefetchNat>(
             [&](int i) {
@@ -230,13 +235,20 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
               else
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, df[i / 2], dp, 0, 0, 0);
             });
+        // a wave-uniform branch: tiles every row sees whole take no mask
+        if (full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // key 32 kb + 8 (r / 4) + 4 h32 + r % 4 against bounds shifted by 4 h32
-          const int kc = 32 * kb + 8 * (r >> 2) + (r & 3);
-          float p = exp2_fast(fmaf(sacc[r], c, -lse2));
-          if (!full && (kc < klo4 || kc >= khi4)) p = 0.f;
-          ds[kb][r >> 3][r & 7] = f32_to_bf16(p * (dp[r] - Dq));
+          for (int r = 0; r < 16; ++r)
+            ds[kb][r >> 3][r & 7] = f32_to_bf16(exp2_fast(fmaf(sacc[r], c, -lse2)) * dp[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            // key 32 kb + 8 (r / 4) + 4 h32 + r % 4 against bounds shifted by 4 h32
+            const int kc = 32 * kb + 8 * (r >> 2) + (r & 3);
+            float p = exp2_fast(fmaf(sacc[r], c, -lse2));
+            if (kc < klo4 || kc >= khi4) p = 0.f;
+            ds[kb][r >> 3][r & 7] = f32_to_bf16(p * dp[r]);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -312,7 +324,7 @@ struct KvCfg {
   static constexpr int kWaves = 8;
   static constexpr int kThreads = kWaves * 64;
   // Q, dO (interleaved row tiles), then 1 KB of row statistics:
-  // D [0, 256), L2 [256, 512), lo [512, 768), anchor [768, 1024)
+  // -D [0, 256), L2 [256, 512), lo [512, 768), anchor [768, 1024)
   static constexpr int kOOff = ITile<D>::kBytes;
   static constexpr int kStatOff = 2 * ITile<D>::kBytes;
   static constexpr int kStageBytes = kStatOff + 1024;
@@ -405,7 +417,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
         // 16 lanes per statistic (D, L2, lo, anchor: consecutive arrays of
         // stat_words each), 4 rows per lane; a tile ends at most 63 rows
         // past the head's rows, inside its padding
-        dma16(reinterpret_cast<const int32_t*>(a.ws_D) + (int64_t)(lane >> 4) * a.stat_words +
+        dma16(reinterpret_cast<const int32_t*>(a.ws_nD) + (int64_t)(lane >> 4) * a.stat_words +
                   (int64_t)head * (rows_per_head + kStatPad) + rho0 + 4 * (lane & 15),
               stage + C::kStatOff);
       }
@@ -543,10 +555,17 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
         const uint32_t stat = stage + C::kStatOff;
         f32x16 dp[2];
         if (any) {
+          // the accumulators start from -D of their rows, so they end as
+          // dP - D
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dp[qb][r] = 0.f;
+            for (int j = 0; j < 4; ++j) {
+              // rows 8 j + 4 h32 + 0..3 of query block qb
+              const f32x4 nd = lds_read_f4(stat + 4 * (qb * 32 + 8 * j + 4 * h32));
+#pragma unroll
+              for (int i = 0; i < 4; ++i) dp[qb][4 * j + i] = nd[i];
+            }
           const uint32_t ofb = opaque(stage + noff + C::kOOff);
           lds_pipelined<2 * (D / 16), C::kPrefetchNat>(
               [&](int i) { return itile_nat<D>(ofb, i % 2, i / 2); },
@@ -564,16 +583,8 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
             for (int t2 = 0; t2 < 2; ++t2) {
               const bf16x8 pr = lds_read16(xslot + (2 * qb + t2) * 1024);
 #pragma unroll
-              for (int jj = 0; jj < 2; ++jj) {
-                // rows 8 (2 t2 + jj) + 4 h32 + 0..3 of query block qb
-                const f32x4 dd = lds_read_f4(stat + 4 * (qb * 32 + 8 * (2 * t2 + jj) + 4 * h32));
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int e = 4 * jj + i;
-                  const int r = 8 * t2 + e;
-                  dsb[qb][t2][e] = f32_to_bf16(static_cast<float>(pr[e]) * (dp[qb][r] - dd[i]));
-                }
-              }
+              for (int e = 0; e < 8; ++e)
+                dsb[qb][t2][e] = f32_to_bf16(static_cast<float>(pr[e]) * dp[qb][8 * t2 + e]);
             }
           const uint32_t qtb = opaque(stage + troff);
           lds_pipelined<4 * NDB, C::kPrefetchTr>(
@@ -624,7 +635,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   constexpr int RPB = 256 / (D / 8);
   SKV_LAUNCH("bwd_pre", bwd_pre_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256), 0, s,
              a.sched, static_cast<const __bf16*>(a.O), static_cast<const __bf16*>(a.dO), a.LSE,
-             a.ws_D, a.ws_L2, a.ws_LO, a.ws_HI, rows, a.hq, a.hq / a.hkv);
+             a.ws_nD, a.ws_L2, a.ws_LO, a.ws_HI, rows, a.hq, a.hq / a.hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_kernel<D>),

@@ -725,7 +725,7 @@ skv_status skv_attn_bwd(const skv_problem* p, const skv_schedule_info* info,
     a.with_draft = p->with_draft;
     const int64_t stat_bytes = align_up(
         int64_t(p->hkv) * (int64_t(p->nb) * 16 * (p->hq / p->hkv) + skv::kStatPad) * 4, 256);
-    a.ws_D = static_cast<float*>(workspace);
+    a.ws_nD = static_cast<float*>(workspace);
     a.ws_L2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + stat_bytes);
     a.ws_LO = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 2 * stat_bytes);
     a.ws_HI = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 3 * stat_bytes);

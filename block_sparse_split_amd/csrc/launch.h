@@ -37,13 +37,13 @@ struct BwdArgs {
   void* dV;
   void* dKd;                // [Nq, hkv, d]
   void* dVd;
-  float* ws_D;              // rowsum(dO * O), [hkv][Nq * G + kStatPad] in query-tile row
+  float* ws_nD;             // -rowsum(dO * O), [hkv][Nq * G + kStatPad] in query-tile row
                             //   order; padding rows see no key
   float* ws_L2;             // LSE * log2(e) (+inf: no key), same layout
   int32_t* ws_LO;           // first / end context key each row may see (its
   int32_t* ws_HI;           //   anchor block's lo and anchor), same layout
   float* ws_dQ;             // partial slots [n_slots, 256, d]
-  int64_t stat_words;       // distance between the D, L2, LO and HI arrays
+  int64_t stat_words;       // distance between the -D, L2, LO and HI arrays
   int32_t grad_bf16, dtype_bf16;
   int32_t hq, hkv, d, nb, n_local;
   int32_t n_wg, n_split, n_slots, with_draft;
