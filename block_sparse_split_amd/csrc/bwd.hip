@@ -103,21 +103,27 @@ struct DqCfg {
   static constexpr int kPrefetchTr = 4;
 };
 
+// This wave's share of one step's DMA: waves 0-3 copy the K blocks of the
+// interleaved row tile, waves 4-7 the V blocks.  The step's first key row is
+// in the buffer base, block g adds a scalar offset and `lane_off` is the
+// lane's row (lane % kRB) and 16-byte column.  Rows past the end of a ragged
+// step read the keys that follow it (masked), or zeros past the tensor's end.
 template <int D>
-__device__ __forceinline__ void dq_issue(const __bf16* Kg, const __bf16* Vg, const Step& st,
-                                         int head, int hkv, uint32_t stage, int wave, int lane) {
+__device__ __forceinline__ void dq_issue(const __bf16* Kg, const __bf16* Vg, int64_t kv_rows,
+                                         const Step& st, int head, int hkv, uint32_t stage,
+                                         int wave, uint32_t lane_off) {
   using C = DqCfg<D>;
-  constexpr int B = ITile<D>::kBlocks;
+  using T = ITile<D>;
+  const bool isv = wave >= 4;
+  const int64_t row_bytes = (int64_t)hkv * D * 2;
+  const int64_t off = st.row * row_bytes + (int64_t)head * D * 2;
+  const i32x4 res = buf_res(reinterpret_cast<const char*>(isv ? Vg : Kg) + off,
+                            kv_rows * row_bytes - off);
 #pragma unroll
   for (int i = 0; i < C::kDmaPerWave; ++i) {
-    const int u = wave * C::kDmaPerWave + i;
-    const bool isv = u >= B;
-    const int g = isv ? u - B : u;
-    int row, col;
-    itile_rc<D>(g, lane, row, col);
-    const int grow = min(row, st.n - 1);
-    dma16((isv ? Vg : Kg) + ((int64_t)(st.row + grow) * hkv + head) * D + col,
-          stage + (isv ? C::kVOff : 0) + g * ITile<D>::kBlockStride);
+    const int g = (wave & 3) * C::kDmaPerWave + i;
+    dma16_buf(res, lane_off, (uint32_t)(g * T::kRB * row_bytes),
+              stage + (isv ? C::kVOff : 0) + g * T::kBlockStride);
   }
 }
 
@@ -144,6 +150,10 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
   const uint32_t knoff = itile_nat_offset<D>(lane);
   const uint32_t voff = C::kVOff + itile_nat_offset<D>(lane);
   const uint32_t troff = itile_tr_offset<D>(lane);
+  // per-lane byte offset of this lane's DMA source inside a K/V block
+  int drow, dcol;
+  itile_rc<D>(0, lane, drow, dcol);
+  const uint32_t dma_off = (uint32_t)((drow * hkv * D + dcol) * 2);
 
   for (int qi = qbeg; qi < qend; ++qi) {
     const sched_t it = items + queue[qi] * I_WORDS;
@@ -166,7 +176,8 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
       const Step st = item_step(tiles, s, n_draft, t0, sp);
       const __bf16* Kg = static_cast<const __bf16*>(st.draft ? a.Kd : a.K);
       const __bf16* Vg = static_cast<const __bf16*>(st.draft ? a.Vd : a.V);
-      dq_issue<D>(Kg, Vg, st, head, hkv, lds0 + (s % C::kStages) * C::kStageBytes, wave, lane);
+      dq_issue<D>(Kg, Vg, st.draft ? nq : a.n_local, st, head, hkv,
+                  lds0 + (s % C::kStages) * C::kStageBytes, wave, dma_off);
     };
     bf16x8 qf[D / 16], df[D / 16];
 #pragma unroll
@@ -370,6 +381,15 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
   const uint32_t noff = itile_nat_offset<D>(lane);
   const uint32_t troff = itile_tr_offset<D>(lane);
   const uint32_t xslot = lds0 + C::kXOff + pair * 4096 + 16 * lane;
+  // byte offset of row r of a query tile from the tile's first row (tiles
+  // start at a multiple of G rows: r / G tokens on, head r % G)
+  auto qrow_bytes = [&](int r) { return (uint32_t)((((r >> lgG) * hq) + (r & (G - 1))) * D * 2); };
+  const int64_t q_bytes = (int64_t)nb * kBlock * hq * D * 2;
+  int drow, dcol;
+  itile_rc<D>(0, lane, drow, dcol);
+  const uint32_t dma_off = qrow_bytes(drow) + 2 * dcol;
+  const i32x4 stat_res = buf_res(a.ws_nD, 16 * a.stat_words);
+  const uint32_t stat_off = (uint32_t)(((lane >> 4) * a.stat_words + 4 * (lane & 15)) * 4);
 
   for (int qi = qbeg; qi < qend; ++qi) {
     const sched_t it = kvs + queue[qi] * K_WORDS;
@@ -396,30 +416,32 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
     const int n_rt = (r_end - r_begin + kTileK - 1) / kTileK;
 
     auto stage_of = [&](int rt) { return lds0 + (rt % C::kStages) * C::kStageBytes; };
-    // P waves only: this wave's share of tile rt (Q and dO fragments; wave 0
-    // also the row statistics)
+    // P waves only: this wave's share of tile rt -- waves 0, 1 the Q blocks,
+    // waves 2, 3 the dO blocks (wave 0 also the row statistics).  The tile's
+    // first row is in the buffer base, block g adds the scalar qrow_bytes(g
+    // kRB) and `dma_off` is the lane's row and column.  Rows past r_end read
+    // the rows that follow (their statistics mask them), or zeros past the
+    // tensor's end.
     auto issue = [&](int rt) {
       const uint32_t stage = stage_of(rt);
       const int rho0 = r_begin + kTileK * rt;
+      const bool iso = wave >= 2;
+      const int64_t off = ((int64_t)(rho0 >> lgG) * hq + head * G) * D * 2;
+      const i32x4 res =
+          buf_res(reinterpret_cast<const char*>(iso ? dOg : Qg) + off, q_bytes - off);
 #pragma unroll
       for (int i = 0; i < C::kDmaPerWave; ++i) {
-        const int u = wave * C::kDmaPerWave + i;
-        const bool iso = u >= ITile<D>::kBlocks;  // dO after Q
-        const int g = iso ? u - ITile<D>::kBlocks : u;
-        int row, col;
-        itile_rc<D>(g, lane, row, col);
-        const int rho = min(rho0 + row, r_end - 1);
-        const int64_t grow = (int64_t)(rho >> lgG) * hq + head * G + (rho & (G - 1));
-        dma16((iso ? dOg : Qg) + grow * D + col,
-              stage + (iso ? C::kOOff : 0) + g * ITile<D>::kBlockStride);
+        const int g = (wave & 1) * C::kDmaPerWave + i;
+        dma16_buf(res, dma_off, qrow_bytes(g * ITile<D>::kRB),
+                  stage + (iso ? C::kOOff : 0) + g * ITile<D>::kBlockStride);
       }
       if (wave == 0) {
-        // 16 lanes per statistic (D, L2, lo, anchor: consecutive arrays of
+        // 16 lanes per statistic (-D, L2, lo, anchor: consecutive arrays of
         // stat_words each), 4 rows per lane; a tile ends at most 63 rows
         // past the head's rows, inside its padding
-        dma16(reinterpret_cast<const int32_t*>(a.ws_nD) + (int64_t)(lane >> 4) * a.stat_words +
-                  (int64_t)head * (rows_per_head + kStatPad) + rho0 + 4 * (lane & 15),
-              stage + C::kStatOff);
+        dma16_buf(stat_res, stat_off,
+                  (uint32_t)(((int64_t)head * (rows_per_head + kStatPad) + rho0) * 4),
+                  stage + C::kStatOff);
       }
     };
     // this wave's stationary B operand: K (P wave) or V (dS wave) of its keys

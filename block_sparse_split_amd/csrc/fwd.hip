@@ -41,7 +41,7 @@ constexpr int kKB = kTileK / 32;   // 32-key blocks per step
 // ---------------------------------------------------------------------------
 // bf16 path.  Eight waves (two per SIMD) each own 32 query rows of the
 // 256-row tile.  K and V tiles reach LDS by direct global->LDS DMA
-// (global_load_lds_dwordx4, whole rows per instruction) into a 4-stage ring
+// (buffer_load_dwordx4 ... lds, whole rows per instruction) into a 4-stage ring
 // of interleaved row tiles, so loads run two steps ahead and no registers
 // hold staged data; K is read as natural MFMA operands, V as transposed ones,
 // each one base register plus an immediate offset, without bank conflicts.
@@ -63,25 +63,28 @@ struct FwdCfg {
 };
 
 // Issue this group-B wave's share of the DMA for one step into `stage`:
-// K blocks, then V blocks, both interleaved row tiles.  Rows past the end of
-// a ragged step repeat the last valid row (their keys are masked, the values
-// stay finite).
+// waves 4, 5 copy the K blocks of the interleaved row tile, waves 6, 7 the V
+// blocks.  Block g holds key rows g kRB .. g kRB + kRB - 1 of the step, so a
+// lane's address is the step's first row (in the buffer base), a per-block
+// scalar offset and a per-lane offset `lane_off` (row lane % kRB, its 16-byte
+// column).  Rows past the end of a ragged step read the keys that follow it
+// (masked), or zeros past the end of the tensor.
 template <int D>
-__device__ __forceinline__ void issue_step(const __bf16* Kg, const __bf16* Vg, const Step& st,
-                                           int head, int hkv, uint32_t stage, int wave,
-                                           int lane) {
+__device__ __forceinline__ void issue_step(const __bf16* Kg, const __bf16* Vg, int64_t kv_rows,
+                                           const Step& st, int head, int hkv, uint32_t stage,
+                                           int wave, uint32_t lane_off) {
   using C = FwdCfg<D>;
-  constexpr int B = ITile<D>::kBlocks;
+  using T = ITile<D>;
+  const bool isv = wave >= 6;
+  const int64_t row_bytes = (int64_t)hkv * D * 2;
+  const int64_t off = st.row * row_bytes + (int64_t)head * D * 2;
+  const i32x4 res = buf_res(reinterpret_cast<const char*>(isv ? Vg : Kg) + off,
+                            kv_rows * row_bytes - off);
 #pragma unroll
   for (int i = 0; i < C::kDmaPerWave; ++i) {
-    const int u = (wave - 4) * C::kDmaPerWave + i;
-    const bool isv = u >= B;
-    const int g = isv ? u - B : u;
-    int row, col;
-    itile_rc<D>(g, lane, row, col);
-    const int grow = min(row, st.n - 1);
-    dma16((isv ? Vg : Kg) + ((int64_t)(st.row + grow) * hkv + head) * D + col,
-          stage + (isv ? C::kTileBytes : 0) + g * ITile<D>::kBlockStride);
+    const int g = (wave & 1) * C::kDmaPerWave + i;
+    dma16_buf(res, lane_off, (uint32_t)(g * T::kRB * row_bytes),
+              stage + (isv ? C::kTileBytes : 0) + g * T::kBlockStride);
   }
 }
 
@@ -119,6 +122,10 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
   // transposed V read
   const uint32_t koff = itile_nat_offset<D>(lane);
   const uint32_t voff = C::kTileBytes + itile_tr_offset<D>(lane);
+  // per-lane byte offset of this lane's DMA source inside a K/V block
+  int drow, dcol;
+  itile_rc<D>(0, lane, drow, dcol);
+  const uint32_t dma_off = (uint32_t)((drow * hkv * D + dcol) * 2);
 
   for (int qi = qbeg; qi < qend; ++qi) {
     const sched_t it = items + queue[qi] * I_WORDS;
@@ -142,7 +149,8 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
       const Step st = item_step(tiles, s, n_draft, t0, sp);
       const __bf16* Kg = static_cast<const __bf16*>(st.draft ? a.Kd : a.K);
       const __bf16* Vg = static_cast<const __bf16*>(st.draft ? a.Vd : a.V);
-      issue_step<D>(Kg, Vg, st, head, hkv, stage_of(s), wave, lane);
+      issue_step<D>(Kg, Vg, st.draft ? nq : a.n_local, st, head, hkv, stage_of(s), wave,
+                    dma_off);
     };
     bf16x8 qf[D / 16];
 #pragma unroll

@@ -656,6 +656,7 @@ skv_status skv_attn_fwd_partial(const skv_problem* p, const skv_schedule_info* i
     a.o_bf16 = o_dtype == SKV_BF16;
     a.dtype_bf16 = p->dtype == SKV_BF16;
     a.hq = p->hq; a.hkv = p->hkv; a.d = p->d; a.nb = p->nb;
+    a.n_local = info->n_local;
     a.scale = p->scale;
     a.n_wg = info->n_workgroups;
     a.n_split = info->n_split_qtiles;

@@ -17,7 +17,7 @@ struct FwdArgs {
   float* ws_O;              // partial slots [n_slots, 256, d] fp32
   float* ws_LSE;            // [n_slots, 256]
   int32_t o_bf16, dtype_bf16;
-  int32_t hq, hkv, d, nb;
+  int32_t hq, hkv, d, nb, n_local;
   int32_t n_wg, n_split, n_slots;
   float scale;
 };

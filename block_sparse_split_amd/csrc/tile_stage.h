@@ -1,16 +1,15 @@
 // Direct-to-LDS tile staging and LDS operand reads (gfx950 kernels).
 //
 // Tiles of 64 rows x D bf16 (rows are keys or query rows) are copied from
-// HBM into LDS with global_load_lds_dwordx4: every lane of a wave moves 16
-// bytes and writes them at lds_base + 16 * lane, choosing its own global
-// address.  All tiles use one layout (the interleaved row tile below): each
-// DMA instruction moves whole rows, and MFMA operands are read either
-// naturally (lane = row, ds_read_b128) or transposed (lane = column,
-// ds_read_b64_tr_b16) without bank conflicts and without any register
-// transpose.  Reads use one base register plus an immediate offset.  The
-// DMA is issued as inline asm so the compiler neither waits on it nor
-// serialises it against LDS reads; kernels wait with explicit vmcnt counts
-// and a bare s_barrier.
+// HBM into LDS with buffer_load_dwordx4 ... lds: every lane of a wave moves
+// 16 bytes and writes them at lds_base + 16 * lane.  All tiles use one
+// layout (the interleaved row tile below): each DMA instruction moves whole
+// rows, and MFMA operands are read either naturally (lane = row,
+// ds_read_b128) or transposed (lane = column, ds_read_b64_tr_b16) without
+// bank conflicts and without any register transpose.  Reads use one base
+// register plus an immediate offset.  The DMA is issued as inline asm so the
+// compiler neither waits on it nor serialises it against LDS reads; kernels
+// wait with explicit vmcnt counts and a bare s_barrier.
 #pragma once
 #include "device_common.h"
 
@@ -18,13 +17,37 @@ namespace skv {
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over the bytes [base, base + bytes) of global memory
+// (bytes above 2^32 - 1 are clamped).  A buffer load's range check covers
+// voffset + soffset: a lane whose offset lands at or past `bytes` reads no
+// memory and its 16 LDS bytes become zero.  base and bytes must be
+// wave-uniform.
+__device__ __forceinline__ i32x4 buf_res(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  // 32-bit halves the optimiser cannot fuse back into a 64-bit compare keep
+  // the clamp on the scalar unit
+  uint32_t lo = (uint32_t)bytes, hi = (uint32_t)((uint64_t)bytes >> 32);
+  asm volatile("" : "+s"(lo), "+s"(hi));
+  const uint32_t n = (int32_t)hi < 0 ? 0u : hi != 0 ? 0xFFFFFFFFu : lo;
+  // word 1: base[47:32], stride 0; word 3: 32-bit data format, no swizzle
+  i32x4 r = {(int32_t)(uint32_t)b, (int32_t)((b >> 32) & 0xFFFFu), (int32_t)n, 0x00020000};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
+  return r;
+}
+
+// 16 bytes per lane from buffer `res` at byte offset voff + soff into LDS at
+// lds_base + 16 * lane (buffer_load_dwordx4 ... lds).  The per-lane part of
+// the address is one 32-bit register and the rest is scalar, so issuing
+// costs no vector ALU work.  soff and lds_base must be wave-uniform.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane;
-// lds_base must be wave-uniform.
-__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gsrc), "s"(lds_base) : "memory", "m0");
+__device__ __forceinline__ void dma16_buf(const i32x4& res, uint32_t voff, uint32_t soff,
+                                          uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(res), "s"(soff), "s"(lds_base) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -66,7 +89,6 @@ __device__ __forceinline__ int32_t lds_read_i32(uint32_t addr) {
       static_cast<uintptr_t>(addr));
 }
 
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 lds_read_i4(uint32_t addr) {
   return *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
       static_cast<uintptr_t>(addr));
