@@ -199,24 +199,51 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
     // idle half step and skips the (empty) last one, so both groups pass the
     // same 2 n + 2 barriers.
     const int k0 = groupA ? -1 : 0;
-    // O^T += V^T P^T for the tile in `stage` (P from the last softmax)
+    constexpr int NDB = D / 32;
+    constexpr int NMF = D / 8;  // MFMAs of PV, and of QK
+    // PV MFMA i: O^T += V^T P^T (P from the last softmax) for key block kb,
+    // k-half t2, output block db
+    auto pv_read = [&](uint32_t vbase, int i) {
+      return itile_tr<D>(vbase, i % NDB, i / (2 * NDB), (i / NDB) % 2);
+    };
+    auto pv_mfma = [&](int i, const bf16x8& v) {
+      o[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pf[i / (2 * NDB)][(i / NDB) % 2],
+                                                           o[i % NDB], 0, 0, 0);
+    };
     auto pv = [&](int s) {
       const uint32_t vbase = opaque(stage_of(s) + voff);
-      constexpr int NDB = D / 32;
-      // MFMA i: key block kb, k-half t2, output block db
-      lds_pipelined<4 * NDB, C::kPrefetchV>(
-          [&](int i) { return itile_tr<D>(vbase, i % NDB, i / (2 * NDB), (i / NDB) % 2); },
-          [&](int i, const bf16x8& v) {
-            o[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                v, pf[i / (2 * NDB)][(i / NDB) % 2], o[i % NDB], 0, 0, 0);
-          });
+      lds_pipelined<NMF, C::kPrefetchV>([&](int i) { return pv_read(vbase, i); }, pv_mfma);
     };
     if (!groupA) half_step(-1);
     for (int p = 0; p < n_steps; ++p) {
       half_step(2 * p + k0);
-      if (p_act) pv(p - 1);
-      __builtin_amdgcn_sched_barrier(0);
-      // QK of step p
+      // PV of step p-1, then QK of step p, in one operand pipeline (the
+      // first QK operands load during the last PV MFMAs).  QK runs even for
+      // a step no row sees; its softmax is skipped.
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      const uint32_t kbase = opaque(stage_of(p) + koff);
+      // QK MFMA i: d-step t = i / 2, key block kb = i % 2
+      auto qk_read = [&](int i) { return itile_nat<D>(kbase, i % 2, i / 2); };
+      auto qk_mfma = [&](int i, const bf16x8& k) {
+        sacc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[i / 2], sacc[i % 2], 0, 0, 0);
+      };
+      if (p_act) {
+        const uint32_t vbase = opaque(stage_of(p - 1) + voff);
+        lds_pipelined<2 * NMF, C::kPrefetchK>(
+            [&](int i) { return i < NMF ? pv_read(vbase, i) : qk_read(i - NMF); },
+            [&](int i, const bf16x8& x) {
+              if (i < NMF) pv_mfma(i, x);
+              else qk_mfma(i - NMF, x);
+            });
+      } else {
+        lds_pipelined<NMF, C::kPrefetchK>(qk_read, qk_mfma);
+      }
+      half_step(2 * p + k0 + 1);
+      // softmax of step p
       const Step st = item_step(tiles, p, n_draft, t0, sp);
       int klo = 0, khi = kTileK;
       bool lane_any = false, lane_full = true;
@@ -227,23 +254,6 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
       }
       const bool s_act = __any(lane_any);
       const bool s_full = __all(lane_full);
-      f32x16 sacc[2];
-      if (s_act) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-        const uint32_t kbase = opaque(stage_of(p) + koff);
-        // MFMA i: d-step t = i / 2, key block kb = i % 2
-        lds_pipelined<2 * (D / 16), C::kPrefetchK>(
-            [&](int i) { return itile_nat<D>(kbase, i % 2, i / 2); },
-            [&](int i, const bf16x8& k) {
-              sacc[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[i / 2], sacc[i % 2], 0,
-                                                                    0, 0);
-            });
-      }
-      half_step(2 * p + k0 + 1);
-      // softmax of step p
       p_act = s_act;
       if (s_act) {
         if (!s_full) {
