@@ -10,7 +10,7 @@ sources.
 
 Usage:
   python -m block_sparse_split_amd.rocprof_summary kernels STATS_CSV \\
-      --command "..." [--out FILE]
+      --command "..." [--trace TRACE_CSV --skip-first N --bench-json OUT] [--out FILE]
   python -m block_sparse_split_amd.rocprof_summary traffic KERNEL \\
       --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV \\
       --copy-bytes N --workload NAME --command "..." [--out FILE]
@@ -18,6 +18,7 @@ Usage:
 import argparse
 import csv
 import hashlib
+import json
 import os
 import sys
 from collections import defaultdict
@@ -67,13 +68,36 @@ def counter_per_dispatch(path, counter, match):
 def cmd_kernels(a):
     rows = list(csv.DictReader(open(a.stats)))
     total = sum(float(r["TotalDurationNs"]) for r in rows)
-    out = [f"# rocprofv3 kernel statistics", f"command: {a.command}", "",
+    out = [f"# rocprofv3 kernel statistics", f"command: {a.command}",
+           f"kernel_source_sha256: {kernel_source_hash()}", "",
+           "all dispatches:",
            f"{'kernel':<14} {'calls':>6} {'avg_ms':>9} {'min_ms':>9} {'max_ms':>9} {'share':>7}"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         name = short_name(r["Name"]) or ("torch_elementwise" if "at::native" in r["Name"] else r["Name"][:40])
         out.append(f"{name:<14} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e6:>9.4f} "
                    f"{float(r['MinNs']) / 1e6:>9.4f} {float(r['MaxNs']) / 1e6:>9.4f} "
                    f"{100 * float(r['TotalDurationNs']) / total:>6.2f}%")
+    if a.trace:
+        # per-dispatch durations without the warm-up launches, beside the
+        # bench's own HIP-event averages from the same run
+        per = defaultdict(list)
+        for r in csv.DictReader(open(a.trace)):
+            name = short_name(r["Kernel_Name"])
+            if name:
+                per[name].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        bench = {}
+        if a.bench_json:
+            line = open(a.bench_json).read().strip().splitlines()[-1]
+            bench = {k: v.get("avg_ms") for k, v in json.loads(line).get("kernels", {}).items()}
+        out += ["", f"timed dispatches (first {a.skip_first} of each kernel skipped as warm-up):",
+                f"{'kernel':<14} {'calls':>6} {'avg_ms':>9} {'bench_avg_ms':>13}"]
+        for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            d = d[a.skip_first:]
+            if not d:
+                continue
+            b = bench.get(name)
+            out.append(f"{name:<14} {len(d):>6} {sum(d) / len(d) / 1e6:>9.4f} "
+                       f"{b if b is None else f'{b:.4f}':>13}")
     emit("\n".join(out) + "\n", a.out)
 
 
@@ -121,6 +145,9 @@ def main(argv=None):
     k = sub.add_parser("kernels")
     k.add_argument("stats")
     k.add_argument("--command", required=True)
+    k.add_argument("--trace", help="kernel trace CSV of the same run")
+    k.add_argument("--skip-first", type=int, default=0)
+    k.add_argument("--bench-json", help="bench.py output of the same run")
     k.add_argument("--out")
     t = sub.add_parser("traffic")
     t.add_argument("kernel")
