@@ -215,6 +215,18 @@ struct Item {
   int64_t cost;
 };
 
+// Cost of GPU work items in time units, fitted to per-workgroup times
+// measured on MI355X (least squares over the 256 workgroups of the 32K
+// workload, 1 % rms).  A forward / dQ item pays a fixed part (loading the
+// query tile, filling and draining the tile ring, writing the output) of
+// about 5.5 key steps, and every key step costs the same whether one or all
+// of the tile's anchor blocks see it.  A dK/dV item pays about 2.6 row
+// tiles, then one unit per 64-row tile of its block range.
+constexpr int64_t kStepCost = 8;
+constexpr int64_t kItemCost = 44;
+constexpr int64_t kKvRowCost = 5;
+constexpr int64_t kKvItemCost = 13;
+
 struct KvItem {
   int32_t head, t0, nt, dtok0, ndraft, b0, b1;
   int64_t cost;
@@ -268,39 +280,35 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
   const int32_t* L = p->lo;
   const int32_t tok_per_qt = skv::kQTile / g.G;
 
-  // Visible (anchor block, tile) pairs per query tile and tile.
+  // Tiles that some anchor block of the query tile sees, per query tile.
   std::vector<Item> items;
   std::vector<std::vector<int32_t>> qt_vis(g.qt_per_head);
-  std::vector<std::vector<int64_t>> qt_cost(g.qt_per_head);
-  int64_t total = 0;
   for (int32_t qt = 0; qt < g.qt_per_head; ++qt) {
     const int32_t b0 = qt * tok_per_qt / skv::kBlock;
     const int32_t b1 = std::min(g.nb, ((qt + 1) * tok_per_qt + skv::kBlock - 1) / skv::kBlock);
     for (int32_t t = 0; t < nt; ++t) {
-      int64_t c = 0;
-      for (int32_t b = b0; b < b1; ++b)
-        c += std::max<int64_t>(L[b], tiles[t].pos) <
-             std::min<int64_t>(A[b], int64_t(tiles[t].pos) + tiles[t].len);
-      if (c) {
-        qt_vis[qt].push_back(t);
-        qt_cost[qt].push_back(c);
-        total += c * g.hkv;
-      }
+      bool seen = false;
+      for (int32_t b = b0; b < b1 && !seen; ++b)
+        seen = std::max<int64_t>(L[b], tiles[t].pos) <
+               std::min<int64_t>(A[b], int64_t(tiles[t].pos) + tiles[t].len);
+      if (seen) qt_vis[qt].push_back(t);
     }
-    if (p->with_draft) total += int64_t(b1 - b0) * g.hkv;
   }
   // Forward / dQ items.  Units are runs of consecutive visible tiles of one
   // (kv head, query tile); the first run of a query tile also carries its
-  // draft keys (one pair per anchor block).  Per XCD class, units are placed
-  // LPT-first (largest remaining cost first, ties: lowest unit, then lowest
-  // bin) on the least-loaded workgroup; a unit that would push that
-  // workgroup past the class's target load T = ceil(class cost / bins) is
-  // cut at a tile boundary: the prefix that fits stays, the rest goes back to
-  // the pending set.  Work units are divisible (their partials merge exactly),
-  // so every bin ends at most one tile above T, with at most one cut per bin.
+  // draft keys.  A piece of a unit costs kItemCost plus kStepCost per key
+  // step.  Per XCD class, units are placed LPT-first (largest remaining cost
+  // first, ties: lowest unit, then lowest bin) on the least-loaded
+  // workgroup; a unit that would push that workgroup past the class's target
+  // load T is cut at a tile boundary: the prefix that fits stays, the rest
+  // (which pays its own kItemCost) goes back to the pending set.  Work units
+  // are divisible (their partials merge exactly), so every bin ends within
+  // one step and one item cost of T, with at most one cut per bin.  T is
+  // ceil(class cost / bins) for a first pass, then raised by the item costs
+  // of the cuts that pass made, and the class is planned again.
   struct Unit {
     int32_t head, qt, k0, k1;  // tiles qt_vis[qt][k0 .. k1-1]
-    int64_t draft_cost;        // cost of the draft step (first run only)
+    int64_t draft_cost;        // cost of the draft steps (first run only)
   };
   std::vector<Unit> units;
   for (int32_t h = 0; h < g.hkv; ++h) {
@@ -308,7 +316,11 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
       const int32_t b0 = qt * tok_per_qt / skv::kBlock;
       const int32_t b1 =
           std::min(g.nb, ((qt + 1) * tok_per_qt + skv::kBlock - 1) / skv::kBlock);
-      const int64_t dcost = p->with_draft ? int64_t(b1 - b0) : 0;
+      // draft keys: the query tile's anchor blocks, in steps of 64
+      const int64_t dcost =
+          p->with_draft ? kStepCost * ((int64_t(b1 - b0) * skv::kBlock + skv::kTileK - 1) /
+                                       skv::kTileK)
+                        : 0;
       const auto& vis = qt_vis[qt];
       if (vis.empty()) {  // still one item: it writes O = 0, LSE = -inf (or the draft part)
         units.push_back({h, qt, 0, 0, dcost});
@@ -329,9 +341,7 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
   std::vector<std::vector<int32_t>> q(n_wg);
   std::vector<int64_t> wg_load(n_wg, 0);
   auto piece_cost = [&](const Unit& u, int32_t k0, int32_t k1) {
-    int64_t c = k0 == u.k0 ? u.draft_cost : 0;
-    for (int32_t k = k0; k < k1; ++k) c += qt_cost[u.qt][k];
-    return c;
+    return kItemCost + (k0 == u.k0 ? u.draft_cost : 0) + kStepCost * (k1 - k0);
   };
   for (int32_t cls = 0; cls < n_cls_fwd; ++cls) {
     // pending pieces: (cost, unit, first tile) -- largest cost first
@@ -344,51 +354,73 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
         return k0 > o.k0;
       }
     };
-    std::priority_queue<Pending> pend;
     int64_t cls_total = 0;
-    for (int32_t ui = 0; ui < int32_t(units.size()); ++ui) {
-      const Unit& u = units[ui];
-      if (u.head % n_cls_fwd != cls) continue;
-      const int64_t c = piece_cost(u, u.k0, u.k1);
-      cls_total += c;
-      pend.push({c, ui, u.k0});
-    }
-    const int64_t target = (cls_total + per_cls - 1) / per_cls;
-    using Bin = std::pair<int64_t, int32_t>;  // (load, bin)
-    std::priority_queue<Bin, std::vector<Bin>, std::greater<Bin>> bins;
-    for (int32_t b = 0; b < per_cls; ++b) bins.push({0, b});
-    while (!pend.empty()) {
-      const Pending pc = pend.top();
-      pend.pop();
-      const Unit& u = units[pc.unit];
-      Bin bin = bins.top();
-      bins.pop();
-      int32_t k_end = u.k1;
-      int64_t placed = pc.cost;
-      if (bin.first + pc.cost > target && u.k1 - pc.k0 > 1) {
-        // cut: the longest prefix that fits (at least one tile)
-        const int64_t room = target - bin.first;
-        int64_t acc = pc.k0 == u.k0 ? u.draft_cost : 0;
-        int32_t k = pc.k0;
-        while (k < u.k1 && acc + qt_cost[u.qt][k] <= room) acc += qt_cost[u.qt][k++];
-        if (k == pc.k0) acc += qt_cost[u.qt][k++];
-        if (k < u.k1) {
-          k_end = k;
-          placed = acc;
-          pend.push({pc.cost - acc, pc.unit, k});
-        }
+    for (int32_t ui = 0; ui < int32_t(units.size()); ++ui)
+      if (units[ui].head % n_cls_fwd == cls)
+        cls_total += piece_cost(units[ui], units[ui].k0, units[ui].k1);
+    // one planning pass at target load T; emit = false only measures it
+    int64_t total_placed = 0;
+    auto plan = [&](int64_t target, bool emit) {
+      std::priority_queue<Pending> pend;
+      for (int32_t ui = 0; ui < int32_t(units.size()); ++ui) {
+        const Unit& u = units[ui];
+        if (u.head % n_cls_fwd == cls) pend.push({piece_cost(u, u.k0, u.k1), ui, u.k0});
       }
-      const auto& vis = qt_vis[u.qt];
-      Item it{u.head, u.qt, u.k1 > u.k0 ? vis[pc.k0] : 0, u.k1 > u.k0 ? vis[k_end - 1] + 1 : 0,
-              -1, 0, placed};
-      if (pc.k0 == u.k0 && p->with_draft && u.draft_cost > 0) it.flags |= skv::kItemDraft;
-      const int32_t wg = cls + bin.second * n_cls_fwd;
-      q[wg].push_back(int32_t(items.size()));
-      items.push_back(it);
-      bin.first += placed;
-      wg_load[wg] = bin.first;
-      bins.push(bin);
+      using Bin = std::pair<int64_t, int32_t>;  // (load, bin)
+      std::priority_queue<Bin, std::vector<Bin>, std::greater<Bin>> bins;
+      for (int32_t b = 0; b < per_cls; ++b) bins.push({0, b});
+      int32_t pieces = 0;
+      total_placed = 0;
+      while (!pend.empty()) {
+        const Pending pc = pend.top();
+        pend.pop();
+        const Unit& u = units[pc.unit];
+        Bin bin = bins.top();
+        bins.pop();
+        int32_t k_end = u.k1;
+        int64_t placed = pc.cost;
+        const int64_t head_cost = kItemCost + (pc.k0 == u.k0 ? u.draft_cost : 0);
+        if (bin.first + pc.cost > target && u.k1 - pc.k0 > 1 &&
+            target - bin.first >= head_cost + kStepCost) {
+          // cut: the longest prefix that fits (a bin with no room for one
+          // more step takes the piece whole)
+          const int64_t room = target - bin.first;
+          int64_t acc = head_cost;
+          int32_t k = pc.k0;
+          while (k < u.k1 && acc + kStepCost <= room) acc += kStepCost, ++k;
+          if (k < u.k1) {
+            k_end = k;
+            placed = acc;
+            pend.push({piece_cost(u, k, u.k1), pc.unit, k});
+          }
+        }
+        ++pieces;
+        total_placed += placed;
+        if (emit) {
+          const auto& vis = qt_vis[u.qt];
+          Item it{u.head, u.qt, u.k1 > u.k0 ? vis[pc.k0] : 0,
+                  u.k1 > u.k0 ? vis[k_end - 1] + 1 : 0, -1, 0, placed};
+          if (pc.k0 == u.k0 && p->with_draft && u.draft_cost > 0) it.flags |= skv::kItemDraft;
+          const int32_t wg = cls + bin.second * n_cls_fwd;
+          q[wg].push_back(int32_t(items.size()));
+          items.push_back(it);
+          wg_load[wg] = bin.first + placed;
+        }
+        bin.first += placed;
+        bins.push(bin);
+      }
+      return pieces;
+    };
+    // T starts at ceil(class cost / bins); cuts add item costs, so T is
+    // raised to the mean load each pass produced (a few passes settle it)
+    int64_t target = (cls_total + per_cls - 1) / per_cls;
+    for (int pass = 0; pass < 4; ++pass) {
+      plan(target, false);
+      const int64_t next = (total_placed + per_cls - 1) / per_cls + kItemCost / 2;
+      if (next == target) break;
+      target = next;
     }
+    plan(target, true);
   }
   // query tiles with several items write partial slots, merged afterwards
   std::vector<int32_t> split_rec;  // S_WORDS per split query tile
@@ -405,18 +437,21 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
     }
   }
   // dK/dV items: two consecutive tiles per item (one if a lone tile is
-  // left), plus draft groups of 128 draft tokens.
+  // left), plus draft groups of 128 draft tokens.  An item walks the 64-row
+  // tiles of its anchor blocks [b0, b1).
+  auto kv_cost = [&](int32_t b0, int32_t b1) {
+    const int64_t rows = int64_t(std::max(0, b1 - b0)) * skv::kBlock * g.G;
+    return kKvItemCost + kKvRowCost * ((rows + skv::kTileK - 1) / skv::kTileK);
+  };
   std::vector<KvItem> kv;
   for (int32_t h = 0; h < g.hkv; ++h) {
     for (int32_t t = 0; t < nt; t += 2) {
       const int32_t n2 = std::min(2, nt - t);
       int32_t bmin = g.nb, bmax = -1;
-      int64_t c = 0;
       for (int32_t u = t; u < t + n2; ++u)
         for (int32_t b = 0; b < g.nb; ++b)
           if (std::max<int64_t>(L[b], tiles[u].pos) <
               std::min<int64_t>(A[b], int64_t(tiles[u].pos) + tiles[u].len)) {
-            ++c;
             bmin = std::min(bmin, b);
             bmax = std::max(bmax, b);
           }
@@ -424,13 +459,13 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
         bmin = 0;
         bmax = -1;
       }
-      kv.push_back({h, t, n2, 0, 0, bmin, bmax + 1, c});
+      kv.push_back({h, t, n2, 0, 0, bmin, bmax + 1, kv_cost(bmin, bmax + 1)});
     }
     if (p->with_draft) {
       for (int32_t tok = 0; tok < g.nq; tok += skv::kKvGroup) {
         const int32_t nd = std::min(skv::kKvGroup, g.nq - tok);
         const int32_t b0 = tok / skv::kBlock, b1 = (tok + nd) / skv::kBlock;
-        kv.push_back({h, 0, 0, tok, nd, b0, b1, int64_t(b1 - b0)});
+        kv.push_back({h, 0, 0, tok, nd, b0, b1, kv_cost(b0, b1)});
       }
     }
   }

@@ -139,32 +139,38 @@ def _check_lpt_per_class(costs, heads, qoff, queue, n_wg, n_cls):
             assert queue[qoff[wgi]:qoff[wgi + 1]].tolist() == lst
 
 
+STEP_COST, ITEM_COST = 8, 44  # time units of a key step and of an item's fixed part
+
+
 def _lpt_split_items(w, g, tiles, n_wg, n_cls, with_draft):
     """Independent re-derivation of the forward item plan: per XCD class,
     runs of consecutive visible tiles of each (kv head, query tile) are
-    placed largest-first on the least-loaded workgroup, and a run that would
-    pass the class target ceil(total / bins) is cut after the longest tile
-    prefix that fits (at least one tile); the rest is pending again.
+    placed largest-first on the least-loaded workgroup.  A piece costs
+    ITEM_COST plus STEP_COST per key step (its tiles, and for the first run
+    of a query tile its draft steps).  A run that would pass the class target
+    T is cut after the longest tile prefix that fits, if the bin has room
+    for the piece's fixed part and one step; otherwise the bin takes it
+    whole.  T starts at ceil(total / bins) and is re-set (at most four times,
+    until it repeats) to the mean load of a pass plus ITEM_COST // 2.
     Returns the items (head, qt, t0, t1, flags, cost) in emission order and
     the per-workgroup queues."""
     import heapq
     G = w.hq // w.hkv
     tpq = QTILE // G
     qtph = -(-w.nq * G // QTILE)
-    vis, cst = [], []
+    vis = []
     for qt in range(qtph):
         b0 = qt * tpq // BLOCK
         b1 = min(w.nb, -(-((qt + 1) * tpq) // BLOCK))
         c = [oracle.tile_pairs_visible(g.anchors[b0:b1], g.lo[b0:b1], t[1], t[1] + t[2])
              for t in tiles]
         vis.append([i for i, x in enumerate(c) if x > 0])
-        cst.append([x for x in c if x > 0])
     units = []  # (head, qt, k0, k1, draft cost)
     for h in range(w.hkv):
         for qt in range(qtph):
             b0 = qt * tpq // BLOCK
             b1 = min(w.nb, -(-((qt + 1) * tpq) // BLOCK))
-            dc = (b1 - b0) if with_draft else 0
+            dc = STEP_COST * -(-((b1 - b0) * BLOCK) // 64) if with_draft else 0
             v = vis[qt]
             if not v:
                 units.append((h, qt, 0, 0, dc))
@@ -180,37 +186,46 @@ def _lpt_split_items(w, g, tiles, n_wg, n_cls, with_draft):
     items, queues = [], [[] for _ in range(n_wg)]
 
     def cost(u, k0):
-        return (u[4] if k0 == u[2] else 0) + sum(cst[u[1]][k0:u[3]])
+        return ITEM_COST + (u[4] if k0 == u[2] else 0) + STEP_COST * (u[3] - k0)
 
-    for c in range(n_cls):
+    def plan(c, target, emit):
         pend = [(-cost(u, u[2]), ui, u[2]) for ui, u in enumerate(units) if u[0] % n_cls == c]
-        total = -sum(x[0] for x in pend)
-        target = -(-total // per)
         heapq.heapify(pend)
         bins = [(0, b) for b in range(per)]
+        placed_total = 0
         while pend:
             negc, ui, k0 = heapq.heappop(pend)
             u = units[ui]
             load, b = heapq.heappop(bins)
             k_end, placed = u[3], -negc
-            if load - negc > target and u[3] - k0 > 1:
-                acc = u[4] if k0 == u[2] else 0
-                k = k0
-                while k < u[3] and acc + cst[u[1]][k] <= target - load:
-                    acc += cst[u[1]][k]
-                    k += 1
-                if k == k0:
-                    acc += cst[u[1]][k]
+            head = ITEM_COST + (u[4] if k0 == u[2] else 0)
+            if load - negc > target and u[3] - k0 > 1 and target - load >= head + STEP_COST:
+                acc, k = head, k0
+                while k < u[3] and acc + STEP_COST <= target - load:
+                    acc += STEP_COST
                     k += 1
                 if k < u[3]:
                     k_end, placed = k, acc
-                    heapq.heappush(pend, (-(-negc - acc), ui, k))
-            v = vis[u[1]]
-            t0, t1 = (v[k0], v[k_end - 1] + 1) if u[3] > u[2] else (0, 0)
-            flags = 1 if (k0 == u[2] and with_draft and u[4] > 0) else 0
-            queues[c + b * n_cls].append(len(items))
-            items.append((u[0], u[1], t0, t1, flags, placed))
+                    heapq.heappush(pend, (-cost(u, k), ui, k))
+            placed_total += placed
+            if emit:
+                v = vis[u[1]]
+                t0, t1 = (v[k0], v[k_end - 1] + 1) if u[3] > u[2] else (0, 0)
+                flags = 1 if (k0 == u[2] and with_draft and u[4] > 0) else 0
+                queues[c + b * n_cls].append(len(items))
+                items.append((u[0], u[1], t0, t1, flags, placed))
             heapq.heappush(bins, (load + placed, b))
+        return placed_total
+
+    for c in range(n_cls):
+        total = sum(cost(u, u[2]) for u in units if u[0] % n_cls == c)
+        target = -(-total // per)
+        for _ in range(4):
+            nxt = -(-plan(c, target, False) // per) + ITEM_COST // 2
+            if nxt == target:
+                break
+            target = nxt
+        plan(c, target, True)
     return items, queues
 
 
@@ -258,12 +273,14 @@ def test_schedule_covers_visible_work_once_and_is_lpt(case):
         hd, qt, t0, t1, slot, flags, cost = it[:7]
         seen[hd, qt, t0:t1] += 1
         draft_seen[hd, qt] += flags & 1
-        # the item cost is the oracle's pair count over its tiles (+ draft)
+        # the item cost: its fixed part plus one step per tile and per 64
+        # draft keys; every tile of the run is one some block sees
         b0 = qt * (QTILE // G) // BLOCK
         b1 = min(w.nb, -(-((qt + 1) * (QTILE // G)) // BLOCK))
-        want = sum(oracle.tile_pairs_visible(g.anchors[b0:b1], g.lo[b0:b1], tiles[t, 1],
-                                             tiles[t, 1] + tiles[t, 2]) for t in range(t0, t1))
-        want += (b1 - b0) if flags & 1 else 0
+        assert all(oracle.tile_pairs_visible(g.anchors[b0:b1], g.lo[b0:b1], tiles[t, 1],
+                                             tiles[t, 1] + tiles[t, 2]) > 0 for t in range(t0, t1))
+        want = ITEM_COST + STEP_COST * (t1 - t0)
+        want += STEP_COST * -(-((b1 - b0) * BLOCK) // 64) if flags & 1 else 0
         assert cost == want
     for qt in range(qtph):
         b0 = qt * (QTILE // G) // BLOCK
