@@ -11,7 +11,7 @@
 // The merge is HBM-bound (a few flops per byte): each thread owns 8
 // consecutive elements of one row (16-byte loads for bf16), rows are
 // contiguous, so every wave streams whole rows; partial loads are unrolled
-// for memory-level parallelism.
+// (eight in flight per thread) for memory-level parallelism.
 #include "device_common.h"
 #include "launch.h"
 #include "timing.h"
@@ -56,34 +56,42 @@ struct Vec8<float> {
 };
 
 // Merge one row: partial k of this row is at O + k*ostride, L + k*lstride.
-template <typename Tin, typename Tout>
+// The TPR threads of a row (consecutive lanes, `sub` = 0 .. TPR-1) each own 8
+// elements; they first split the partials' LSE values between them for the
+// row max and the sum of exp(LSE_k - M), combined by lane shuffles, so the
+// statistics take n / TPR dependent loads instead of n.
+template <typename Tin, typename Tout, int TPR>
 __device__ __forceinline__ void merge_row(int n, const Tin* O, int64_t ostride, const float* L,
-                                          int64_t lstride, Tout* out, float* lse_out,
-                                          bool write_lse) {
+                                          int64_t lstride, Tout* out, float* lse_out, int sub) {
   float M = kNegInf;
-  for (int k = 0; k < n; ++k) M = fmaxf(M, L[k * lstride]);
+  for (int k = sub; k < n; k += TPR) M = fmaxf(M, L[k * lstride]);
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   if (M == kNegInf) {
     Vec8<Tout>::store(out, acc);
-    if (write_lse) *lse_out = kNegInf;
+    if (sub == 0) *lse_out = kNegInf;
     return;
   }
   float sum = 0.f;
-  for (int k = 0; k < n; ++k) sum += exp2_fast((L[k * lstride] - M) * kLog2e);
+  for (int k = sub; k < n; k += TPR) sum += exp2_fast((L[k * lstride] - M) * kLog2e);
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
   const float lse = M + logf(sum);
   const float lse2 = lse * kLog2e;
+  constexpr int U = 8;  // partials in flight per thread
   int k = 0;
-  for (; k + 4 <= n; k += 4) {
-    float x[4][8], w[4];
+  for (; k + U <= n; k += U) {
+    float x[U][8], w[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       w[u] = exp2_fast(L[(k + u) * lstride] * kLog2e - lse2);
       Vec8<Tin>::load(O + (k + u) * ostride, x[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = w[u] > 0.f ? fmaf(w[u], x[u][i], acc[i]) : acc[i];
   }
@@ -95,7 +103,7 @@ __device__ __forceinline__ void merge_row(int n, const Tin* O, int64_t ostride, 
     for (int i = 0; i < 8; ++i) acc[i] = w > 0.f ? fmaf(w, x[i], acc[i]) : acc[i];
   }
   Vec8<Tout>::store(out, acc);
-  if (write_lse) *lse_out = lse;
+  if (sub == 0) *lse_out = lse;
 }
 
 template <typename Tin, typename Tout, int D>
@@ -105,9 +113,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int n, int64_t rows, co
   constexpr int RPB = kThreads / TPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int c = (threadIdx.x % TPR) * 8;
+  // whole rows leave together, so the row's lanes stay complete for the
+  // shuffles
   if (row >= rows) return;
-  merge_row<Tin, Tout>(n, O + row * D + c, rows * D, L + row, rows, Oo + row * D + c, Lo + row,
-                       c == 0);
+  merge_row<Tin, Tout, TPR>(n, O + row * D + c, rows * D, L + row, rows, Oo + row * D + c,
+                            Lo + row, threadIdx.x % TPR);
 }
 
 // Merge the in-GPU segments of split query tiles from the forward workspace.
@@ -128,8 +138,8 @@ __global__ __launch_bounds__(kThreads) void merge_split_kernel(const int32_t* S,
   if (rho >= nq * G) return;
   const int64_t orow = (int64_t)(rho / G) * hq + head * G + rho % G;
   const int64_t prow = (int64_t)slot0 * kQTile + rloc;
-  merge_row<float, Tout>(ns, wsO + prow * D + c, (int64_t)kQTile * D, wsL + prow, kQTile,
-                         O + orow * D + c, LSE + orow, c == 0);
+  merge_row<float, Tout, TPR>(ns, wsO + prow * D + c, (int64_t)kQTile * D, wsL + prow, kQTile,
+                              O + orow * D + c, LSE + orow, threadIdx.x % TPR);
 }
 
 template <int D>
