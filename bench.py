@@ -225,6 +225,9 @@ def main():
     ap.add_argument("--workload", default="ctx32k_q2k")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", choices=("context", "budget"),
+                    help="throughput over context length (2K-32K at 2048 draft queries) or over "
+                         "the draft-query budget (512-4096 at 32K context), fwd+bwd")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time the forward alone (diagnostic; not the benchmark step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -260,7 +263,20 @@ def main():
 
     if args.workload == "ctx1m_merge64":
         return bench_merge64(args)
-    w, g, _ = wl.make(args.workload, args.seed, tensors=False)
+    if args.sweep:
+        return run_sweep(args)
+    print(json.dumps(run_workload(args, args.workload)), flush=True)
+
+
+def run_workload(args, workload):
+    """One workload (a name or a Workload): plan, time `steps` steps, and
+    return the JSON record."""
+    import torch
+    from block_sparse_split_amd import splitkv as skv
+    from block_sparse_split_amd import shards
+    from block_sparse_split_amd import workloads as wl
+
+    w, g, _ = wl.make(workload, args.seed, tensors=False)
     # the 512K workload is one rank's share of a 64-way LPT split: its chunks
     # (no draft keys) against all queries, forward only
     rank_share = w.n_shards > 1
@@ -389,7 +405,44 @@ def main():
     if not args.no_cpu_baseline and not rank_share:
         log("timing the fp64 oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(w, g, t)
-    print(json.dumps(out), flush=True)
+    return out
+
+
+
+
+SWEEPS = {
+    # fixed draft-query budget (2048 queries), context 2K -> 32K; anchors
+    # uniform on [L/4, L) as in the 32K workload
+    "context": [dict(ctx=L, anchor_lo=L // 4, anchor_hi=L) for L in (2048, 4096, 8192, 16384, 32768)],
+    # fixed 32K context, draft-query budget 512 -> 4096
+    "budget": [dict(blocks_per_seq=nb) for nb in (32, 64, 128, 256)],
+}
+
+
+def run_sweep(args):
+    """Throughput over context length at a fixed query budget, or over the
+    query budget at a fixed context (the regime the pages study: a short
+    draft-query set against a long context)."""
+    from block_sparse_split_amd import workloads as wl
+    base = wl.WORKLOADS["ctx32k_q2k"]
+    points = []
+    for over in SWEEPS[args.sweep]:
+        w = wl.scaled(base, name=f"sweep_{args.sweep}", **over)
+        args.no_cpu_baseline = True
+        r = run_workload(args, w)
+        points.append({"context": r["config"]["context"], "draft_queries": r["config"]["draft_queries"],
+                       "ms_per_step": r["ms_per_step"], "tflops_fwd_bwd": r["value"],
+                       "tflops_fwd": r["fwd_tflops"], "fwd_ms": r["fwd_ms"],
+                       "frac_of_bf16_peak": r["frac_of_bf16_peak"],
+                       "item_imbalance_256cu": r["lpt"]["item_imbalance_256cu"],
+                       "plan_ms": r["lpt"]["plan_ms"]})
+        log(f"sweep {args.sweep}: ctx {points[-1]['context']}, queries {points[-1]['draft_queries']}: "
+            f"{points[-1]['ms_per_step']:.3f} ms, {points[-1]['tflops_fwd_bwd']:.0f} TFLOP/s")
+    last = points[-1]
+    print(json.dumps({"metric": METRIC, "value": last["tflops_fwd_bwd"], "unit": "TFLOP/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+                      "sweep": args.sweep, "points": points}), flush=True)
 
 
 if __name__ == "__main__":
