@@ -248,6 +248,11 @@ def _schedule_case(name, seed, shard_of=None, n_wg=256, **over):
     ("ctx32k_q2k", 1, None, 256, {}),
     ("ctx32k_q2k", 2, None, 40, dict(ctx=4096, anchor_lo=512, anchor_hi=4096, blocks_per_seq=16)),
     ("varlen8_fwdbwd", 3, None, 256, dict(len_median=2048, len_min=512, len_max=8192)),
+    # G = 16 (one anchor block per query tile) and G = 2 (eight)
+    ("ctx32k_q2k", 3, None, 64, dict(ctx=4096, anchor_lo=512, anchor_hi=4096, blocks_per_seq=24,
+                                     hq=32, hkv=2)),
+    ("ctx32k_q2k", 4, None, 48, dict(ctx=4096, anchor_lo=512, anchor_hi=4096, blocks_per_seq=24,
+                                     hq=16, hkv=8)),
     ("cp64_rank0_ctx512k", 2, 0, 256, {}),
     ("cp64_rank0_ctx512k", 2, 5, 256, {}),
     ("tiny_f32_ctx1k", 0, 1, 8, {}),
