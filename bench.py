@@ -228,6 +228,9 @@ def main():
     ap.add_argument("--sweep", choices=("context", "budget"),
                     help="throughput over context length (2K-32K at 2048 draft queries) or over "
                          "the draft-query budget (512-4096 at 32K context), fwd+bwd")
+    ap.add_argument("--compare-plans", action="store_true",
+                    help="also time the forward and dQ kernels with a contiguous (cost-blind) "
+                         "item plan of the same items")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time the forward alone (diagnostic; not the benchmark step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -402,10 +405,51 @@ def run_workload(args, workload):
     if rank_share:
         out["config"]["rank"] = f"0 of {w.n_shards} (LPT), {len(chunk_ids)} chunks"
         out["lpt"]["rank_imbalance"] = float(rank_load.max() / rank_load.mean() - 1)
+    if args.compare_plans and not rank_share:
+        out["in_gpu_plan_comparison"] = compare_item_plans(sh, step, kernels, args, torch)
     if not args.no_cpu_baseline and not rank_share:
         log("timing the fp64 oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(w, g, t)
     return out
+
+
+def compare_item_plans(sh, step, kernels_lpt, args, torch):
+    """Kernel times with the library's LPT item plan against a contiguous
+    plan of the same items: items sorted by (kv head, query tile, first
+    tile) and cut into equal-count runs, one per workgroup (no cost model).
+    Both plans compute every item exactly once; only the queues differ."""
+    from block_sparse_split_amd import splitkv as skv
+    img = sh.image.copy()
+    n_items, n_wg = int(img[11]), int(img[12])
+    off_items, off_qoff, off_queue = int(img[19]), int(img[20]), int(img[21])
+    items = img[off_items:off_items + 8 * n_items].reshape(n_items, 8)
+    order = np.lexsort((items[:, 2], items[:, 1], items[:, 0])).astype(np.int32)
+    img[off_queue:off_queue + n_items] = order
+    img[off_qoff:off_qoff + n_wg + 1] = np.linspace(0, n_items, n_wg + 1).astype(np.int32)
+    lpt_sched = sh.schedule
+    sh.schedule = torch.from_numpy(img).to(lpt_sched.device)
+    try:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        skv.skv_timing_collect()
+        skv.skv_timing_enable(True)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        skv.skv_timing_enable(False)
+        kernels_cont = skv.skv_timing_collect()
+    finally:
+        sh.schedule = lpt_sched
+    res = {"plan": "contiguous equal-count runs of the same items"}
+    for name in ("fwd_bf16", "bwd_dq"):
+        if name in kernels_lpt and name in kernels_cont:
+            a = kernels_lpt[name][1] / kernels_lpt[name][0]
+            b = kernels_cont[name][1] / kernels_cont[name][0]
+            res[name] = {"lpt_ms": a, "contiguous_ms": b, "gain": b / a}
+    log("in-GPU item plan, LPT vs contiguous: " + ", ".join(
+        f"{k} {v['lpt_ms']:.3f} vs {v['contiguous_ms']:.3f} ms" for k, v in res.items() if k != "plan"))
+    return res
 
 
 
