@@ -114,6 +114,29 @@ def traffic_for(kernel, workload, src_hash):
         return None
 
 
+def mfma_counters_for(kernel, workload, src_hash):
+    """Matrix-core busy share, MFMA/VALU co-issue share and the settled
+    clock of one kernel from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"mfma_util_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    lines = open(path).read().splitlines()
+    if f"kernel_source_sha256: {src_hash}" not in lines:
+        return None
+    for i, line in enumerate(lines):
+        if line.startswith("kernel ") and "mfma_busy" in line:
+            cols = line.split()
+            for row in lines[i + 1:]:
+                f = row.split()
+                if f and f[0] == kernel:
+                    rec = dict(zip(cols, f))
+                    return {"mfma_busy": float(rec["mfma_busy"].rstrip("%")) / 100,
+                            "mfma_valu_coexec": float(rec["coexec"].rstrip("%")) / 100,
+                            "clock_ghz": float(rec["clock_GHz"])}
+    return None
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_sparse_split_amd", "csrc")
@@ -366,6 +389,7 @@ def run_workload(args, workload):
     roof["kernel"] = dom
     roof["avg_ms"] = avg_s * 1e3
     roof["traffic"] = traffic_for(dom, w.name, kernel_source_hash())
+    roof["counters"] = mfma_counters_for(dom, w.name, kernel_source_hash())
 
     fwd_ms = sum(kernels[k][1] for k in ("fwd_bf16", "merge_split") if k in kernels) / args.steps
     value = step_flops / (ms * 1e-3) / 1e12

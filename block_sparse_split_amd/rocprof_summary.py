@@ -7,6 +7,8 @@ sources.
               (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by
               what the same counter reads for a plain elementwise copy of a
               known number of bytes
+  counters -- matrix-core utilisation per kernel from one `--pmc` run of the
+              SQ/GRBM counters listed in MFMA_COUNTERS
 
 Usage:
   python -m block_sparse_split_amd.rocprof_summary kernels STATS_CSV \\
@@ -14,6 +16,8 @@ Usage:
   python -m block_sparse_split_amd.rocprof_summary traffic KERNEL \\
       --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV \\
       --copy-bytes N --workload NAME --command "..." [--out FILE]
+  python -m block_sparse_split_amd.rocprof_summary counters CSV \\
+      --workload NAME --command "..." [--skip-first N] [--out FILE]
 """
 import argparse
 import csv
@@ -131,6 +135,82 @@ def cmd_traffic(a):
     emit("\n".join(lines) + "\n", a.out)
 
 
+# one --pmc pass: 8 SQ counters and 1 GRBM counter (the per-block limits)
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                 "SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS "
+                 "SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE")
+N_SIMD = 1024  # 256 CUs x 4 SIMDs
+N_XCD = 8
+
+
+def cmd_counters(a):
+    """Matrix-core utilisation of each library kernel.
+
+    Per dispatch, SQ counters are summed over their rows and GRBM_GUI_ACTIVE
+    (GPU busy cycles) is the maximum over its rows.  Derived figures:
+      mfma_busy   = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs)
+      coexec      = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES, the
+                    share of matrix-busy cycles in which a plain VALU
+                    instruction also issued on that SIMD
+      mfma_tflop  = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOP (executed work)
+      clock_ghz   = GRBM_GUI_ACTIVE / dispatch duration, when the CSV carries
+                    timestamps
+    """
+    vals = defaultdict(lambda: defaultdict(list))   # kernel -> counter -> [per dispatch]
+    per = defaultdict(lambda: defaultdict(lambda: defaultdict(list)))
+    durs = defaultdict(dict)
+    for row in csv.DictReader(open(a.csv)):
+        name = short_name(row["Kernel_Name"])
+        if not name:
+            continue
+        did = row["Dispatch_Id"]
+        per[name][did][row["Counter_Name"]].append(float(row["Counter_Value"]))
+        if row.get("Start_Timestamp") and row.get("End_Timestamp"):
+            durs[name][did] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+    out = [f"# matrix-core utilisation per kernel on workload {a.workload}",
+           f"command: {a.command}",
+           f"kernel_source_sha256: {kernel_source_hash()}",
+           f"counters: {MFMA_COUNTERS}",
+           f"dispatches per kernel: first {a.skip_first} skipped as warm-up", ""]
+    head = (f"{'kernel':<12} {'disp':>4} {'mfma_busy':>9} {'coexec':>7} {'mfma_TFLOP':>10} "
+            f"{'clock_GHz':>9} {'exec_TFLOP/s':>12} {'valu/mfma':>9} {'trans/mfma':>10} "
+            f"{'lds/mfma':>8} {'lds_conf':>8}")
+    out.append(head)
+    for name in sorted(per, key=lambda n: -sum(
+            sum(c.get("SQ_VALU_MFMA_BUSY_CYCLES", [0])) for c in per[n].values())):
+        dids = sorted(per[name], key=int)[a.skip_first:]
+        if not dids:
+            continue
+        agg = defaultdict(float)
+        dur = []
+        for did in dids:
+            for cn, v in per[name][did].items():
+                agg[cn] += max(v) if cn.startswith("GRBM_") else sum(v)
+            if did in durs[name]:
+                dur.append(durs[name][did])
+        n = len(dids)
+        g = lambda cn: agg.get(cn, float("nan")) / n
+        cyc = g("GRBM_GUI_ACTIVE")
+        if not g("SQ_VALU_MFMA_BUSY_CYCLES") > 0:
+            continue  # no matrix-core work (copies, reductions)
+        # GRBM_GUI_ACTIVE arrives summed over the 8 XCDs of the GPU
+        cyc /= N_XCD
+        busy = g("SQ_VALU_MFMA_BUSY_CYCLES") / (cyc * N_SIMD)
+        coex = g("SQ_VALU_MFMA_COEXEC_CYCLES") / g("SQ_VALU_MFMA_BUSY_CYCLES")
+        flop = g("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512
+        mf = g("SQ_INSTS_MFMA")
+        ns = sum(dur) / len(dur) if dur else float("nan")
+        clock = cyc / ns
+        out.append(f"{name:<12} {n:>4} {100 * busy:>8.1f}% {100 * coex:>6.1f}% {flop / 1e12:>10.4f} "
+                   f"{clock:>9.3f} {flop / ns / 1e3:>12.1f} {g('SQ_INSTS_VALU') / mf:>9.2f} "
+                   f"{g('SQ_INSTS_VALU_TRANS_F32') / mf:>10.2f} {g('SQ_INSTS_LDS') / mf:>8.2f} "
+                   f"{g('SQ_LDS_BANK_CONFLICT') / cyc / 256:>8.4f}")
+    out += ["", "valu/mfma, trans/mfma, lds/mfma: instructions per MFMA instruction "
+            "(SQ_INSTS_VALU counts MFMAs too); lds_conf: LDS bank-conflict cycles per CU "
+            "per GPU cycle"]
+    emit("\n".join(out) + "\n", a.out)
+
+
 def emit(text, out):
     if out:
         with open(out, "w") as f:
@@ -155,8 +235,14 @@ def main(argv=None):
         t.add_argument(opt, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--out")
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--skip-first", type=int, default=0)
+    c.add_argument("--out")
     a = ap.parse_args(argv)
-    {"kernels": cmd_kernels, "traffic": cmd_traffic}[a.what](a)
+    {"kernels": cmd_kernels, "traffic": cmd_traffic, "counters": cmd_counters}[a.what](a)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,54 @@
+"""Host-side checks of the rocprofv3 summary tooling (no GPU): the derived
+matrix-core figures and the bench's lookup of the committed summary."""
+import csv
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+from block_sparse_split_amd import rocprof_summary as rs  # noqa: E402
+
+
+def _write_csv(path, rows):
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+            "End_Timestamp"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        for r in rows:
+            w.writerow(dict(zip(cols, r)))
+
+
+def test_counters_summary_derived_values(tmp_path, monkeypatch):
+    # one warm-up dispatch (skipped) and two timed ones of a 1 ms kernel at
+    # 2 GHz: 2e6 cycles per XCD, reported summed over 8 XCDs
+    name = "void skv::(anonymous namespace)::bwd_dkdv_kernel<128>(skv::BwdArgs)"
+    rows = []
+    for did, busy in ((1, 9.9e9), (2, 1.024e9), (3, 1.024e9)):
+        vals = {"SQ_VALU_MFMA_BUSY_CYCLES": busy, "SQ_VALU_MFMA_COEXEC_CYCLES": busy / 4,
+                "SQ_INSTS_VALU_MFMA_MOPS_BF16": 2e9, "SQ_INSTS_MFMA": 1e7,
+                "SQ_INSTS_VALU": 5e7, "SQ_INSTS_VALU_TRANS_F32": 5e6, "SQ_INSTS_LDS": 2e7,
+                "SQ_LDS_BANK_CONFLICT": 0, "GRBM_GUI_ACTIVE": 8 * 2e6}
+        for cn, v in vals.items():
+            rows.append((did, name, cn, v, 1000, 1000 + 1_000_000))
+    src = tmp_path / "c.csv"
+    out = tmp_path / "s.txt"
+    _write_csv(src, rows)
+    rs.main(["counters", str(src), "--workload", "w", "--command", "cmd", "--skip-first", "1",
+             "--out", str(out)])
+    text = out.read_text()
+    row = [l.split() for l in text.splitlines() if l.startswith("bwd_dkdv")][0]
+    # busy = 1.024e9 / (2e6 cycles x 1024 SIMDs) = 50 %; co-issue = 25 %
+    assert row[1] == "2" and row[2] == "50.0%" and row[3] == "25.0%"
+    # 2e9 MOPS x 512 FLOP = 1.024 TFLOP in 1 ms at 2 GHz
+    assert row[4] == "1.0240" and row[5] == "2.000" and row[6] == "1024.0"
+
+    import bench
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    (tmp_path / "profiles" / "mfma_util_w.txt").write_text(text)
+    got = bench.mfma_counters_for("bwd_dkdv", "w", rs.kernel_source_hash())
+    assert got == {"mfma_busy": 0.5, "mfma_valu_coexec": 0.25, "clock_ghz": 2.0}
+    # a summary taken on other kernel sources is not reported
+    assert bench.mfma_counters_for("bwd_dkdv", "w", "0" * 64) is None
