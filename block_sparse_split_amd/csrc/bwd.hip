@@ -343,7 +343,7 @@ struct KvCfg {
   // P exchange: per pair 64 rows x 32 keys of bf16, in MFMA B-operand order
   static constexpr int kXOff = kStages * kStageBytes;
   static constexpr int kLdsBytes = kXOff + 4 * 4096;
-  // the four P waves issue all tile DMA (the dS waves issue none)
+  // the four dS waves issue all tile DMA (the P waves issue none)
   static constexpr int kDmaPerWave = 2 * ITile<D>::kBlocks / 4;
   static constexpr int kPrefetchNat = 6;
   static constexpr int kPrefetchTr = 4;
@@ -416,8 +416,8 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
     const int n_rt = (r_end - r_begin + kTileK - 1) / kTileK;
 
     auto stage_of = [&](int rt) { return lds0 + (rt % C::kStages) * C::kStageBytes; };
-    // P waves only: this wave's share of tile rt -- waves 0, 1 the Q blocks,
-    // waves 2, 3 the dO blocks (wave 0 also the row statistics).  The tile's
+    // dS waves only: this wave's share of tile rt -- waves 4, 5 the Q blocks,
+    // waves 6, 7 the dO blocks (wave 4 also the row statistics).  The tile's
     // first row is in the buffer base, block g adds the scalar qrow_bytes(g
     // kRB) and `dma_off` is the lane's row and column.  Rows past r_end read
     // the rows that follow (their statistics mask them), or zeros past the
@@ -425,7 +425,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
     auto issue = [&](int rt) {
       const uint32_t stage = stage_of(rt);
       const int rho0 = r_begin + kTileK * rt;
-      const bool iso = wave >= 2;
+      const bool iso = (wave & 2) != 0;
       const int64_t off = ((int64_t)(rho0 >> lgG) * hq + head * G) * D * 2;
       const i32x4 res =
           buf_res(reinterpret_cast<const char*>(iso ? dOg : Qg) + off, q_bytes - off);
@@ -435,7 +435,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
         dma16_buf(res, dma_off, qrow_bytes(g * ITile<D>::kRB),
                   stage + (iso ? C::kOOff : 0) + g * ITile<D>::kBlockStride);
       }
-      if (wave == 0) {
+      if ((wave & 3) == 0) {
         // 16 lanes per statistic (-D, L2, lo, anchor: consecutive arrays of
         // stat_words each), 4 rows per lane; a tile ends at most 63 rows
         // past the head's rows, inside its padding
@@ -457,7 +457,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
     }
     // settle the per-item loads before any tile DMA is in flight
     wait_vmcnt<0>();
-    if (pwave) {
+    if (!pwave) {
       if (n_rt > 0) issue(0);
       if (n_rt > 1) issue(1);
     }
@@ -467,16 +467,17 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-    // Opening barrier of tile rt: a P wave's share of tile rt has landed
+    // Opening barrier of tile rt: a dS wave's share of tile rt has landed
     // once at most tile rt+1's loads are in flight.  Tile rt+2 goes into the
-    // stage of tile rt-1, free after this barrier; the P waves issue it at
-    // the end of step rt, where they would otherwise wait for the dS waves.
+    // stage of tile rt-1, free after this barrier; the dS waves issue it
+    // after their dP MFMAs, where they would otherwise wait for the P
+    // waves' softmax.
     // Returns whether any row of the tile sees any of the pair's keys, and
     // whether all rows see all of them.
     auto open_tile = [&](int rt, bool& full) {
-      if (pwave) {
+      if (!pwave) {
         if (rt + 1 < n_rt) {
-          if (wave == 0) wait_vmcnt<C::kDmaPerWave + 1>();
+          if ((wave & 3) == 0) wait_vmcnt<C::kDmaPerWave + 1>();
           else wait_vmcnt<C::kDmaPerWave>();
         } else {
           wait_vmcnt<0>();
@@ -567,7 +568,6 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
                     o, pb[i / (2 * NDB)][(i / NDB) % 2], acc[i % NDB], 0, 0, 0);
               });
         }
-        if (rt + 2 < n_rt) issue(rt + 2);
       }
     } else {
       for (int rt = 0; rt < n_rt; ++rt) {
@@ -596,6 +596,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
                                                                     0, 0);
               });
         }
+        if (rt + 2 < n_rt) issue(rt + 2);
         block_barrier();
         if (any) {
           bf16x8 dsb[2][2];
