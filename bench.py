@@ -114,6 +114,26 @@ def traffic_for(kernel, workload, src_hash):
         return None
 
 
+def plan_imbalances(g, tile_k, bin_counts=(64, 256)):
+    """Chunk-level balance of one workload: for each bin count, the
+    max/mean - 1 of the bin loads under the library's LPT plan and under a
+    contiguous equal-length split (chunk c to bin floor(c m / n)) of the same
+    chunk costs."""
+    from block_sparse_split_amd import splitkv as skv
+
+    def imb(load):
+        load = np.asarray(load, np.float64)
+        return float(load.max() / load.mean() - 1.0) if load.mean() > 0 else 0.0
+
+    out = {}
+    for m in bin_counts:
+        _, cost, load = skv.skv_plan_lpt(g.anchors, g.lo, g.chunk_pos, g.chunk_len, tile_k, m)
+        cont = np.zeros(m, np.int64)
+        np.add.at(cont, np.arange(len(cost), dtype=np.int64) * m // len(cost), cost)
+        out[str(m)] = {"lpt": imb(load), "contiguous": imb(cont)}
+    return out
+
+
 def mfma_counters_for(kernel, workload, src_hash):
     """Matrix-core busy share, MFMA/VALU co-issue share and the settled
     clock of one kernel from the committed rocprofv3 counter summary, if it
@@ -225,7 +245,8 @@ def bench_merge64(args):
         "merge_ms": merge_ms,
         "merge_gbs": merge_bytes / (merge_ms * 1e-3) / 1e9,
         "merge_frac_of_hbm_peak": merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "lpt": {"shard_imbalance_64": float(load.max() / load.mean() - 1)},
+        "lpt": {"shard_imbalance_64": float(load.max() / load.mean() - 1),
+                "chunk_imbalance_by_bins": plan_imbalances(g, w.tile_k)},
         "simulated_cp_step": {
             "ranks": w.n_shards,
             "lpt_max_ms": float(t_lpt.max()), "lpt_mean_ms": float(t_lpt.mean()),
