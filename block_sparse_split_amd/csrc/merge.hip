@@ -11,7 +11,7 @@
 // The merge is HBM-bound (a few flops per byte): each thread owns 8
 // consecutive elements of one row (16-byte loads for bf16), rows are
 // contiguous, so every wave streams whole rows; partial loads are unrolled
-// (eight in flight per thread) for memory-level parallelism.
+// (sixteen in flight per thread) for memory-level parallelism.
 #include "device_common.h"
 #include "launch.h"
 #include "timing.h"
@@ -21,13 +21,17 @@ namespace {
 
 constexpr int kThreads = 256;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Partials are read exactly once: non-temporal loads keep them from
+// displacing reusable lines in the caches (about 7 % more HBM bandwidth for
+// the 64-way merge on MI355X).
 template <typename T>
 struct Vec8;
 template <>
 struct Vec8<__bf16> {
   static __device__ __forceinline__ void load(const __bf16* p, float* x) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[2 * i] = __uint_as_float(w[i] << 16);
@@ -44,10 +48,13 @@ struct Vec8<__bf16> {
 template <>
 struct Vec8<float> {
   static __device__ __forceinline__ void load(const float* p, float* x) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = a[i];
+      x[4 + i] = b[i];
+    }
   }
   static __device__ __forceinline__ void store(float* p, const float* x) {
     *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
@@ -81,7 +88,7 @@ __device__ __forceinline__ void merge_row(int n, const Tin* O, int64_t ostride, 
   for (int o = TPR / 2; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
   const float lse = M + logf(sum);
   const float lse2 = lse * kLog2e;
-  constexpr int U = 8;  // partials in flight per thread
+  constexpr int U = 16;  // partials in flight per thread
   int k = 0;
   for (; k + U <= n; k += U) {
     float x[U][8], w[U];
