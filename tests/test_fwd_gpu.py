@@ -149,7 +149,9 @@ def test_empty_and_draft_only_shards():
 
 @pytest.mark.parametrize("k,rows,d,in_dt,out_dt", [
     (1, 100, 128, "f32", "f32"), (3, 1000, 64, "f32", "f32"), (5, 333, 128, "bf16", "f32"),
-    (64, 2048, 128, "bf16", "bf16"), (7, 517, 64, "f32", "bf16")])
+    (64, 2048, 128, "bf16", "bf16"), (7, 517, 64, "f32", "bf16"),
+    # sixteen partials per unrolled pass: one full pass, and a pass plus a tail
+    (16, 64, 64, "f32", "f32"), (20, 777, 128, "bf16", "bf16")])
 def test_merge_random_partials(k, rows, d, in_dt, out_dt):
     rng = np.random.default_rng(k * 1000 + rows)
     O = rng.standard_normal((k, rows, d)).astype(np.float32)
