@@ -20,6 +20,7 @@
 #include <stdexcept>
 #include <string>
 #include <utility>
+#include <initializer_list>
 #include <vector>
 
 #include "launch.h"
@@ -600,6 +601,16 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
   image[off_kvqoff + n_wg] = pos;
 }
 
+// Tensors are read and written with 16-byte vector accesses (and the
+// workspace with float4 stores); LSE arrays with 4-byte ones.
+void require_aligned(std::initializer_list<const void*> ptrs, uintptr_t align,
+                     const char* what) {
+  for (const void* q : ptrs)
+    if (q != nullptr && (reinterpret_cast<uintptr_t>(q) & (align - 1)) != 0)
+      fail(SKV_ERR_INVALID_ARG, std::string(what) + " must be " + std::to_string(align) +
+                                    "-byte aligned");
+}
+
 void check_info(const skv_problem* p, const skv_schedule_info* info,
                 const int32_t* schedule) {
   const Geometry g = check_problem(p);
@@ -677,6 +688,8 @@ skv_status skv_attn_fwd_partial(const skv_problem* p, const skv_schedule_info* i
     require(Q && O && LSE, "Q/O/LSE must not be NULL");
     require(info->n_local == 0 || (K && V), "K/V must not be NULL");
     require(!p->with_draft || (Kd && Vd), "Kd/Vd must not be NULL with with_draft");
+    require_aligned({Q, K, V, Kd, Vd, O, workspace}, 16, "Q/K/V/Kd/Vd/O/workspace");
+    require_aligned({LSE}, 4, "LSE");
     if (!(o_dtype == SKV_BF16 || o_dtype == SKV_F32))
       fail(SKV_ERR_UNSUPPORTED, "o_dtype must be SKV_BF16 or SKV_F32");
     if (info->fwd_workspace_bytes > 0) {
@@ -716,6 +729,8 @@ skv_status skv_merge_lse(int32_t n_parts, int64_t rows, int32_t d, const void* O
       fail(SKV_ERR_UNSUPPORTED, "dtypes must be SKV_BF16 or SKV_F32");
     if (rows == 0) return;
     require(O_parts && LSE_parts && O_out && LSE_out, "pointers must not be NULL");
+    require_aligned({O_parts, O_out}, 16, "O_parts/O_out");
+    require_aligned({LSE_parts, LSE_out}, 4, "LSE_parts/LSE_out");
     const char* ob = static_cast<const char*>(O_out);
     const char* ib = static_cast<const char*>(O_parts);
     const int64_t out_bytes = rows * d * int64_t(elem_size(out_dtype));
@@ -740,6 +755,9 @@ skv_status skv_attn_bwd(const skv_problem* p, const skv_schedule_info* info,
     require(info->n_local == 0 || (K && V && dK && dV), "K/V/dK/dV must not be NULL");
     require(!p->with_draft || (Kd && Vd && dKd && dVd),
             "Kd/Vd/dKd/dVd must not be NULL with with_draft");
+    require_aligned({Q, K, V, Kd, Vd, O, dO, dQ, dK, dV, dKd, dVd, workspace}, 16,
+                    "Q/K/V/Kd/Vd/O/dO/dQ/dK/dV/dKd/dVd/workspace");
+    require_aligned({LSE}, 4, "LSE");
     if (!(grad_dtype == SKV_BF16 || grad_dtype == SKV_F32))
       fail(SKV_ERR_UNSUPPORTED, "grad_dtype must be SKV_BF16 or SKV_F32");
     if (p->dtype != SKV_BF16) fail(SKV_ERR_UNSUPPORTED, "the backward takes bf16 inputs only");

@@ -33,7 +33,9 @@
  *   - Device calls are asynchronous on the caller's stream (`stream` is a
  *     hipStream_t passed as void*; NULL is the default stream).  Launch
  *     errors are returned as SKV_ERR_HIP.  Host calls are synchronous.
- *   - Tensors are dense, row-major, 16-byte aligned:
+ *   - Tensors are dense, row-major, 16-byte aligned (LSE arrays: 4-byte;
+ *     the workspace: 16-byte).  A misaligned pointer is refused with
+ *     SKV_ERR_INVALID_ARG before anything is launched:
  *       Q, O, dO, dQ   [Nq, hq, d]       (Nq = 16 * nb, token-major)
  *       LSE            [Nq, hq]          fp32, natural log
  *       K, V, dK, dV   [n_local, hkv, d] (local key rows of the shard)

@@ -350,6 +350,38 @@ def test_in_gpu_item_plan_imbalance_below_one_percent(name, seed):
     assert imb < 0.01 and kv_imb < 0.01, (imb, kv_imb)
 
 
+def test_device_calls_reject_misaligned_tensors_before_launch():
+    """Tensors must be 16-byte aligned (LSE arrays 4-byte): a misaligned
+    pointer is refused before any launch (the fake pointers are never
+    dereferenced)."""
+    import ctypes
+    w, g, _ = wl.make("tiny_f32_ctx1k", 0, tensors=False)
+    prob = shards.whole_context_problem(w, g)
+    image, info = skv.skv_schedule_build(prob, 8)
+    L = skv.lib()
+    ok, bad8, bad2 = ctypes.c_void_p(256), ctypes.c_void_p(264), ctypes.c_void_p(258)
+    # forward: K at an 8-byte boundary
+    st = L.skv_attn_fwd_partial(ctypes.byref(prob.c), ctypes.byref(info), ok, ok, bad8, ok,
+                                ok, ok, ok, 1, ok, ok, 1 << 30, None)
+    assert st == -1 and b"16-byte aligned" in L.skv_last_error()
+    # forward: LSE off a 4-byte boundary
+    st = L.skv_attn_fwd_partial(ctypes.byref(prob.c), ctypes.byref(info), ok, ok, ok, ok,
+                                ok, ok, ok, 1, bad2, ok, 1 << 30, None)
+    assert st == -1 and b"4-byte aligned" in L.skv_last_error()
+    # merge: O_out misaligned
+    st = L.skv_merge_lse(2, 16, 64, ok, 1, ok, ctypes.c_void_p(1 << 20 | 8), 1, ok, None)
+    assert st == -1 and b"16-byte aligned" in L.skv_last_error()
+    # backward (bf16 problem): dK misaligned
+    wb, gb, _ = wl.make("ctx32k_q2k", 1, tensors=False)
+    wb = wl.scaled(wb, ctx=2048, anchor_lo=512, anchor_hi=2048, blocks_per_seq=8)
+    wb, gb, _ = wl.make(wb, 0, tensors=False)
+    pb = shards.whole_context_problem(wb, gb)
+    _, ib = skv.skv_schedule_build(pb, 8)
+    st = L.skv_attn_bwd(ctypes.byref(pb.c), ctypes.byref(ib), ok, ok, ok, ok, ok, ok, ok, ok,
+                        ok, ok, bad8, ok, ok, ok, 0, ok, 1 << 40, None)
+    assert st == -1 and b"16-byte aligned" in L.skv_last_error()
+
+
 def test_device_calls_reject_bad_dtypes_before_launch():
     """Argument errors are returned before anything touches a device (the
     fake pointers below are never dereferenced)."""
