@@ -159,6 +159,7 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
     const sched_t it = items + queue[qi] * I_WORDS;
     const int head = it[I_HEAD], qt = it[I_QT], t0 = it[I_T0], t1 = it[I_T1];
     const int slot = it[I_SLOT], flags = it[I_FLAGS];
+    const int ws0 = it[I_WHOLE] & 0xFFFF, ws1 = it[I_WHOLE] >> 16;
     const QTileSpan sp = qtile_span(qt, G, nq);
     const int n_draft = (flags & kItemDraft) ? (sp.dtok1 - sp.dtok0 + kTileK - 1) / kTileK : 0;
     const int n_steps = n_draft + (t1 - t0);
@@ -212,17 +213,21 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
       else wait_vmcnt<0>();
       block_barrier();
       if (s + 2 < n_steps) issue(s + 2);
-      const Step st = item_step(tiles, s, n_draft, t0, sp);
       const uint32_t stage = lds0 + (s % C::kStages) * C::kStageBytes;
+      // steps every row sees whole need no bounds
       int klo = 0, khi = kTileK;
-      bool lane_any = false, lane_full = true;
-      if (valid) {
-        step_bounds(st, lo_, an, blk, klo, khi);
-        lane_any = klo < khi;
-        lane_full = klo <= 0 && khi >= kTileK;
+      bool full = true;
+      if (s < ws0 || s >= ws1) {
+        const Step st = item_step(tiles, s, n_draft, t0, sp);
+        bool lane_any = false, lane_full = true;
+        if (valid) {
+          step_bounds(st, lo_, an, blk, klo, khi);
+          lane_any = klo < khi;
+          lane_full = klo <= 0 && khi >= kTileK;
+        }
+        if (!__any(lane_any)) continue;
+        full = __all(lane_full);
       }
-      if (!__any(lane_any)) continue;
-      const bool full = __all(lane_full);
       const int klo4 = klo - 4 * h32, khi4 = khi - 4 * h32;
       const uint32_t kbase = opaque(stage + knoff);
       const uint32_t vbase = opaque(stage + voff);

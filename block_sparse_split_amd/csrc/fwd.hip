@@ -131,6 +131,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
     const sched_t it = items + queue[qi] * I_WORDS;
     const int head = it[I_HEAD], qt = it[I_QT], t0 = it[I_T0], t1 = it[I_T1];
     const int slot = it[I_SLOT], flags = it[I_FLAGS];
+    const int ws0 = it[I_WHOLE] & 0xFFFF, ws1 = it[I_WHOLE] >> 16;
     const QTileSpan sp = qtile_span(qt, G, nq);
     const int n_draft = (flags & kItemDraft) ? (sp.dtok1 - sp.dtok0 + kTileK - 1) / kTileK : 0;
     const int n_steps = n_draft + (t1 - t0);
@@ -243,17 +244,20 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
         lds_pipelined<NMF, C::kPrefetchK>(qk_read, qk_mfma);
       }
       half_step(2 * p + k0 + 1);
-      // softmax of step p
-      const Step st = item_step(tiles, p, n_draft, t0, sp);
+      // softmax of step p; steps every row sees whole need no bounds
       int klo = 0, khi = kTileK;
-      bool lane_any = false, lane_full = true;
-      if (valid) {
-        step_bounds(st, lo_, an, blk, klo, khi);
-        lane_any = klo < khi;
-        lane_full = klo <= 0 && khi >= kTileK;
+      bool s_act = true, s_full = true;
+      if (p < ws0 || p >= ws1) {
+        const Step st = item_step(tiles, p, n_draft, t0, sp);
+        bool lane_any = false, lane_full = true;
+        if (valid) {
+          step_bounds(st, lo_, an, blk, klo, khi);
+          lane_any = klo < khi;
+          lane_full = klo <= 0 && khi >= kTileK;
+        }
+        s_act = __any(lane_any);
+        s_full = __all(lane_full);
       }
-      const bool s_act = __any(lane_any);
-      const bool s_full = __all(lane_full);
       p_act = s_act;
       if (s_act) {
         if (!s_full) {

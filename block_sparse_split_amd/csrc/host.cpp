@@ -481,6 +481,36 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
   int64_t item_total = 0;
   for (const auto& it : items) item_total += it.cost;
 
+  // Steps of an item that every row of its query tile sees whole: the
+  // first maximal run of full-length tiles inside [max lo, min anchor) of
+  // the tile's anchor blocks.  Packed as s0 | s1 << 16 in item steps (the
+  // draft steps come first and are never whole); empty if the item has
+  // 2^16 steps or more.
+  auto whole_steps = [&](const Item& it) -> int32_t {
+    const int32_t b0 = it.qt * tok_per_qt / skv::kBlock;
+    const int32_t b1 = std::min(g.nb, ((it.qt + 1) * tok_per_qt + skv::kBlock - 1) / skv::kBlock);
+    if (b1 <= b0) return 0;
+    int64_t lo_max = INT64_MIN, a_min = INT64_MAX;
+    for (int32_t b = b0; b < b1; ++b) {
+      lo_max = std::max<int64_t>(lo_max, L[b]);
+      a_min = std::min<int64_t>(a_min, A[b]);
+    }
+    const int32_t nd = (it.flags & skv::kItemDraft)
+                           ? ((b1 - b0) * skv::kBlock + skv::kTileK - 1) / skv::kTileK
+                           : 0;
+    if (int64_t(nd) + (it.t1 - it.t0) >= (int64_t(1) << 16)) return 0;
+    auto whole = [&](int32_t t) {
+      return tiles[t].len == skv::kTileK && tiles[t].pos >= lo_max &&
+             int64_t(tiles[t].pos) + skv::kTileK <= a_min;
+    };
+    int32_t t = it.t0;
+    while (t < it.t1 && !whole(t)) ++t;
+    int32_t e = t;
+    while (e < it.t1 && whole(e)) ++e;
+    if (e == t) return 0;
+    return (nd + (t - it.t0)) | ((nd + (e - it.t0)) << 16);
+  };
+
   // Image layout.
   using namespace skv;
   int64_t off = H_WORDS;
@@ -574,6 +604,7 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
     w[I_SLOT] = items[i].slot;
     w[I_FLAGS] = items[i].flags;
     w[I_COST] = int32_t(std::min<int64_t>(items[i].cost, INT32_MAX));
+    w[I_WHOLE] = whole_steps(items[i]);
   }
   int32_t pos = 0;
   for (int32_t w = 0; w < n_wg; ++w) {

@@ -34,8 +34,11 @@ enum TileW : int { T_ROW = 0, T_POS, T_LEN, T_PAD, T_WORDS = 4 };
 
 // Forward / dQ item: 8 words.  Tiles [t0, t1) of the sorted tile list;
 // slot < 0 writes the final rows directly, else partial slot `slot`.
+// I_WHOLE packs the item's steps [s0, s1) (s0 in the low 16 bits) that
+// every row of the query tile sees whole: full 64-key tiles inside every
+// row's visible interval, which need neither bounds nor masks.
 enum ItemW : int {
-  I_HEAD = 0, I_QT, I_T0, I_T1, I_SLOT, I_FLAGS, I_COST, I_PAD, I_WORDS = 8
+  I_HEAD = 0, I_QT, I_T0, I_T1, I_SLOT, I_FLAGS, I_COST, I_WHOLE, I_WORDS = 8
 };
 constexpr int32_t kItemDraft = 1;  // the item also covers the draft keys
 

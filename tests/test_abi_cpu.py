@@ -258,6 +258,54 @@ def _schedule_case(name, seed, shard_of=None, n_wg=256, **over):
     ("tiny_f32_ctx1k", 0, 1, 8, {}),
     ("tiny_f32_ctx1k", 0, 0, 3, {}),
 ])
+def test_whole_step_ranges_need_no_mask(case):
+    """Each item marks the run of its steps [s0, s1) that every row of its
+    query tile sees whole, so the kernels skip bounds and masks there: each
+    such step must be a full 64-key context tile inside every anchor block's
+    interval [lo, anchor)."""
+    name, seed, shard_of, n_wg, over = case
+    w, g, prob, pos, image, info = _schedule_case(name, seed, shard_of, n_wg, **over)
+    h, tiles, items, *_ = _decode(image)
+    G = w.hq // w.hkv
+    tpq = QTILE // G
+    n_whole = 0
+    for it in items:
+        hd, qt, t0, t1, slot, flags, cost, whole = (int(x) for x in it)
+        s0, s1 = whole & 0xFFFF, whole >> 16
+        b0 = qt * tpq // BLOCK
+        b1 = min(w.nb, -(-((qt + 1) * tpq) // BLOCK))
+        dtok0 = b0 * BLOCK
+        dtok1 = min(w.nq, b1 * BLOCK)
+        nd = -(-(dtok1 - dtok0) // TILE_K) if flags & 1 else 0
+        assert s0 <= s1 <= nd + t1 - t0
+        if s1 > s0:
+            assert s0 >= nd
+        for s in range(s0, s1):
+            t = t0 + s - nd
+            p0, n = int(tiles[t][1]), int(tiles[t][2])
+            assert n == TILE_K
+            assert all(g.lo[b] <= p0 and p0 + n <= g.anchors[b] for b in range(b0, b1))
+        n_whole += s1 - s0
+    # most steps of the long-context workloads are whole
+    if name in ("ctx32k_q2k", "cp64_rank0_ctx512k") and not over:
+        n_ctx = sum(int(it[3]) - int(it[2]) for it in items)
+        assert n_whole > 0.8 * n_ctx
+
+
+@pytest.mark.parametrize("case", [
+    ("ctx32k_q2k", 1, None, 256, {}),
+    ("ctx32k_q2k", 2, None, 40, dict(ctx=4096, anchor_lo=512, anchor_hi=4096, blocks_per_seq=16)),
+    ("varlen8_fwdbwd", 3, None, 256, dict(len_median=2048, len_min=512, len_max=8192)),
+    # G = 16 (one anchor block per query tile) and G = 2 (eight)
+    ("ctx32k_q2k", 3, None, 64, dict(ctx=4096, anchor_lo=512, anchor_hi=4096, blocks_per_seq=24,
+                                     hq=32, hkv=2)),
+    ("ctx32k_q2k", 4, None, 48, dict(ctx=4096, anchor_lo=512, anchor_hi=4096, blocks_per_seq=24,
+                                     hq=16, hkv=8)),
+    ("cp64_rank0_ctx512k", 2, 0, 256, {}),
+    ("cp64_rank0_ctx512k", 2, 5, 256, {}),
+    ("tiny_f32_ctx1k", 0, 1, 8, {}),
+    ("tiny_f32_ctx1k", 0, 0, 3, {}),
+])
 def test_schedule_covers_visible_work_once_and_is_lpt(case):
     name, seed, shard_of, n_wg, over = case
     w, g, prob, pos, image, info = _schedule_case(name, seed, shard_of, n_wg, **over)
