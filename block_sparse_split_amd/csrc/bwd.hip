@@ -400,6 +400,8 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
     const sched_t it = kvs + queue[qi] * K_WORDS;
     const int head = it[K_HEAD], t0 = it[K_T0], nt = it[K_NT];
     const int dtok0 = it[K_DTOK0], nd = it[K_NDRAFT], b0 = it[K_B0], b1 = it[K_B1];
+    // row tiles every row of which sees all of the item's keys
+    const int kw0 = it[K_WHOLE] & 0xFFFF, kw1 = it[K_WHOLE] >> 16;
     const bool draft = nd > 0;
     // the pair's 32 keys: rows of K/V (or Kd/Vd) and absolute positions
     // (draft keys: their draft token)
@@ -479,7 +481,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
     // waves' softmax.
     // Returns whether any row of the tile sees any of the pair's keys, and
     // whether all rows see all of them.
-    auto open_tile = [&](int rt, bool& full) {
+    auto open_tile = [&](int rt, bool& full) -> bool {
       if (!pwave) {
         if (rt + 1 < n_rt) {
           if ((wave & 3) == 0) wait_vmcnt<C::kDmaPerWave + 1>();
@@ -489,6 +491,10 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
         }
       }
       block_barrier();
+      if (rt >= kw0 && rt < kw1) {
+        full = true;
+        return nk > 0;
+      }
       // Rows past r_end belong to blocks that see none of the item's keys
       // (their statistics, or the padding rows, say so), so every row's own
       // interval decides; draft keys: the row's block.

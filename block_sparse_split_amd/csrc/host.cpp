@@ -231,6 +231,7 @@ constexpr int64_t kKvItemCost = 13;
 struct KvItem {
   int32_t head, t0, nt, dtok0, ndraft, b0, b1;
   int64_t cost;
+  int32_t whole = 0;  // row tiles [w0, w1) every row of which sees all keys: w0 | w1 << 16
 };
 
 // XCD classes: workgroup w runs on XCD w % 8 (round-robin dispatch), so the
@@ -461,6 +462,29 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
         bmax = -1;
       }
       kv.push_back({h, t, n2, 0, 0, bmin, bmax + 1, kv_cost(bmin, bmax + 1)});
+      // row tiles inside [b0, b1) whose anchor blocks all see every key of
+      // the item: they need neither the per-row intervals nor masks
+      {
+        const int64_t kmin = tiles[t].pos;
+        const int64_t kend = int64_t(tiles[t + n2 - 1].pos) + tiles[t + n2 - 1].len;
+        const int64_t rpb = int64_t(skv::kBlock) * g.G;  // rows per anchor block
+        const int64_t r_begin = int64_t(bmin) * rpb, r_end = int64_t(bmax + 1) * rpb;
+        const int64_t n_rt = (std::max<int64_t>(0, r_end - r_begin) + skv::kTileK - 1) / skv::kTileK;
+        auto whole = [&](int64_t rt) {
+          const int64_t r0 = r_begin + rt * skv::kTileK;
+          if (r0 + skv::kTileK > r_end) return false;
+          for (int64_t b = r0 / rpb; b <= (r0 + skv::kTileK - 1) / rpb; ++b)
+            if (!(L[b] <= kmin && A[b] >= kend)) return false;
+          return true;
+        };
+        if (n_rt < (int64_t(1) << 16)) {
+          int64_t w0 = 0;
+          while (w0 < n_rt && !whole(w0)) ++w0;
+          int64_t w1 = w0;
+          while (w1 < n_rt && whole(w1)) ++w1;
+          if (w1 > w0) kv.back().whole = int32_t(w0 | (w1 << 16));
+        }
+      }
     }
     if (p->with_draft) {
       for (int32_t tok = 0; tok < g.nq; tok += skv::kKvGroup) {
@@ -623,6 +647,7 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
     w[K_B0] = kv[i].b0;
     w[K_B1] = kv[i].b1;
     w[K_COST] = int32_t(std::min<int64_t>(kv[i].cost, INT32_MAX));
+    w[K_WHOLE] = kv[i].whole;
   }
   pos = 0;
   for (int32_t w = 0; w < n_wg; ++w) {

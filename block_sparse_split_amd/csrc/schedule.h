@@ -45,11 +45,11 @@ constexpr int32_t kItemDraft = 1;  // the item also covers the draft keys
 // Split query tile: 4 words.
 enum SplitW : int { S_HEAD = 0, S_QT, S_SLOT0, S_NSLOT, S_WORDS = 4 };
 
-// dK/dV item: 8 words.  Either context keys (tiles t0 .. t0+nt-1, nt in
+// dK/dV item: 9 words.  Either context keys (tiles t0 .. t0+nt-1, nt in
 // {1, 2}) or draft keys (draft tokens [dtok0, dtok0 + ndraft)).  Query
 // blocks [b0, b1) may see the keys.
 enum KvW : int {
-  K_HEAD = 0, K_T0, K_NT, K_DTOK0, K_NDRAFT, K_B0, K_B1, K_COST, K_WORDS = 8
+  K_HEAD = 0, K_T0, K_NT, K_DTOK0, K_NDRAFT, K_B0, K_B1, K_COST, K_WHOLE, K_WORDS = 9
 };
 
 }  // namespace skv

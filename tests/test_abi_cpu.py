@@ -258,6 +258,55 @@ def _schedule_case(name, seed, shard_of=None, n_wg=256, **over):
     ("tiny_f32_ctx1k", 0, 1, 8, {}),
     ("tiny_f32_ctx1k", 0, 0, 3, {}),
 ])
+def test_whole_row_tiles_of_dkdv_items_need_no_mask(case):
+    """Each context dK/dV item marks the run of its 64-row tiles [w0, w1)
+    whose rows all see every key of the item, so the kernel skips the
+    per-row intervals and masks there: each such tile must lie inside the
+    item's rows, and every anchor block it covers must see the item's whole
+    key range."""
+    name, seed, shard_of, n_wg, over = case
+    w, g, prob, pos, image, info = _schedule_case(name, seed, shard_of, n_wg, **over)
+    h, tiles, items, qoff, queue, split, kv, kvqoff, kvqueue = _decode(image)
+    G = w.hq // w.hkv
+    rpb = BLOCK * G
+    n_whole = n_rt_all = 0
+    for k in kv:
+        hd, t0, nt, dtok0, nd, b0, b1, cost, whole = (int(x) for x in k)
+        w0, w1 = whole & 0xFFFF, whole >> 16
+        r_begin, r_end = b0 * rpb, b1 * rpb
+        n_rt = -(-max(0, r_end - r_begin) // TILE_K)
+        assert w0 <= w1 <= n_rt
+        if nd > 0:
+            assert whole == 0
+            continue
+        if w1 > w0:
+            kmin = int(tiles[t0][1])
+            kend = int(tiles[t0 + nt - 1][1]) + int(tiles[t0 + nt - 1][2])
+            for rt in range(w0, w1):
+                r0 = r_begin + TILE_K * rt
+                assert r0 + TILE_K <= r_end
+                for b in range(r0 // rpb, (r0 + TILE_K - 1) // rpb + 1):
+                    assert g.lo[b] <= kmin and g.anchors[b] >= kend
+        n_whole += w1 - w0
+        n_rt_all += n_rt
+    if name == "ctx32k_q2k" and not over:
+        assert n_whole > 0.8 * n_rt_all
+
+
+@pytest.mark.parametrize("case", [
+    ("ctx32k_q2k", 1, None, 256, {}),
+    ("ctx32k_q2k", 2, None, 40, dict(ctx=4096, anchor_lo=512, anchor_hi=4096, blocks_per_seq=16)),
+    ("varlen8_fwdbwd", 3, None, 256, dict(len_median=2048, len_min=512, len_max=8192)),
+    # G = 16 (one anchor block per query tile) and G = 2 (eight)
+    ("ctx32k_q2k", 3, None, 64, dict(ctx=4096, anchor_lo=512, anchor_hi=4096, blocks_per_seq=24,
+                                     hq=32, hkv=2)),
+    ("ctx32k_q2k", 4, None, 48, dict(ctx=4096, anchor_lo=512, anchor_hi=4096, blocks_per_seq=24,
+                                     hq=16, hkv=8)),
+    ("cp64_rank0_ctx512k", 2, 0, 256, {}),
+    ("cp64_rank0_ctx512k", 2, 5, 256, {}),
+    ("tiny_f32_ctx1k", 0, 1, 8, {}),
+    ("tiny_f32_ctx1k", 0, 0, 3, {}),
+])
 def test_whole_step_ranges_need_no_mask(case):
     """Each item marks the run of its steps [s0, s1) that every row of its
     query tile sees whole, so the kernels skip bounds and masks there: each
