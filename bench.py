@@ -492,10 +492,10 @@ def run_workload(args, workload):
     dVd = torch.empty_like(Vd)
     stream = torch.cuda.current_stream()
 
-    def step():
-        sh.fwd(Q, K, V, Kd, Vd, O, LSE, stream)
+    def step(s=stream):
+        sh.fwd(Q, K, V, Kd, Vd, O, LSE, s)
         if not args.fwd_only:
-            sh.bwd(Q, K, V, Kd, Vd, O, dO, LSE, dQ, dK, dV, dKd, dVd, skv.SKV_BF16, stream)
+            sh.bwd(Q, K, V, Kd, Vd, O, dO, LSE, dQ, dK, dV, dKd, dVd, skv.SKV_BF16, s)
 
     for _ in range(args.warmup):
         step()
@@ -514,6 +514,8 @@ def run_workload(args, workload):
     kernels = skv.skv_timing_collect()
     ms = start.elapsed_time(stop) / args.steps
     log(f"{ms:.3f} ms/step")
+    graph = graph_step(step, (O, LSE) if args.fwd_only else (O, LSE, dQ, dK, dV, dKd, dVd),
+                       args, torch)
 
     E = (shard_visible_elements(g, w.hq, chunk_ids, False) if rank_share
          else visible_elements(g, w.hq))
@@ -570,6 +572,10 @@ def run_workload(args, workload):
         "fwd_frac_of_bf16_peak": fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "fwd_ms": fwd_ms,
         "algorithmic_tflop_per_step": step_flops / 1e12,
+        "timed_as": "eager launches, one HIP event pair around each kernel",
+        "hip_graph": (None if graph is None else
+                      {"ms_per_step": graph, "tflops": step_flops / (graph * 1e-3) / 1e12,
+                       "replays_checked": "bit-equal to the eager step"}),
         "lpt": {"work_items": sh.info.n_items, "item_imbalance_256cu": item_imb,
                 "kv_items": sh.info.n_kv_items, "kv_item_imbalance_256cu": kv_imb,
                 "chunk_imbalance_256bins": chunk_imb, "plan_ms": 1e3 * float(np.median(plan_times)),
@@ -588,6 +594,48 @@ def run_workload(args, workload):
         log("timing the fp64 oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(w, g, t)
     return out
+
+
+def graph_step(step, outs, args, torch):
+    """The same step captured once in a HIP graph and replayed: the time of
+    `steps` replays without per-kernel events or host launch gaps.  Every
+    output is cleared before each of three checked replays and must come back
+    bit-equal to the eager step's (the kernels are deterministic); None when
+    capture fails or a replay differs."""
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in outs]
+    try:
+        side = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                step(side)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            for x in outs:
+                x.zero_()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(x, r) for x, r in zip(outs, ref)):
+                log("graph replay differs from the eager step")
+                return None
+        for _ in range(args.warmup):
+            graph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+    except RuntimeError as exc:
+        log(f"graph capture failed ({exc})")
+        return None
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"{ms:.3f} ms/step as one HIP graph")
+    return ms
 
 
 def compare_item_plans(sh, step, kernels_lpt, args, torch):
