@@ -477,7 +477,8 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
             if (!(L[b] <= kmin && A[b] >= kend)) return false;
           return true;
         };
-        if (n_rt < (int64_t(1) << 16)) {
+        // the kernels decode the high half with a signed shift: 15 bits
+        if (n_rt < (int64_t(1) << 15)) {
           int64_t w0 = 0;
           while (w0 < n_rt && !whole(w0)) ++w0;
           int64_t w1 = w0;
@@ -509,7 +510,8 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
   // first maximal run of full-length tiles inside [max lo, min anchor) of
   // the tile's anchor blocks.  Packed as s0 | s1 << 16 in item steps (the
   // draft steps come first and are never whole); empty if the item has
-  // 2^16 steps or more.
+  // 2^15 steps or more (the kernels decode the high half with a signed
+  // shift).
   auto whole_steps = [&](const Item& it) -> int32_t {
     const int32_t b0 = it.qt * tok_per_qt / skv::kBlock;
     const int32_t b1 = std::min(g.nb, ((it.qt + 1) * tok_per_qt + skv::kBlock - 1) / skv::kBlock);
@@ -522,7 +524,7 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
     const int32_t nd = (it.flags & skv::kItemDraft)
                            ? ((b1 - b0) * skv::kBlock + skv::kTileK - 1) / skv::kTileK
                            : 0;
-    if (int64_t(nd) + (it.t1 - it.t0) >= (int64_t(1) << 16)) return 0;
+    if (int64_t(nd) + (it.t1 - it.t0) >= (int64_t(1) << 15)) return 0;
     auto whole = [&](int32_t t) {
       return tiles[t].len == skv::kTileK && tiles[t].pos >= lo_max &&
              int64_t(tiles[t].pos) + skv::kTileK <= a_min;

@@ -306,6 +306,10 @@ def test_whole_row_tiles_of_dkdv_items_need_no_mask(case):
     ("cp64_rank0_ctx512k", 2, 5, 256, {}),
     ("tiny_f32_ctx1k", 0, 1, 8, {}),
     ("tiny_f32_ctx1k", 0, 0, 3, {}),
+    # one workgroup, one anchor block near the end of a 2.1M-key context:
+    # each item has more than 2^15 steps, too many to mark
+    ("ctx32k_q2k", 5, None, 1, dict(ctx=2162688, anchor_lo=2162600, anchor_hi=2162688,
+                                    blocks_per_seq=1, hq=1, hkv=1)),
 ])
 def test_whole_step_ranges_need_no_mask(case):
     """Each item marks the run of its steps [s0, s1) that every row of its
@@ -320,7 +324,11 @@ def test_whole_step_ranges_need_no_mask(case):
     n_whole = 0
     for it in items:
         hd, qt, t0, t1, slot, flags, cost, whole = (int(x) for x in it)
+        # the kernels decode the high half with a signed shift
+        assert 0 <= whole < 2 ** 31
         s0, s1 = whole & 0xFFFF, whole >> 16
+        if t1 - t0 >= 2 ** 15:
+            assert whole == 0
         b0 = qt * tpq // BLOCK
         b1 = min(w.nb, -(-((qt + 1) * tpq) // BLOCK))
         dtok0 = b0 * BLOCK
