@@ -410,7 +410,12 @@ def main():
                     help="instead of the benchmark, run a plain elementwise copy of this many "
                          "MiB (read once, written once) three times; used to calibrate HBM "
                          "byte counters")
+    ap.add_argument("--plan-sweep", action="store_true",
+                    help="host only: time the chunk-level LPT plan (costs + placement) for "
+                         "1K-4M chunks of 256 keys on 64 and 256 bins")
     args = ap.parse_args()
+    if args.plan_sweep:
+        return plan_sweep()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -686,6 +691,35 @@ SWEEPS = {
     # fixed 32K context, draft-query budget 512 -> 4096
     "budget": [dict(blocks_per_seq=nb) for nb in (32, 64, 128, 256)],
 }
+
+
+def plan_sweep():
+    """Host time of `skv_plan_lpt` (realised tile costs of every chunk, then
+    LPT) against the chunk count: chunks of 256 keys, 512 anchor blocks
+    uniform on [L/4, L), tile 64; one JSON line."""
+    from block_sparse_split_amd import splitkv as skv
+    rng = np.random.default_rng(1)
+    points = []
+    for n in (1024, 4096, 16384, 65536, 262144, 1048576, 4194304):
+        ctx = min(n * 256, (1 << 31) - 256)
+        n = ctx // 256
+        nb = 512
+        a = np.sort(rng.choice(np.arange(ctx // 4, ctx), nb, replace=False)).astype(np.int32)
+        lo = np.zeros(nb, np.int32)
+        pos = (np.arange(n, dtype=np.int64) * 256).astype(np.int32)
+        ln = np.full(n, 256, np.int32)
+        for m in (64, 256):
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                _, _, load = skv.skv_plan_lpt(a, lo, pos, ln, 64, m)
+                ts.append(time.perf_counter() - t0)
+            points.append({"chunks": n, "bins": m, "plan_ms": 1e3 * float(np.median(ts)),
+                           "imbalance": float(load.max() / load.mean() - 1)})
+            log(f"plan: {n} chunks on {m} bins: {points[-1]['plan_ms']:.2f} ms, "
+                f"imbalance {points[-1]['imbalance']:.2e}")
+    print(json.dumps({"metric": "lpt_plan_time", "unit": "ms", "host_threads": 1,
+                      "points": points}), flush=True)
 
 
 def run_sweep(args):

@@ -67,14 +67,30 @@ void check_hip(hipError_t e, const char* what) {
     fail(SKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// Number of anchor blocks whose visible interval [lo_i, a_i) meets [t0, t1).
-int64_t pairs_visible(const int32_t* anchors, const int32_t* lo, int32_t nb,
-                      int64_t t0, int64_t t1) {
-  int64_t n = 0;
-  for (int32_t i = 0; i < nb; ++i)
-    n += std::max<int64_t>(lo[i], t0) < std::min<int64_t>(anchors[i], t1);
-  return n;
-}
+// Number of anchor blocks whose visible interval [lo_i, a_i) meets a key
+// interval [t0, t1), t0 < t1.  For a non-empty interval that holds exactly
+// when a_i > t0 and lo_i < t1, and every block with lo_i >= t1 also has
+// a_i > t0; so the count is #{a_i > t0} - #{lo_i >= t1} over the non-empty
+// intervals, two binary searches in their sorted bounds.
+struct VisibleCounter {
+  std::vector<int32_t> a, l;  // sorted anchors and starts of non-empty intervals
+  VisibleCounter(const int32_t* anchors, const int32_t* lo, int32_t nb) {
+    for (int32_t i = 0; i < nb; ++i)
+      if (lo[i] < anchors[i]) {
+        a.push_back(anchors[i]);
+        l.push_back(lo[i]);
+      }
+    std::sort(a.begin(), a.end());
+    std::sort(l.begin(), l.end());
+  }
+  int64_t operator()(int64_t t0, int64_t t1) const {
+    const auto ga = std::upper_bound(a.begin(), a.end(), t0,
+                                     [](int64_t x, int32_t y) { return x < y; });
+    const auto gl = std::lower_bound(l.begin(), l.end(), t1,
+                                     [](int32_t y, int64_t x) { return y < x; });
+    return int64_t(a.end() - ga) - int64_t(l.end() - gl);
+  }
+};
 
 void check_blocks(const int32_t* anchors, const int32_t* lo, int32_t nb) {
   require(nb >= 0, "nb must be >= 0");
@@ -89,12 +105,13 @@ void chunk_costs(const int32_t* anchors, const int32_t* lo, int32_t nb,
   check_blocks(anchors, lo, nb);
   require(n >= 0 && tile_k >= 1, "need n_chunks >= 0 and tile_k >= 1");
   require(n == 0 || (pos && len && out), "chunk arrays must not be NULL");
+  const VisibleCounter visible(anchors, lo, nb);
   for (int32_t c = 0; c < n; ++c) {
     require(len[c] >= 1 && pos[c] >= 0, "chunk_len must be >= 1, pos >= 0");
     int64_t total = 0;
     const int64_t end = int64_t(pos[c]) + len[c];
     for (int64_t t0 = pos[c]; t0 < end; t0 += tile_k)
-      total += pairs_visible(anchors, lo, nb, t0, std::min(t0 + tile_k, end));
+      total += visible(t0, std::min(t0 + tile_k, end));
     out[c] = total;
   }
 }

@@ -90,6 +90,27 @@ def test_chunk_costs_and_lpt_bit_exact_vs_oracle(name, seed):
         np.testing.assert_array_equal(cost, c_or)
 
 
+def test_chunk_costs_random_blocks_bit_exact_vs_oracle():
+    """Random visible intervals, including empty ones (lo = anchor), ones
+    that start inside a tile and unsorted blocks, against chunks of random
+    lengths and positions (overlapping, ragged) and several tile sizes."""
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        nb = int(rng.integers(0, 40))
+        L = int(rng.integers(1, 2000))
+        lo = rng.integers(0, L, size=nb)
+        an = np.minimum(lo + rng.integers(0, L // 2 + 1, size=nb), L)
+        empty = rng.random(nb) < 0.2
+        an[empty] = lo[empty]
+        n = int(rng.integers(0, 30))
+        pos = rng.integers(0, L + 50, size=n)
+        ln = rng.integers(1, 300, size=n)
+        tk = int(rng.choice([1, 7, 16, 64, 100]))
+        got = skv.skv_chunk_costs(an, lo, pos, ln, tk)
+        want = oracle.chunk_costs(an, lo, pos, ln, tk)
+        np.testing.assert_array_equal(got, want)
+
+
 def test_lpt_costs_random_bit_exact():
     rng = np.random.default_rng(0)
     for _ in range(50):
