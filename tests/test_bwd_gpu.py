@@ -267,3 +267,37 @@ def test_hip_graph_replays_match_eager():
     torch.cuda.synchronize()
     for name, x, r in zip(("O", "LSE", "dQ", "dK", "dV", "dKd", "dVd"), outs, new):
         assert torch.equal(x, r), f"replay on new Q: {name} differs from the eager step"
+
+
+def test_bwd_empty_and_draft_only_shards():
+    """Shards with no context keys: an empty shard adds exactly nothing to
+    dQ; a draft-only shard adds the draft keys' share and their gradients.
+    With every anchor at the sequence start no row sees a context key, so
+    dK and dV are exactly zero."""
+    w, g, t = _small(9, blocks_per_seq=4)
+    allc = np.arange(len(g.chunk_pos))
+    O, L, _ = oracle_fwd_bwd(w, g, t, allc, True)
+    Od = to_dev(wl.round_to_bf16(O.astype(np.float32)), "bf16")
+    Ld = torch.from_numpy(L.astype(np.float32)).cuda()
+    announce("bwd empty shard")
+    dQ, dK, dV, _, _ = gpu_bwd(w, g, t, [], False, Od, Ld, n_wg=16)
+    assert dK.shape[0] == 0 and dV.shape[0] == 0
+    assert torch.all(dQ == 0), "an empty shard must add nothing to dQ"
+    announce("bwd draft-only shard")
+    dQ, _, _, dKd, dVd = gpu_bwd(w, g, t, [], True, Od, Ld, n_wg=16)
+    _, _, (wq, _, _, wkd, wvd) = oracle_fwd_bwd(w, g, t, [], True)
+    check_grad(dQ, wq, "draft-only dQ share")
+    check_grad(dKd, wkd, "draft-only dKd")
+    check_grad(dVd, wvd, "draft-only dVd")
+    g0 = wl.Geometry(g.seq_start, g.seq_len, np.zeros_like(g.anchors), g.lo, g.ctx,
+                     g.chunk_pos, g.chunk_len)
+    O0, L0, (zq, zk, zv, zkd, zvd) = oracle_fwd_bwd(w, g0, t, allc, True)
+    announce("bwd zero anchors")
+    dQ, dK, dV, dKd, dVd = gpu_bwd(w, g0, t, allc, True,
+                                   to_dev(wl.round_to_bf16(O0.astype(np.float32)), "bf16"),
+                                   torch.from_numpy(L0.astype(np.float32)).cuda(), n_wg=16)
+    assert torch.all(dK.float() == 0) and torch.all(dV.float() == 0)
+    assert not np.any(zk) and not np.any(zv)
+    check_grad(dQ, zq, "zero anchors dQ")
+    check_grad(dKd, zkd, "zero anchors dKd")
+    check_grad(dVd, zvd, "zero anchors dVd")
