@@ -410,6 +410,10 @@ def main():
                     help="instead of the benchmark, run a plain elementwise copy of this many "
                          "MiB (read once, written once) three times; used to calibrate HBM "
                          "byte counters")
+    ap.add_argument("--wg-times", action="store_true",
+                    help="instead of the benchmark: per-workgroup start/end stamps of the "
+                         "forward, dQ and dK/dV kernels over --steps steps; realised against "
+                         "planned imbalance")
     ap.add_argument("--plan-sweep", action="store_true",
                     help="host only: time the chunk-level LPT plan (costs + placement) for "
                          "1K-4M chunks of 256 keys on 64 and 256 bins")
@@ -448,6 +452,8 @@ def main():
         return bench_tiny(args)
     if args.sweep:
         return run_sweep(args)
+    if args.wg_times:
+        return wg_balance(args)
     print(json.dumps(run_workload(args, args.workload)), flush=True)
 
 
@@ -691,6 +697,65 @@ SWEEPS = {
     # fixed 32K context, draft-query budget 512 -> 4096
     "budget": [dict(blocks_per_seq=nb) for nb in (32, 64, 128, 256)],
 }
+
+
+def wg_balance(args):
+    """Realised balance of the in-GPU plan: every workgroup of the forward,
+    dQ and dK/dV kernels stamps its start and end (100 MHz clock); per
+    kernel and step, max(duration) / mean(duration) - 1 against the plan's
+    max(load) / mean(load) - 1, and the mean duration per XCD (workgroup
+    w runs on XCD w mod 8)."""
+    import torch
+    from block_sparse_split_amd import splitkv as skv
+    from block_sparse_split_amd import shards
+    from block_sparse_split_amd import workloads as wl
+    w, g, t = wl.make(args.workload, args.seed, with_grad=True)
+    sh = skv.Shard(shards.whole_context_problem(w, g))
+    n = sh.info.n_workgroups
+    to = lambda x: torch.from_numpy(x).cuda().to(torch.bfloat16)
+    Q, K, V, Kd, Vd, dO = (to(x) for x in (t.Q, t.K, t.V, t.Kd, t.Vd, t.dO))
+    O = torch.empty((w.nq, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+    LSE = torch.empty((w.nq, w.hq), device="cuda")
+    dQ = torch.empty((w.nq, w.hq, w.d), device="cuda")
+    dK, dV, dKd, dVd = (torch.empty_like(x) for x in (K, V, Kd, Vd))
+
+    def step():
+        sh.fwd(Q, K, V, Kd, Vd, O, LSE)
+        sh.bwd(Q, K, V, Kd, Vd, O, dO, LSE, dQ, dK, dV, dKd, dVd, skv.SKV_BF16)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    clk = torch.zeros(3 * n * 2, dtype=torch.int64, device="cuda")
+    runs = []
+    skv.skv_timing_wg_clock(clk)
+    try:
+        for _ in range(args.steps):
+            step()
+            torch.cuda.synchronize()
+            runs.append(clk.view(3, n, 2).cpu().numpy().copy())
+    finally:
+        skv.skv_timing_wg_clock(None)
+    info = sh.info
+    planned = {"fwd_bf16": info.item_cost_max_bin / (info.item_cost_total / n) - 1,
+               "bwd_dq": info.item_cost_max_bin / (info.item_cost_total / n) - 1,
+               "bwd_dkdv": info.kv_cost_max_bin / (info.kv_cost_total / n) - 1}
+    out = {}
+    for k, name in enumerate(("fwd_bf16", "bwd_dq", "bwd_dkdv")):
+        dur = np.stack([r[k, :, 1] - r[k, :, 0] for r in runs]).astype(np.float64) / 100.0  # us
+        span = np.array([r[k, :, 1].max() - r[k, :, 0].min() for r in runs]) / 100.0
+        imb = dur.max(1) / dur.mean(1) - 1
+        xcd = dur.reshape(len(runs), n // 8, 8).mean((0, 1)) if n % 8 == 0 else None
+        out[name] = {"planned_imbalance": planned[name],
+                     "realized_imbalance_median": float(np.median(imb)),
+                     "realized_imbalance_runs": [float(x) for x in imb],
+                     "mean_workgroup_us": float(dur.mean()),
+                     "kernel_span_us_median": float(np.median(span)),
+                     "xcd_mean_us": None if xcd is None else [float(x) for x in xcd]}
+        log(f"{name}: planned {planned[name] * 100:.2f} %, realised "
+            f"{np.median(imb) * 100:.2f} % (median of {len(runs)}), mean {dur.mean():.1f} us")
+    print(json.dumps({"metric": "workgroup_balance", "workload": w.name, "workgroups": n,
+                      "clock": "s_memrealtime, 100 MHz", "steps": args.steps,
+                      "kernels": out}), flush=True)
 
 
 def plan_sweep():

@@ -130,6 +130,7 @@ __device__ __forceinline__ void dq_issue(const __bf16* Kg, const __bf16* Vg, int
 template <int D>
 __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   using C = DqCfg<D>;
+  const uint64_t t_wg = wg_clock_now();
   extern __shared__ __align__(16) char smem[];
   const sched_t S = sched_const(a.sched);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -292,6 +293,7 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
         }
     }
   }
+  wg_clock_record(a.wg_clock_dq, t_wg);
 }
 
 // Sum the dQ partial slots of split query tiles.
@@ -659,8 +661,10 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
 
 template <int D>
 __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  const uint64_t t_wg = wg_clock_now();
   if (threadIdx.x < 256) dkdv_role<D, true>(a);
   else dkdv_role<D, false>(a);
+  wg_clock_record(a.wg_clock_kv, t_wg);
 }
 
 template <int D>

@@ -101,6 +101,7 @@ __device__ __forceinline__ void issue_step(const __bf16* Kg, const __bf16* Vg, i
 template <int D>
 __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
+  const uint64_t t_wg = wg_clock_now();
   extern __shared__ __align__(16) char smem[];
   const sched_t S = sched_const(a.sched);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -346,6 +347,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
       }
     }
   }
+  wg_clock_record(a.wg_clock, t_wg);
 }
 
 // ---------------------------------------------------------------------------

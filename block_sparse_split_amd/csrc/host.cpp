@@ -26,6 +26,7 @@
 #include "launch.h"
 #include "schedule.h"
 #include "splitkv.h"
+#include "timing.h"
 
 namespace {
 
@@ -789,6 +790,9 @@ skv_status skv_attn_fwd_partial(const skv_problem* p, const skv_schedule_info* i
                    static_cast<char*>(workspace) +
                    align_up(int64_t(info->n_partial_slots) * skv::kQTile * p->d * 4, 256))
                          : nullptr;
+    bool fits = true;
+    a.wg_clock = a.dtype_bf16 ? skv::wg_clock_region(skv::kClockFwd, a.n_wg, &fits) : nullptr;
+    require(fits, "per-workgroup clock buffer too small for this schedule's workgroups");
     check_hip(skv::launch_fwd(a, static_cast<hipStream_t>(stream)), "forward launch");
   });
 }
@@ -860,6 +864,10 @@ skv_status skv_attn_bwd(const skv_problem* p, const skv_schedule_info* info,
     a.ws_HI = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 3 * stat_bytes);
     a.ws_dQ = reinterpret_cast<float*>(static_cast<char*>(workspace) + 4 * stat_bytes);
     a.stat_words = stat_bytes / 4;
+    bool fits = true;
+    a.wg_clock_dq = skv::wg_clock_region(skv::kClockDq, a.n_wg, &fits);
+    a.wg_clock_kv = skv::wg_clock_region(skv::kClockKv, a.n_wg, &fits);
+    require(fits, "per-workgroup clock buffer too small for this schedule's workgroups");
     check_hip(skv::launch_bwd(a, static_cast<hipStream_t>(stream)), "backward launch");
   });
 }

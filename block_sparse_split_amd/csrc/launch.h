@@ -16,6 +16,7 @@ struct FwdArgs {
   float* LSE;               // [Nq, hq]
   float* ws_O;              // partial slots [n_slots, 256, d] fp32
   float* ws_LSE;            // [n_slots, 256]
+  unsigned long long* wg_clock;  // per-workgroup (start, end) stamps, or null
   int32_t o_bf16, dtype_bf16;
   int32_t hq, hkv, d, nb, n_local;
   int32_t n_wg, n_split, n_slots;
@@ -44,6 +45,8 @@ struct BwdArgs {
   int32_t* ws_HI;           //   anchor block's lo and anchor), same layout
   float* ws_dQ;             // partial slots [n_slots, 256, d]
   int64_t stat_words;       // distance between the -D, L2, LO and HI arrays
+  unsigned long long* wg_clock_dq;  // per-workgroup (start, end) stamps, or null
+  unsigned long long* wg_clock_kv;
   int32_t grad_bf16, dtype_bf16;
   int32_t hq, hkv, d, nb, n_local;
   int32_t n_wg, n_split, n_slots, with_draft;

@@ -62,6 +62,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
+// Start and end of a workgroup on the constant-rate (100 MHz) clock, for
+// measuring the realised balance of a plan; `clk` is null unless a caller
+// asked for the stamps (then each workgroup writes its pair).
+__device__ __forceinline__ uint64_t wg_clock_now() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ void wg_clock_record(unsigned long long* clk, uint64_t t0) {
+  if (clk == nullptr) return;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    clk[2 * blockIdx.x] = t0;
+    clk[2 * blockIdx.x + 1] = t1;
+  }
+}
+
 __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();

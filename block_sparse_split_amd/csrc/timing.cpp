@@ -29,6 +29,10 @@ struct State {
 
 thread_local State g_state;
 
+// caller's buffer for per-workgroup clock stamps (device memory)
+thread_local unsigned long long* g_clock = nullptr;
+thread_local int64_t g_clock_bytes = 0;
+
 hipEvent_t get_event() {
   State& s = g_state;
   if (!s.pool.empty()) {
@@ -44,6 +48,16 @@ hipEvent_t get_event() {
 }  // namespace
 
 bool timing_on() { return g_state.on; }
+
+unsigned long long* wg_clock_region(int k, int32_t n_wg, bool* fits) {
+  *fits = true;
+  if (!g_clock) return nullptr;
+  if (g_clock_bytes < int64_t(kClockKernels) * n_wg * 16) {
+    *fits = false;
+    return nullptr;
+  }
+  return g_clock + int64_t(k) * n_wg * 2;
+}
 
 void timing_begin(const char* name, hipStream_t stream) {
   State& s = g_state;
@@ -65,6 +79,14 @@ void timing_end(hipStream_t stream) {
 }  // namespace skv
 
 extern "C" {
+
+skv_status skv_timing_wg_clock(void* buffer, int64_t bytes) {
+  if (buffer && (bytes < 0 || reinterpret_cast<uintptr_t>(buffer) % 8 != 0))
+    return SKV_ERR_INVALID_ARG;
+  skv::g_clock = static_cast<unsigned long long*>(buffer);
+  skv::g_clock_bytes = buffer ? bytes : 0;
+  return SKV_OK;
+}
 
 skv_status skv_timing_enable(int32_t on) {
   skv::g_state.on = on != 0;

@@ -92,9 +92,10 @@ def lib():
     L.skv_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int32)]
     L.skv_timing_result.argtypes = [ctypes.c_int32, ctypes.c_char_p, ctypes.c_int32, _i64p,
                                     ctypes.POINTER(ctypes.c_double)]
+    L.skv_timing_wg_clock.argtypes = [_vp, ctypes.c_int64]
     for name in ("skv_chunk_costs", "skv_plan_lpt_costs", "skv_plan_lpt", "skv_schedule_build",
                  "skv_attn_fwd_partial", "skv_merge_lse", "skv_attn_bwd", "skv_timing_enable",
-                 "skv_timing_collect", "skv_timing_result"):
+                 "skv_timing_collect", "skv_timing_result", "skv_timing_wg_clock"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -320,6 +321,16 @@ class Shard:
 
 
 # ---------------------------------------------------------------- timing
+
+def skv_timing_wg_clock(buffer=None):
+    """Set (a uint64/int64 device tensor) or clear (None) the per-workgroup
+    clock stamp buffer of the calling thread."""
+    if buffer is None:
+        _check("skv_timing_wg_clock", lib().skv_timing_wg_clock(None, 0))
+        return
+    _check("skv_timing_wg_clock", lib().skv_timing_wg_clock(
+        ctypes.c_void_p(buffer.data_ptr()), buffer.numel() * buffer.element_size()))
+
 
 def skv_timing_enable(on: bool = True):
     _check("skv_timing_enable", lib().skv_timing_enable(int(bool(on))))

@@ -248,6 +248,19 @@ skv_status skv_timing_collect(int32_t* n_kernels);
 skv_status skv_timing_result(int32_t k, char* name, int32_t name_cap, int64_t* launches,
                              double* total_ms);
 
+/* Per-workgroup clock stamps, for measuring how evenly a plan's work lands
+ * on the workgroups (the pages' load-balance claim, measured rather than
+ * planned).  While `buffer` (device memory, 8-byte aligned, owned by the
+ * caller) is set on the calling thread, the bf16 forward, dQ and dK/dV
+ * kernels each write, per workgroup w, the pair (start, end) of the GPU's
+ * constant 100 MHz clock as two uint64 at [2w, 2w + 1] of their region:
+ * forward at 0, dQ at 2 n_wg, dK/dV at 4 n_wg (n_wg = the schedule's
+ * workgroup count).  Each launch overwrites its region.  NULL turns it off
+ * (the default).  A device call whose n_wg needs more than `bytes`
+ * (3 * n_wg * 16) fails with SKV_ERR_INVALID_ARG before launching.
+ * Errors: SKV_ERR_INVALID_ARG for a misaligned buffer or negative bytes. */
+skv_status skv_timing_wg_clock(void* buffer, int64_t bytes);
+
 #ifdef __cplusplus
 }
 #endif

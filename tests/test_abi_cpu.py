@@ -1,6 +1,7 @@
 """CPU checks of the C-ABI library: exports, argument errors, the planner
 (bit-exact against the oracle) and the in-GPU schedule (coverage and LPT
 placement re-derived with the oracle).  No device call is made here."""
+import ctypes
 import os
 import re
 import subprocess
@@ -109,6 +110,13 @@ def test_chunk_costs_random_blocks_bit_exact_vs_oracle():
         got = skv.skv_chunk_costs(an, lo, pos, ln, tk)
         want = oracle.chunk_costs(an, lo, pos, ln, tk)
         np.testing.assert_array_equal(got, want)
+
+
+def test_workgroup_clock_buffer_arguments():
+    L = skv.lib()
+    assert L.skv_timing_wg_clock(ctypes.c_void_p(8 * 1000 + 4), 64) == -1  # misaligned
+    assert L.skv_timing_wg_clock(ctypes.c_void_p(8 * 1000), -1) == -1
+    assert L.skv_timing_wg_clock(None, 0) == 0  # off (no device access either way)
 
 
 def test_lpt_costs_random_bit_exact():

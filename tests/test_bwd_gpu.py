@@ -301,3 +301,46 @@ def test_bwd_empty_and_draft_only_shards():
     check_grad(dQ, zq, "zero anchors dQ")
     check_grad(dKd, zkd, "zero anchors dKd")
     check_grad(dVd, zvd, "zero anchors dVd")
+
+
+def test_workgroup_clock_stamps():
+    """With a per-workgroup clock buffer set, the forward, dQ and dK/dV
+    kernels stamp every workgroup (start <= end) and compute the same bits;
+    a buffer too small for the schedule is refused before any launch."""
+    w, g, t = _small(8, blocks_per_seq=16)
+    prob = shards.whole_context_problem(w, g)
+    sh = skv.Shard(prob, n_workgroups=40)
+    dt = w.dtype
+    Q, K, V = to_dev(t.Q, dt), to_dev(t.K, dt), to_dev(t.V, dt)
+    Kd, Vd, dO = to_dev(t.Kd, dt), to_dev(t.Vd, dt), to_dev(t.dO, dt)
+
+    def step():
+        O = torch.empty((w.nq, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+        LSE = torch.empty((w.nq, w.hq), device="cuda")
+        dQ = torch.empty((w.nq, w.hq, w.d), device="cuda")
+        dK, dV = torch.empty_like(K), torch.empty_like(V)
+        dKd, dVd = torch.empty_like(Kd), torch.empty_like(Vd)
+        sh.fwd(Q, K, V, Kd, Vd, O, LSE)
+        sh.bwd(Q, K, V, Kd, Vd, O, dO, LSE, dQ, dK, dV, dKd, dVd, skv.SKV_BF16)
+        torch.cuda.synchronize()
+        return O, LSE, dQ, dK, dV, dKd, dVd
+
+    announce("workgroup clock stamps, 40 workgroups")
+    ref = step()
+    clk = torch.zeros(3 * 40 * 2, dtype=torch.int64, device="cuda")
+    skv.skv_timing_wg_clock(clk)
+    try:
+        got = step()
+        small = torch.zeros(3 * 39 * 2, dtype=torch.int64, device="cuda")
+        skv.skv_timing_wg_clock(small)
+        with pytest.raises(skv.SplitKVError):
+            step()
+    finally:
+        skv.skv_timing_wg_clock(None)
+    for x, r in zip(got, ref):
+        assert torch.equal(x, r)
+    st = clk.view(3, 40, 2).cpu().numpy()
+    assert np.all(st[:, :, 0] > 0) and np.all(st[:, :, 1] >= st[:, :, 0])
+    # the three kernels run one after another on the stream
+    assert st[0, :, 1].max() <= st[1, :, 0].min() + 1
+    assert st[1, :, 1].max() <= st[2, :, 0].min() + 1
