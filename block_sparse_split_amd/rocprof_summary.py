@@ -101,7 +101,7 @@ def cmd_kernels(a):
                 continue
             b = bench.get(name)
             out.append(f"{name:<14} {len(d):>6} {sum(d) / len(d) / 1e6:>9.4f} "
-                       f"{b if b is None else f'{b:.4f}':>13}")
+                       f"{'-' if b is None else f'{b:.4f}':>13}")
     emit("\n".join(out) + "\n", a.out)
 
 
