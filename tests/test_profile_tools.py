@@ -52,3 +52,28 @@ def test_counters_summary_derived_values(tmp_path, monkeypatch):
     assert got == {"mfma_busy": 0.5, "mfma_valu_coexec": 0.25, "clock_ghz": 2.0}
     # a summary taken on other kernel sources is not reported
     assert bench.mfma_counters_for("bwd_dkdv", "w", "0" * 64) is None
+
+
+def test_kernels_summary_without_bench_figures(tmp_path):
+    """Kernel statistics beside a bench record that has no per-kernel
+    figures (the 1M merge workload's): the column shows '-'."""
+    stats = tmp_path / "stats.csv"
+    trace = tmp_path / "trace.csv"
+    name = "void skv::(anonymous namespace)::fwd_bf16_kernel<128>(skv::FwdArgs)"
+    with open(stats, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs",
+                    "MaxNs", "StdDev"])
+        w.writerow([name, 3, 3_000_000, 1_000_000.0, 100.0, 900_000, 1_100_000, 1.0])
+    with open(trace, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        for i, dur in enumerate((1_100_000, 1_000_000, 900_000)):
+            w.writerow([name, 10_000_000 * i, 10_000_000 * i + dur])
+    bench_json = tmp_path / "b.json"
+    bench_json.write_text('{"metric": "m", "value": 1.0}\n')
+    out = tmp_path / "k.txt"
+    rs.main(["kernels", str(stats), "--trace", str(trace), "--skip-first", "1",
+             "--bench-json", str(bench_json), "--command", "cmd", "--out", str(out)])
+    row = [l.split() for l in out.read_text().splitlines() if l.startswith("fwd_bf16")][-1]
+    assert row == ["fwd_bf16", "2", "0.9500", "-"]
