@@ -257,7 +257,9 @@ skv_status skv_timing_result(int32_t k, char* name, int32_t name_cap, int64_t* l
  * forward at 0, dQ at 2 n_wg, dK/dV at 4 n_wg (n_wg = the schedule's
  * workgroup count).  Each launch overwrites its region.  NULL turns it off
  * (the default).  A device call whose n_wg needs more than `bytes`
- * (3 * n_wg * 16) fails with SKV_ERR_INVALID_ARG before launching.
+ * (3 * n_wg * 16) fails with SKV_ERR_INVALID_ARG before launching.  The
+ * buffer must stay allocated until it is cleared (NULL) or replaced: the
+ * library keeps only the pointer.  Launches on other threads do not see it.
  * Errors: SKV_ERR_INVALID_ARG for a misaligned buffer or negative bytes. */
 skv_status skv_timing_wg_clock(void* buffer, int64_t bytes);
 
