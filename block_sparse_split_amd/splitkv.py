@@ -9,6 +9,7 @@ raises: there is no fallback path.
 from __future__ import annotations
 
 import ctypes
+import threading
 import os
 from typing import Optional
 
@@ -322,14 +323,20 @@ class Shard:
 
 # ---------------------------------------------------------------- timing
 
+_wg_clock_keep = threading.local()
+
+
 def skv_timing_wg_clock(buffer=None):
     """Set (a uint64/int64 device tensor) or clear (None) the per-workgroup
-    clock stamp buffer of the calling thread."""
+    clock stamp buffer of the calling thread.  The tensor is kept alive
+    here while it is set, since the library holds only its pointer."""
     if buffer is None:
         _check("skv_timing_wg_clock", lib().skv_timing_wg_clock(None, 0))
+        _wg_clock_keep.buf = None
         return
     _check("skv_timing_wg_clock", lib().skv_timing_wg_clock(
         ctypes.c_void_p(buffer.data_ptr()), buffer.numel() * buffer.element_size()))
+    _wg_clock_keep.buf = buffer
 
 
 def skv_timing_enable(on: bool = True):
