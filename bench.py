@@ -699,6 +699,28 @@ SWEEPS = {
 }
 
 
+def balance_stats(runs, planned):
+    """Per kernel (forward, dQ, dK/dV = index 0, 1, 2 of each run's
+    [3, n_wg, 2] array of (start, end) stamps in 100 MHz ticks): workgroup
+    durations in us, max/mean - 1 per run and its median, the span from the
+    first start to the last end, and the mean duration per XCD class
+    (workgroup w on XCD w mod 8, when n_wg is a multiple of 8)."""
+    out = {}
+    n = runs[0].shape[1]
+    for k, name in enumerate(("fwd_bf16", "bwd_dq", "bwd_dkdv")):
+        dur = np.stack([r[k, :, 1] - r[k, :, 0] for r in runs]).astype(np.float64) / 100.0
+        span = np.array([r[k, :, 1].max() - r[k, :, 0].min() for r in runs]) / 100.0
+        imb = dur.max(1) / dur.mean(1) - 1
+        xcd = dur.reshape(len(runs), n // 8, 8).mean((0, 1)) if n % 8 == 0 else None
+        out[name] = {"planned_imbalance": planned[name],
+                     "realized_imbalance_median": float(np.median(imb)),
+                     "realized_imbalance_runs": [float(x) for x in imb],
+                     "mean_workgroup_us": float(dur.mean()),
+                     "kernel_span_us_median": float(np.median(span)),
+                     "xcd_mean_us": None if xcd is None else [float(x) for x in xcd]}
+    return out
+
+
 def wg_balance(args):
     """Realised balance of the in-GPU plan: every workgroup of the forward,
     dQ and dK/dV kernels stamps its start and end (100 MHz clock); per
@@ -739,20 +761,11 @@ def wg_balance(args):
     planned = {"fwd_bf16": info.item_cost_max_bin / (info.item_cost_total / n) - 1,
                "bwd_dq": info.item_cost_max_bin / (info.item_cost_total / n) - 1,
                "bwd_dkdv": info.kv_cost_max_bin / (info.kv_cost_total / n) - 1}
-    out = {}
-    for k, name in enumerate(("fwd_bf16", "bwd_dq", "bwd_dkdv")):
-        dur = np.stack([r[k, :, 1] - r[k, :, 0] for r in runs]).astype(np.float64) / 100.0  # us
-        span = np.array([r[k, :, 1].max() - r[k, :, 0].min() for r in runs]) / 100.0
-        imb = dur.max(1) / dur.mean(1) - 1
-        xcd = dur.reshape(len(runs), n // 8, 8).mean((0, 1)) if n % 8 == 0 else None
-        out[name] = {"planned_imbalance": planned[name],
-                     "realized_imbalance_median": float(np.median(imb)),
-                     "realized_imbalance_runs": [float(x) for x in imb],
-                     "mean_workgroup_us": float(dur.mean()),
-                     "kernel_span_us_median": float(np.median(span)),
-                     "xcd_mean_us": None if xcd is None else [float(x) for x in xcd]}
-        log(f"{name}: planned {planned[name] * 100:.2f} %, realised "
-            f"{np.median(imb) * 100:.2f} % (median of {len(runs)}), mean {dur.mean():.1f} us")
+    out = balance_stats(runs, planned)
+    for name, v in out.items():
+        log(f"{name}: planned {v['planned_imbalance'] * 100:.2f} %, realised "
+            f"{v['realized_imbalance_median'] * 100:.2f} % (median of {len(runs)}), "
+            f"mean {v['mean_workgroup_us']:.1f} us")
     print(json.dumps({"metric": "workgroup_balance", "workload": w.name, "workgroups": n,
                       "clock": "s_memrealtime, 100 MHz", "steps": args.steps,
                       "kernels": out}), flush=True)

@@ -36,3 +36,29 @@ def test_plan_imbalances_match_oracle(name, scale):
         assert got[str(m)]["contiguous"] == planner.imbalance(cont)
         # LPT never does worse than the contiguous split here
         assert got[str(m)]["lpt"] <= got[str(m)]["contiguous"]
+
+
+def test_balance_stats_from_workgroup_stamps():
+    """Synthetic stamps: 16 workgroups, XCD class 3 runs 10 % longer; the
+    realised imbalance, span and per-XCD means follow by hand."""
+    import bench
+    n = 16
+    runs = []
+    for shift in (0, 1000):
+        r = np.zeros((3, n, 2), np.int64)
+        for k in range(3):
+            for w in range(n):
+                d = 1100 if w % 8 == 3 else 1000          # ticks (10 / 11 us)
+                r[k, w] = (shift + 5 * w, shift + 5 * w + d)
+        runs.append(r)
+    planned = {"fwd_bf16": 0.01, "bwd_dq": 0.02, "bwd_dkdv": 0.03}
+    out = bench.balance_stats(runs, planned)
+    mean = (14 * 10.0 + 2 * 11.0) / 16
+    for name in planned:
+        v = out[name]
+        assert v["planned_imbalance"] == planned[name]
+        assert abs(v["realized_imbalance_median"] - (11.0 / mean - 1)) < 1e-12
+        assert abs(v["mean_workgroup_us"] - mean) < 1e-12
+        # last end: workgroup 11 (class 3) at 5 * 11 + 1100 ticks
+        assert abs(v["kernel_span_us_median"] - (55 + 1100) / 100.0) < 1e-12
+        assert v["xcd_mean_us"] == [10.0, 10.0, 10.0, 11.0, 10.0, 10.0, 10.0, 10.0]
