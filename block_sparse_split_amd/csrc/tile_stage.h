@@ -55,11 +55,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// s_waitcnt vmcnt(n) (n < 16), leaving lgkmcnt/expcnt alone.
+// s_waitcnt vmcnt(n) (n < 64: bits 3:0 and 15:14 of the immediate), leaving
+// lgkmcnt/expcnt alone.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Start and end of a workgroup on the constant-rate (100 MHz) clock, for
