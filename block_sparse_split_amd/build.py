@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsplitkv.so")
-SOURCES = ["host.cpp", "timing.cpp", "fwd.hip", "merge.hip", "bwd.hip"]
+SOURCES = ["host.cpp", "timing.cpp", "fwd.hip", "merge.hip", "bwd.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -797,6 +797,26 @@ skv_status skv_attn_fwd_partial(const skv_problem* p, const skv_schedule_info* i
   });
 }
 
+skv_status skv_attn_fwd_partial_noalloc(const skv_problem* p, const skv_schedule_info* info,
+                                        const int32_t* schedule, const void* Q, const void* K,
+                                        const void* V, const void* Kd, const void* Vd, void* O,
+                                        int32_t o_dtype, float* LSE, void* stream) {
+  void* scratch = nullptr;
+  const skv_status st = guarded([&] {
+    require(info != nullptr, "info must not be NULL");
+    if (info->fwd_workspace_bytes > skv::kNoAllocScratchBytes)
+      fail(SKV_ERR_WORKSPACE,
+           "this schedule needs " + std::to_string(info->fwd_workspace_bytes) +
+               " bytes of forward workspace; the allocation-free forward holds at most " +
+               std::to_string(skv::kNoAllocScratchBytes) +
+               " (use skv_attn_fwd_partial with a workspace)");
+    check_hip(skv::noalloc_scratch(&scratch), "hipGetSymbolAddress(scratch)");
+  });
+  if (st != SKV_OK) return st;
+  return skv_attn_fwd_partial(p, info, schedule, Q, K, V, Kd, Vd, O, o_dtype, LSE, scratch,
+                              skv::kNoAllocScratchBytes, stream);
+}
+
 skv_status skv_merge_lse(int32_t n_parts, int64_t rows, int32_t d, const void* O_parts,
                          int32_t in_dtype, const float* LSE_parts, void* O_out,
                          int32_t out_dtype, float* LSE_out, void* stream) {

@@ -54,6 +54,11 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+// Scratch of skv_attn_fwd_partial_noalloc: a static device array of this
+// size; *out gets the current device's copy.
+constexpr int64_t kNoAllocScratchBytes = int64_t(64) << 20;
+hipError_t noalloc_scratch(void** out);
 hipError_t launch_merge(int32_t n_parts, int64_t rows, int32_t d, const void* O_parts,
                         bool in_bf16, const float* LSE_parts, void* O_out, bool out_bf16,
                         float* LSE_out, hipStream_t stream);

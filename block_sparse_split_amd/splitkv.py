@@ -81,6 +81,10 @@ def lib():
                                        ctypes.POINTER(SkvScheduleInfo), _vp, _vp, _vp, _vp,
                                        _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int64,
                                        _vp]
+    L.skv_attn_fwd_partial_noalloc.argtypes = [ctypes.POINTER(SkvProblem),
+                                               ctypes.POINTER(SkvScheduleInfo), _vp, _vp,
+                                               _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp,
+                                               _vp]
     L.skv_merge_lse.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _vp,
                                 ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, _vp]
     L.skv_attn_bwd.argtypes = [ctypes.POINTER(SkvProblem), ctypes.POINTER(SkvScheduleInfo),
@@ -95,7 +99,7 @@ def lib():
                                     ctypes.POINTER(ctypes.c_double)]
     L.skv_timing_wg_clock.argtypes = [_vp, ctypes.c_int64]
     for name in ("skv_chunk_costs", "skv_plan_lpt_costs", "skv_plan_lpt", "skv_schedule_build",
-                 "skv_attn_fwd_partial", "skv_merge_lse", "skv_attn_bwd", "skv_timing_enable",
+                 "skv_attn_fwd_partial", "skv_attn_fwd_partial_noalloc", "skv_merge_lse", "skv_attn_bwd", "skv_timing_enable",
                  "skv_timing_collect", "skv_timing_result", "skv_timing_wg_clock"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -257,6 +261,25 @@ def skv_attn_fwd_partial(problem: Problem, info, schedule, Q, K, V, Kd, Vd, O, L
     _check("skv_attn_fwd_partial", lib().skv_attn_fwd_partial(*args))
 
 
+def skv_attn_fwd_partial_noalloc(problem: Problem, info, schedule, Q, K, V, Kd, Vd, O, LSE,
+                                 stream=None):
+    torch = _torch()
+    p = problem.c
+    dt = _tdtype(problem.dtype)
+    nq, nl = problem.nq, problem.n_local
+    nd = not p.with_draft
+    _check("skv_attn_fwd_partial_noalloc", lib().skv_attn_fwd_partial_noalloc(
+        ctypes.byref(p), ctypes.byref(info),
+        _ptr(schedule, "schedule", torch.int32, (info.words,)),
+        _ptr(Q, "Q", dt, (nq, p.hq, p.d)),
+        _ptr(K, "K", dt, (nl, p.hkv, p.d), allow_none=nl == 0),
+        _ptr(V, "V", dt, (nl, p.hkv, p.d), allow_none=nl == 0),
+        None if nd else _ptr(Kd, "Kd", dt, (nq, p.hkv, p.d)),
+        None if nd else _ptr(Vd, "Vd", dt, (nq, p.hkv, p.d)),
+        _ptr(O, "O", None, (nq, p.hq, p.d)), _dtype_code(O),
+        _ptr(LSE, "LSE", torch.float32, (nq, p.hq)), _stream(stream)))
+
+
 def skv_merge_lse(O_parts, LSE_parts, O_out, LSE_out, stream=None):
     torch = _torch()
     k = O_parts.shape[0]
@@ -314,6 +337,10 @@ class Shard:
     def fwd(self, Q, K, V, Kd, Vd, O, LSE, stream=None):
         skv_attn_fwd_partial(self.problem, self.info, self.schedule, Q, K, V, Kd, Vd, O, LSE,
                              self.workspace, stream)
+
+    def fwd_noalloc(self, Q, K, V, Kd, Vd, O, LSE, stream=None):
+        skv_attn_fwd_partial_noalloc(self.problem, self.info, self.schedule, Q, K, V, Kd, Vd, O,
+                                     LSE, stream)
 
     def bwd(self, Q, K, V, Kd, Vd, O, dO, LSE, dQ, dK, dV, dKd, dVd, grad_dtype=SKV_F32,
             stream=None):

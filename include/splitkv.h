@@ -29,7 +29,9 @@
  *     calling thread.  No call aborts the process.
  *   - Device pointers are HIP device addresses.  The caller owns every
  *     buffer; the library allocates no device memory.  Scratch space is the
- *     caller's `workspace` of the size the schedule reports.
+ *     caller's `workspace` of the size the schedule reports, except for
+ *     skv_attn_fwd_partial_noalloc, whose scratch is a static array of the
+ *     library's code object.
  *   - Device calls are asynchronous on the caller's stream (`stream` is a
  *     hipStream_t passed as void*; NULL is the default stream).  Launch
  *     errors are returned as SKV_ERR_HIP.  Host calls are synchronous.
@@ -42,8 +44,10 @@
  *       Kd, Vd, dKd... [Nq, hkv, d]      (draft-block keys/values)
  *   - dtypes: SKV_BF16 (bfloat16) or SKV_F32.  d is 64 or 128.  hq must be
  *     a multiple of hkv with hq / hkv in {1, 2, 4, 8, 16}.
- *   - The library keeps no state across calls except a per-device cache of
- *     the compute-unit count; it is safe to call from several threads.
+ *   - The library keeps no state across calls except per-device caches of
+ *     the compute-unit count and of the static scratch array's address; it is
+ *     safe to call from several threads (skv_attn_fwd_partial_noalloc: see
+ *     there).
  */
 #ifndef SPLITKV_H
 #define SPLITKV_H
@@ -194,6 +198,26 @@ skv_status skv_attn_fwd_partial(const skv_problem* p,
                                 const void* Vd, void* O, int32_t o_dtype,
                                 float* LSE, void* workspace,
                                 int64_t workspace_bytes, void* stream);
+
+/* skv_attn_fwd_partial without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The partial slots of split query tiles
+ * live in a static device array of the library: 64 MiB on each GPU the
+ * library runs on, held from the first call on that GPU until the process
+ * ends.  A schedule whose info->fwd_workspace_bytes exceeds 64 MiB is refused
+ * with SKV_ERR_WORKSPACE before anything is launched.  The call uses the
+ * current device's copy (stream must belong to the current device); nothing
+ * in it needs to start at zero.  Every call on one GPU shares that copy, so
+ * calls that overlap on one GPU (from other threads or on other streams) race
+ * on it and must be serialised by the caller.  Other arguments, results and
+ * errors as skv_attn_fwd_partial; SKV_ERR_HIP if the array's address cannot
+ * be looked up. */
+skv_status skv_attn_fwd_partial_noalloc(const skv_problem* p,
+                                        const skv_schedule_info* info,
+                                        const int32_t* schedule, const void* Q,
+                                        const void* K, const void* V,
+                                        const void* Kd, const void* Vd, void* O,
+                                        int32_t o_dtype, float* LSE, void* stream);
 
 /* Exact merge of n_parts partial results (rit.work blog, section "Split-KV
  * moves queries, not keys and values": participants reconcile the

@@ -546,3 +546,20 @@ def test_device_calls_reject_bad_dtypes_before_launch():
     st = L.skv_attn_fwd_partial(ctypes.byref(p1.c), ctypes.byref(i1), fake, fake, fake, fake,
                                 fake, fake, fake, 1, fake, fake, 16, None)
     assert st == -4
+
+
+def test_noalloc_forward_refuses_oversized_workspace_before_any_device_call():
+    """The allocation-free forward holds 64 MiB of scratch; a schedule that
+    needs more is refused with SKV_ERR_WORKSPACE and a message that names both
+    sizes, before the library touches the device."""
+    w, g, _ = wl.make("ctx32k_q2k", 1, tensors=False)
+    prob = shards.whole_context_problem(w, g)
+    _, info = skv.skv_schedule_build(prob, 256)
+    assert info.fwd_workspace_bytes <= 64 << 20
+    info.fwd_workspace_bytes = (64 << 20) + 256
+    L = skv.lib()
+    st = L.skv_attn_fwd_partial_noalloc(ctypes.byref(prob.c), ctypes.byref(info), None, None,
+                                        None, None, None, None, None, skv.SKV_BF16, None, None)
+    assert st == -4
+    msg = L.skv_last_error().decode()
+    assert str((64 << 20) + 256) in msg and str(64 << 20) in msg
