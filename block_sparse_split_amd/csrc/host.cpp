@@ -205,6 +205,9 @@ Geometry check_problem(const skv_problem* p) {
     for (int32_t c = 0; c < p->n_chunks; ++c) {
       require(p->chunk_off[c + 1] > p->chunk_off[c], "chunks must hold >= 1 key");
       require(p->chunk_pos[c] >= 0, "chunk_pos must be >= 0");
+      // key positions are int32 in the schedule and the kernels
+      require(int64_t(p->chunk_pos[c]) + (p->chunk_off[c + 1] - p->chunk_off[c]) <= INT32_MAX,
+              "chunk_pos + chunk length must not exceed INT32_MAX");
     }
     g.n_local = p->chunk_off[p->n_chunks];
   }

@@ -83,6 +83,17 @@ extern "C" {
 skv_status skv_timing_wg_clock(void* buffer, int64_t bytes) {
   if (buffer && (bytes < 0 || reinterpret_cast<uintptr_t>(buffer) % 8 != 0))
     return SKV_ERR_INVALID_ARG;
+  if (buffer) {
+    // the kernels store to it: refuse anything but device (or managed) memory
+    hipPointerAttribute_t attr{};
+    const hipError_t e = hipPointerGetAttributes(&attr, buffer);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();  // leave no error for a later launch check to find
+      return SKV_ERR_INVALID_ARG;
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+      return SKV_ERR_INVALID_ARG;
+  }
   skv::g_clock = static_cast<unsigned long long*>(buffer);
   skv::g_clock_bytes = buffer ? bytes : 0;
   return SKV_OK;

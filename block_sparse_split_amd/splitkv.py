@@ -361,8 +361,14 @@ def skv_timing_wg_clock(buffer=None):
         _check("skv_timing_wg_clock", lib().skv_timing_wg_clock(None, 0))
         _wg_clock_keep.buf = None
         return
+    torch = _torch()
+    if buffer.dtype not in (torch.int64, torch.uint64):
+        raise ValueError(f"buffer must be int64 or uint64, got {buffer.dtype}")
+    ptr = _ptr(buffer, "buffer")  # device tensor, contiguous
+    if ptr is None:
+        raise ValueError("buffer must not be empty")
     _check("skv_timing_wg_clock", lib().skv_timing_wg_clock(
-        ctypes.c_void_p(buffer.data_ptr()), buffer.numel() * buffer.element_size()))
+        ptr, buffer.numel() * buffer.element_size()))
     _wg_clock_keep.buf = buffer
 
 

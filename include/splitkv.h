@@ -284,7 +284,8 @@ skv_status skv_timing_result(int32_t k, char* name, int32_t name_cap, int64_t* l
  * (3 * n_wg * 16) fails with SKV_ERR_INVALID_ARG before launching.  The
  * buffer must stay allocated until it is cleared (NULL) or replaced: the
  * library keeps only the pointer.  Launches on other threads do not see it.
- * Errors: SKV_ERR_INVALID_ARG for a misaligned buffer or negative bytes. */
+ * Errors: SKV_ERR_INVALID_ARG for a misaligned buffer, negative bytes or a
+ * pointer that is not device (or managed) memory. */
 skv_status skv_timing_wg_clock(void* buffer, int64_t bytes);
 
 #ifdef __cplusplus

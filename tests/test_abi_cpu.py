@@ -55,6 +55,8 @@ def test_invalid_arguments_return_status_codes():
     for bad, status in [(dict(hq=3), -1), (dict(hq=6, hkv=2), -2), (dict(d=96), -2),
                         (dict(scale=0.0), -1), (dict(dtype=7), -2),
                         (dict(chunk_off=[1, 64]), -1),
+                        # a chunk whose last key lies past INT32_MAX
+                        (dict(chunk_pos=[2**31 - 32]), -1),
                         (dict(chunk_pos=[0, 32], chunk_off=[0, 64, 128]), -1)]:
         kw = dict(base, **bad)
         with pytest.raises(skv.SplitKVError) as e:
@@ -117,6 +119,13 @@ def test_workgroup_clock_buffer_arguments():
     assert L.skv_timing_wg_clock(ctypes.c_void_p(8 * 1000 + 4), 64) == -1  # misaligned
     assert L.skv_timing_wg_clock(ctypes.c_void_p(8 * 1000), -1) == -1
     assert L.skv_timing_wg_clock(None, 0) == 0  # off (no device access either way)
+    # a host pointer is refused (the kernels would store to it)
+    host = (ctypes.c_uint64 * 64)()
+    assert L.skv_timing_wg_clock(ctypes.cast(host, ctypes.c_void_p), 512) == -1
+    assert L.skv_timing_wg_clock(None, 0) == 0
+    import torch
+    with pytest.raises(ValueError):
+        skv.skv_timing_wg_clock(torch.zeros(64, dtype=torch.int64))  # not a device tensor
 
 
 def test_lpt_costs_random_bit_exact():
