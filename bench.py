@@ -70,6 +70,38 @@ def shard_visible_elements(g, hq, chunk_ids, with_draft):
     return (int(keys) + (16 * len(g.anchors) if with_draft else 0)) * 16 * hq
 
 
+def item_pair_loads(image, g, w):
+    """Each workgroup's forward items counted in the chunk planner's unit,
+    not the schedule's time units: the (anchor block, 64-key tile) pairs of
+    the item's tiles that the block sees, plus one pair per anchor block of
+    the query tile for its draft tile.  Returns the per-workgroup loads."""
+    from block_sparse_split_amd.csrc_layout import H, I, T_WORDS, I_WORDS, QTILE, BLOCK
+    h = {k: int(image[v]) for k, v in H.items()}
+    tiles = image[h["OFF_TILES"]: h["OFF_TILES"] + h["NTILES"] * T_WORDS].reshape(-1, T_WORDS)
+    items = image[h["OFF_ITEMS"]: h["OFF_ITEMS"] + h["NITEMS"] * I_WORDS].reshape(-1, I_WORDS)
+    qoff = image[h["OFF_QOFF"]: h["OFF_QOFF"] + h["NWG"] + 1]
+    queue = image[h["OFF_QUEUE"]: h["OFF_QUEUE"] + h["NITEMS"]]
+    G = w.hq // w.hkv
+    tpq = QTILE // G
+    pos = tiles[:, 1].astype(np.int64)
+    end = pos + tiles[:, 2]
+    cum = {}
+    pairs = np.zeros(len(items), np.int64)
+    for i, it in enumerate(items):
+        qt = int(it[I["QT"]])
+        b0 = qt * tpq // BLOCK
+        b1 = min(w.nb, -(-((qt + 1) * tpq) // BLOCK))
+        if qt not in cum:
+            a = g.anchors[b0:b1, None].astype(np.int64)
+            lo = g.lo[b0:b1, None].astype(np.int64)
+            seen = (np.maximum(lo, pos[None]) < np.minimum(a, end[None])).sum(0)
+            cum[qt] = np.concatenate([[0], np.cumsum(seen)])
+        pairs[i] = cum[qt][int(it[I["T1"]])] - cum[qt][int(it[I["T0"]])]
+        if int(it[I["FLAGS"]]) & 1:
+            pairs[i] += b1 - b0
+    return np.array([pairs[queue[qoff[k]:qoff[k + 1]]].sum() for k in range(h["NWG"])])
+
+
 def cpu_baseline(w, g, t, target_s=15.0):
     """The fp64 oracle (as it stands) on a bounded sample of anchor blocks,
     forward + backward, timed on this host's cores."""
@@ -556,6 +588,8 @@ def run_workload(args, workload):
     roof["traffic"] = traffic_for(dom, w.name, kernel_source_hash())
     roof["counters"] = mfma_counters_for(dom, w.name, kernel_source_hash())
 
+    realized = realized_balance(step, sh.info, 5, torch, args.fwd_only)
+    pair_loads = item_pair_loads(sh.image, g, w)
     fwd_ms = sum(kernels[k][1] for k in ("fwd_bf16", "merge_split") if k in kernels) / args.steps
     value = step_flops / (ms * 1e-3) / 1e12
     item_imb = sh.info.item_cost_max_bin / (sh.info.item_cost_total / n_wg) - 1
@@ -588,9 +622,15 @@ def run_workload(args, workload):
                       {"ms_per_step": graph, "tflops": step_flops / (graph * 1e-3) / 1e12,
                        "replays_checked": "bit-equal to the eager step"}),
         "lpt": {"work_items": sh.info.n_items, "item_imbalance_256cu": item_imb,
+                "item_cost_unit": "time units fitted to measured workgroup times",
+                "item_pair_imbalance_256cu": float(pair_loads.max() / pair_loads.mean() - 1),
                 "kv_items": sh.info.n_kv_items, "kv_item_imbalance_256cu": kv_imb,
                 "chunk_imbalance_256bins": chunk_imb, "plan_ms": 1e3 * float(np.median(plan_times)),
-                "workgroups": n_wg},
+                "workgroups": n_wg,
+                "realized": {k: {"imbalance_median": v["realized_imbalance_median"],
+                                 "on_xcd_w_mod_8": v["on_xcd_w_mod_8"],
+                                 "xcd_mean_us": v["xcd_mean_us"]}
+                             for k, v in realized.items()}},
         "kernels": per_kernel,
         "roofline": roof,
         "cpu_baseline": None,
@@ -699,26 +739,59 @@ SWEEPS = {
 }
 
 
-def balance_stats(runs, planned):
+def balance_stats(runs, planned, names=("fwd_bf16", "bwd_dq", "bwd_dkdv")):
     """Per kernel (forward, dQ, dK/dV = index 0, 1, 2 of each run's
-    [3, n_wg, 2] array of (start, end) stamps in 100 MHz ticks): workgroup
-    durations in us, max/mean - 1 per run and its median, the span from the
-    first start to the last end, and the mean duration per XCD class
-    (workgroup w on XCD w mod 8, when n_wg is a multiple of 8)."""
+    [3, n_wg, 4] array of (start, end, XCC_ID, HW_ID) words, stamps in
+    100 MHz ticks): workgroup durations in us, max/mean - 1 per run and its
+    median, the span from the first start to the last end, the mean
+    duration per XCD as the XCC_ID register reports it, the share of
+    workgroups w that ran on XCD w mod 8 (the placement the plan assumes)
+    and the number of distinct compute units (XCD, SE, CU) used."""
     out = {}
     n = runs[0].shape[1]
     for k, name in enumerate(("fwd_bf16", "bwd_dq", "bwd_dkdv")):
+        if name not in names:
+            continue
         dur = np.stack([r[k, :, 1] - r[k, :, 0] for r in runs]).astype(np.float64) / 100.0
         span = np.array([r[k, :, 1].max() - r[k, :, 0].min() for r in runs]) / 100.0
         imb = dur.max(1) / dur.mean(1) - 1
-        xcd = dur.reshape(len(runs), n // 8, 8).mean((0, 1)) if n % 8 == 0 else None
+        xcc = np.stack([r[k, :, 2] & 15 for r in runs])
+        hw = np.stack([r[k, :, 3] for r in runs])
+        cu = (xcc << 8) | (((hw >> 13) & 7) << 4) | ((hw >> 8) & 15)
+        xcd_mean = [float(dur[xcc == x].mean()) if np.any(xcc == x) else None for x in range(8)]
         out[name] = {"planned_imbalance": planned[name],
                      "realized_imbalance_median": float(np.median(imb)),
                      "realized_imbalance_runs": [float(x) for x in imb],
                      "mean_workgroup_us": float(dur.mean()),
                      "kernel_span_us_median": float(np.median(span)),
-                     "xcd_mean_us": None if xcd is None else [float(x) for x in xcd]}
+                     "xcd_mean_us": xcd_mean,
+                     "on_xcd_w_mod_8": float(np.mean(xcc == (np.arange(n) % 8)[None, :])),
+                     "distinct_cus_per_run": int(np.median([len(np.unique(c)) for c in cu]))}
     return out
+
+
+def realized_balance(step, info, steps, torch, fwd_only=False):
+    """Stamp every workgroup for `steps` steps (outside any timed region)
+    and return balance_stats for the forward, dQ and dK/dV kernels (the
+    forward only with fwd_only)."""
+    from block_sparse_split_amd import splitkv as skv
+    n = info.n_workgroups
+    clk = torch.zeros(3 * n * 4, dtype=torch.int64, device="cuda")
+    runs = []
+    skv.skv_timing_wg_clock(clk)
+    try:
+        for _ in range(steps):
+            clk.zero_()
+            step()
+            torch.cuda.synchronize()
+            runs.append(clk.view(3, n, 4).cpu().numpy().copy())
+    finally:
+        skv.skv_timing_wg_clock(None)
+    planned = {"fwd_bf16": info.item_cost_max_bin / (info.item_cost_total / n) - 1,
+               "bwd_dq": info.item_cost_max_bin / (info.item_cost_total / n) - 1,
+               "bwd_dkdv": info.kv_cost_max_bin / (info.kv_cost_total / n) - 1}
+    return balance_stats(runs, planned, ("fwd_bf16",) if fwd_only else
+                         ("fwd_bf16", "bwd_dq", "bwd_dkdv"))
 
 
 def wg_balance(args):
@@ -747,24 +820,10 @@ def wg_balance(args):
 
     for _ in range(max(1, args.warmup)):
         step()
-    clk = torch.zeros(3 * n * 2, dtype=torch.int64, device="cuda")
-    runs = []
-    skv.skv_timing_wg_clock(clk)
-    try:
-        for _ in range(args.steps):
-            step()
-            torch.cuda.synchronize()
-            runs.append(clk.view(3, n, 2).cpu().numpy().copy())
-    finally:
-        skv.skv_timing_wg_clock(None)
-    info = sh.info
-    planned = {"fwd_bf16": info.item_cost_max_bin / (info.item_cost_total / n) - 1,
-               "bwd_dq": info.item_cost_max_bin / (info.item_cost_total / n) - 1,
-               "bwd_dkdv": info.kv_cost_max_bin / (info.kv_cost_total / n) - 1}
-    out = balance_stats(runs, planned)
+    out = realized_balance(step, sh.info, args.steps, torch)
     for name, v in out.items():
         log(f"{name}: planned {v['planned_imbalance'] * 100:.2f} %, realised "
-            f"{v['realized_imbalance_median'] * 100:.2f} % (median of {len(runs)}), "
+            f"{v['realized_imbalance_median'] * 100:.2f} % (median of {args.steps}), "
             f"mean {v['mean_workgroup_us']:.1f} us")
     print(json.dumps({"metric": "workgroup_balance", "workload": w.name, "workgroups": n,
                       "clock": "s_memrealtime, 100 MHz", "steps": args.steps,

@@ -676,8 +676,8 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
              a.ws_nD, a.ws_L2, a.ws_LO, a.ws_HI, rows, a.hq, a.hq / a.hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_kernel<D>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, DqCfg<D>::kLdsBytes);
+  static LdsLimit lds_dq, lds_kv;
+  e = lds_dq.ensure(reinterpret_cast<const void*>(&bwd_dq_kernel<D>), DqCfg<D>::kLdsBytes);
   if (e != hipSuccess) return e;
   SKV_LAUNCH("bwd_dq", bwd_dq_kernel<D>, dim3(a.n_wg), dim3(DqCfg<D>::kThreads),
              DqCfg<D>::kLdsBytes, s, a);
@@ -687,8 +687,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
                s, a.sched, a.ws_dQ, a.dQ);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, KvCfg<D>::kLdsBytes);
+  e = lds_kv.ensure(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D>), KvCfg<D>::kLdsBytes);
   if (e != hipSuccess) return e;
   SKV_LAUNCH("bwd_dkdv", bwd_dkdv_kernel<D>, dim3(a.n_wg), dim3(KvCfg<D>::kThreads),
              KvCfg<D>::kLdsBytes, s, a);

@@ -545,15 +545,15 @@ template <int D>
 hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   if (a.dtype_bf16) {
     constexpr int bytes = FwdCfg<D>::kLdsBytes;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_kernel<D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    static LdsLimit lds;
+    const hipError_t e = lds.ensure(reinterpret_cast<const void*>(&fwd_bf16_kernel<D>), bytes);
     if (e != hipSuccess) return e;
     SKV_LAUNCH("fwd_bf16", fwd_bf16_kernel<D>, dim3(a.n_wg), dim3(FwdCfg<D>::kThreads), bytes,
                stream, a);
   } else {
     constexpr int bytes = F32Lds<D>::bytes;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_f32_kernel<D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    static LdsLimit lds;
+    const hipError_t e = lds.ensure(reinterpret_cast<const void*>(&fwd_f32_kernel<D>), bytes);
     if (e != hipSuccess) return e;
     SKV_LAUNCH("fwd_f32", fwd_f32_kernel<D>, dim3(a.n_wg), dim3(kThreads), bytes, stream, a);
   }

@@ -149,6 +149,98 @@ std::vector<int32_t> lpt(const std::vector<int64_t>& cost, int32_t m,
   return bin;
 }
 
+// LPT with splitting, for work that is divisible into equal steps (the
+// partials of the pieces of one unit merge exactly).  Unit u is steps[u]
+// steps; a piece [k0, k1) of it costs item_cost + step_cost * (k1 - k0),
+// plus extra[u] if it is the unit's first piece (k0 == 0).  Pieces are taken
+// largest cost first (ties: lower unit, then lower k0), each to the
+// least-loaded bin (ties: lower bin).  A piece that would lift that bin
+// above the target load T is cut after the longest step prefix that fits,
+// provided the piece has two or more steps and the bin has room for its
+// fixed part and one step; the rest returns to the pending set and pays
+// item_cost again.  Otherwise the bin takes the piece whole.  A cut leaves
+// its bin within one step of T, so no bin is cut twice and there are at
+// most n_units + m pieces.
+struct Piece {
+  int32_t unit, k0, k1, bin;
+  int64_t cost;
+};
+
+struct SplitJob {
+  std::vector<int64_t> extra;
+  std::vector<int32_t> steps;
+  int64_t item_cost = 0, step_cost = 0;
+  int32_t m = 1;
+
+  int64_t cost(int32_t u, int32_t k0) const {
+    return item_cost + (k0 == 0 ? extra[u] : 0) + step_cost * (steps[u] - k0);
+  }
+
+  std::vector<Piece> pass(int64_t target, std::vector<int64_t>* load_out) const {
+    struct Pending {
+      int64_t cost;
+      int32_t unit, k0;
+      bool operator<(const Pending& o) const {  // priority_queue: top = largest
+        if (cost != o.cost) return cost < o.cost;
+        if (unit != o.unit) return unit > o.unit;
+        return k0 > o.k0;
+      }
+    };
+    std::priority_queue<Pending> pend;
+    for (int32_t u = 0; u < int32_t(steps.size()); ++u) pend.push({cost(u, 0), u, 0});
+    using Bin = std::pair<int64_t, int32_t>;  // (load, bin)
+    std::priority_queue<Bin, std::vector<Bin>, std::greater<Bin>> bins;
+    for (int32_t b = 0; b < m; ++b) bins.push({0, b});
+    std::vector<Piece> out;
+    std::vector<int64_t> load(m, 0);
+    while (!pend.empty()) {
+      const Pending pc = pend.top();
+      pend.pop();
+      Bin bin = bins.top();
+      bins.pop();
+      const int32_t n = steps[pc.unit];
+      int32_t k_end = n;
+      int64_t placed = pc.cost;
+      const int64_t head = item_cost + (pc.k0 == 0 ? extra[pc.unit] : 0);
+      if (bin.first + pc.cost > target && n - pc.k0 > 1 &&
+          target - bin.first >= head + step_cost) {
+        const int64_t room = target - bin.first;
+        int64_t acc = head;
+        int32_t k = pc.k0;
+        while (k < n && acc + step_cost <= room) acc += step_cost, ++k;
+        if (k < n) {
+          k_end = k;
+          placed = acc;
+          pend.push({cost(pc.unit, k), pc.unit, k});
+        }
+      }
+      out.push_back({pc.unit, pc.k0, k_end, bin.second, placed});
+      bin.first += placed;
+      load[bin.second] = bin.first;
+      bins.push(bin);
+    }
+    if (load_out) *load_out = std::move(load);
+    return out;
+  }
+
+  // T starts at ceil(total cost / m); cuts add fixed costs, so T is reset
+  // to the mean load a pass produced plus half an item cost, until it
+  // repeats (at most four passes).
+  int64_t auto_target() const {
+    int64_t total = 0;
+    for (int32_t u = 0; u < int32_t(steps.size()); ++u) total += cost(u, 0);
+    int64_t target = (total + m - 1) / m;
+    for (int p = 0; p < 4; ++p) {
+      int64_t placed = 0;
+      for (const Piece& pc : pass(target, nullptr)) placed += pc.cost;
+      const int64_t next = (placed + m - 1) / m + item_cost / 2;
+      if (next == target) break;
+      target = next;
+    }
+    return target;
+  }
+};
+
 std::atomic<int32_t> g_cu_cache[64];
 
 int32_t device_cu_count() {
@@ -303,147 +395,124 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
   const int32_t* L = p->lo;
   const int32_t tok_per_qt = skv::kQTile / g.G;
 
-  // Tiles that some anchor block of the query tile sees, per query tile.
+  // Tiles that each anchor block sees: tiles are sorted and disjoint, so
+  // their ends increase too and block b's interval [lo_b, a_b) meets the
+  // contiguous range [tr_lo[b], tr_hi[b]) found by two binary searches.
+  std::vector<int32_t> tr_lo(g.nb, 0), tr_hi(g.nb, 0);
+  for (int32_t b = 0; b < g.nb; ++b) {
+    if (L[b] >= A[b]) continue;
+    tr_lo[b] = int32_t(std::partition_point(tiles.begin(), tiles.end(), [&](const Tile& t) {
+                         return int64_t(t.pos) + t.len <= L[b];
+                       }) - tiles.begin());
+    tr_hi[b] = int32_t(std::partition_point(tiles.begin(), tiles.end(), [&](const Tile& t) {
+                         return t.pos < A[b];
+                       }) - tiles.begin());
+    tr_hi[b] = std::max(tr_hi[b], tr_lo[b]);
+  }
+  // Lowest and highest block that sees each tile (-1: none): blocks in
+  // order, each claiming the still-unclaimed tiles of its range; a
+  // next-unclaimed pointer forest makes the sweep near-linear.
+  auto claim = [&](bool ascending) {
+    std::vector<int32_t> who(nt, -1), next(nt + 1);
+    for (int32_t t = 0; t <= nt; ++t) next[t] = t;
+    auto find = [&](int32_t x) {
+      while (next[x] != x) x = next[x] = next[next[x]];
+      return x;
+    };
+    for (int32_t i = 0; i < g.nb; ++i) {
+      const int32_t b = ascending ? i : g.nb - 1 - i;
+      for (int32_t t = find(tr_lo[b]); t < tr_hi[b]; t = find(t)) {
+        who[t] = b;
+        next[t] = t + 1;
+      }
+    }
+    return who;
+  };
+  const std::vector<int32_t> tile_bmin = claim(true), tile_bmax = claim(false);
+  // Tiles that some anchor block of the query tile sees, per query tile:
+  // the union of its blocks' ranges.
   std::vector<Item> items;
   std::vector<std::vector<int32_t>> qt_vis(g.qt_per_head);
   for (int32_t qt = 0; qt < g.qt_per_head; ++qt) {
     const int32_t b0 = qt * tok_per_qt / skv::kBlock;
     const int32_t b1 = std::min(g.nb, ((qt + 1) * tok_per_qt + skv::kBlock - 1) / skv::kBlock);
-    for (int32_t t = 0; t < nt; ++t) {
-      bool seen = false;
-      for (int32_t b = b0; b < b1 && !seen; ++b)
-        seen = std::max<int64_t>(L[b], tiles[t].pos) <
-               std::min<int64_t>(A[b], int64_t(tiles[t].pos) + tiles[t].len);
-      if (seen) qt_vis[qt].push_back(t);
+    std::vector<std::pair<int32_t, int32_t>> rng;
+    for (int32_t b = b0; b < b1; ++b)
+      if (tr_hi[b] > tr_lo[b]) rng.push_back({tr_lo[b], tr_hi[b]});
+    std::sort(rng.begin(), rng.end());
+    int32_t upto = 0;  // ranges sorted by start: emit each tile once, in order
+    for (const auto& r : rng) {
+      for (int32_t t = std::max(upto, r.first); t < r.second; ++t) qt_vis[qt].push_back(t);
+      upto = std::max(upto, r.second);
     }
   }
   // Forward / dQ items.  Units are runs of consecutive visible tiles of one
   // (kv head, query tile); the first run of a query tile also carries its
-  // draft keys.  A piece of a unit costs kItemCost plus kStepCost per key
-  // step.  Per XCD class, units are placed LPT-first (largest remaining cost
-  // first, ties: lowest unit, then lowest bin) on the least-loaded
-  // workgroup; a unit that would push that workgroup past the class's target
-  // load T is cut at a tile boundary: the prefix that fits stays, the rest
-  // (which pays its own kItemCost) goes back to the pending set.  Work units
-  // are divisible (their partials merge exactly), so every bin ends within
-  // one step and one item cost of T, with at most one cut per bin.  T is
-  // ceil(class cost / bins) for a first pass, then raised by the item costs
-  // of the cuts that pass made, and the class is planned again.
+  // draft keys.  Costs are in the time units above: kItemCost per piece plus
+  // kStepCost per 64-key step (draft steps included).  Per XCD class the
+  // units are placed by LPT with splitting (SplitJob) on the class's
+  // workgroups; a cut falls on a tile boundary.
   struct Unit {
     int32_t head, qt, k0, k1;  // tiles qt_vis[qt][k0 .. k1-1]
     int64_t draft_cost;        // cost of the draft steps (first run only)
   };
-  std::vector<Unit> units;
-  for (int32_t h = 0; h < g.hkv; ++h) {
-    for (int32_t qt = 0; qt < g.qt_per_head; ++qt) {
-      const int32_t b0 = qt * tok_per_qt / skv::kBlock;
-      const int32_t b1 =
-          std::min(g.nb, ((qt + 1) * tok_per_qt + skv::kBlock - 1) / skv::kBlock);
-      // draft keys: the query tile's anchor blocks, in steps of 64
-      const int64_t dcost =
-          p->with_draft ? kStepCost * ((int64_t(b1 - b0) * skv::kBlock + skv::kTileK - 1) /
-                                       skv::kTileK)
-                        : 0;
-      const auto& vis = qt_vis[qt];
-      if (vis.empty()) {  // still one item: it writes O = 0, LSE = -inf (or the draft part)
-        units.push_back({h, qt, 0, 0, dcost});
-        continue;
-      }
-      bool first = true;
-      for (size_t i = 0; i < vis.size();) {
-        size_t j = i + 1;
-        while (j < vis.size() && vis[j] == vis[j - 1] + 1) ++j;
-        units.push_back({h, qt, int32_t(i), int32_t(j), first ? dcost : 0});
-        first = false;
-        i = j;
-      }
+  // units of one kv head (the same for every head)
+  std::vector<Unit> head_units;
+  for (int32_t qt = 0; qt < g.qt_per_head; ++qt) {
+    const int32_t b0 = qt * tok_per_qt / skv::kBlock;
+    const int32_t b1 = std::min(g.nb, ((qt + 1) * tok_per_qt + skv::kBlock - 1) / skv::kBlock);
+    // draft keys: the query tile's anchor blocks, in steps of 64
+    const int64_t dcost =
+        p->with_draft
+            ? kStepCost * ((int64_t(b1 - b0) * skv::kBlock + skv::kTileK - 1) / skv::kTileK)
+            : 0;
+    const auto& vis = qt_vis[qt];
+    if (vis.empty()) {  // still one item: it writes O = 0, LSE = -inf (or the draft part)
+      head_units.push_back({0, qt, 0, 0, dcost});
+      continue;
+    }
+    bool first = true;
+    for (size_t i = 0; i < vis.size();) {
+      size_t j = i + 1;
+      while (j < vis.size() && vis[j] == vis[j - 1] + 1) ++j;
+      head_units.push_back({0, qt, int32_t(i), int32_t(j), first ? dcost : 0});
+      first = false;
+      i = j;
     }
   }
+  std::vector<Unit> units;
+  for (int32_t h = 0; h < g.hkv; ++h)
+    for (Unit u : head_units) {
+      u.head = h;
+      units.push_back(u);
+    }
   const int32_t n_cls_fwd = xcd_classes(g.hkv, n_wg);
   const int32_t per_cls = n_wg / n_cls_fwd;
   std::vector<std::vector<int32_t>> q(n_wg);
   std::vector<int64_t> wg_load(n_wg, 0);
-  auto piece_cost = [&](const Unit& u, int32_t k0, int32_t k1) {
-    return kItemCost + (k0 == u.k0 ? u.draft_cost : 0) + kStepCost * (k1 - k0);
-  };
   for (int32_t cls = 0; cls < n_cls_fwd; ++cls) {
-    // pending pieces: (cost, unit, first tile) -- largest cost first
-    struct Pending {
-      int64_t cost;
-      int32_t unit, k0;
-      bool operator<(const Pending& o) const {  // priority_queue: top = largest
-        if (cost != o.cost) return cost < o.cost;
-        if (unit != o.unit) return unit > o.unit;
-        return k0 > o.k0;
-      }
-    };
-    int64_t cls_total = 0;
+    std::vector<int32_t> ids;  // units of this XCD class
+    SplitJob job;
+    job.item_cost = kItemCost;
+    job.step_cost = kStepCost;
+    job.m = per_cls;
     for (int32_t ui = 0; ui < int32_t(units.size()); ++ui)
-      if (units[ui].head % n_cls_fwd == cls)
-        cls_total += piece_cost(units[ui], units[ui].k0, units[ui].k1);
-    // one planning pass at target load T; emit = false only measures it
-    int64_t total_placed = 0;
-    auto plan = [&](int64_t target, bool emit) {
-      std::priority_queue<Pending> pend;
-      for (int32_t ui = 0; ui < int32_t(units.size()); ++ui) {
-        const Unit& u = units[ui];
-        if (u.head % n_cls_fwd == cls) pend.push({piece_cost(u, u.k0, u.k1), ui, u.k0});
+      if (units[ui].head % n_cls_fwd == cls) {
+        ids.push_back(ui);
+        job.extra.push_back(units[ui].draft_cost);
+        job.steps.push_back(units[ui].k1 - units[ui].k0);
       }
-      using Bin = std::pair<int64_t, int32_t>;  // (load, bin)
-      std::priority_queue<Bin, std::vector<Bin>, std::greater<Bin>> bins;
-      for (int32_t b = 0; b < per_cls; ++b) bins.push({0, b});
-      int32_t pieces = 0;
-      total_placed = 0;
-      while (!pend.empty()) {
-        const Pending pc = pend.top();
-        pend.pop();
-        const Unit& u = units[pc.unit];
-        Bin bin = bins.top();
-        bins.pop();
-        int32_t k_end = u.k1;
-        int64_t placed = pc.cost;
-        const int64_t head_cost = kItemCost + (pc.k0 == u.k0 ? u.draft_cost : 0);
-        if (bin.first + pc.cost > target && u.k1 - pc.k0 > 1 &&
-            target - bin.first >= head_cost + kStepCost) {
-          // cut: the longest prefix that fits (a bin with no room for one
-          // more step takes the piece whole)
-          const int64_t room = target - bin.first;
-          int64_t acc = head_cost;
-          int32_t k = pc.k0;
-          while (k < u.k1 && acc + kStepCost <= room) acc += kStepCost, ++k;
-          if (k < u.k1) {
-            k_end = k;
-            placed = acc;
-            pend.push({piece_cost(u, k, u.k1), pc.unit, k});
-          }
-        }
-        ++pieces;
-        total_placed += placed;
-        if (emit) {
-          const auto& vis = qt_vis[u.qt];
-          Item it{u.head, u.qt, u.k1 > u.k0 ? vis[pc.k0] : 0,
-                  u.k1 > u.k0 ? vis[k_end - 1] + 1 : 0, -1, 0, placed};
-          if (pc.k0 == u.k0 && p->with_draft && u.draft_cost > 0) it.flags |= skv::kItemDraft;
-          const int32_t wg = cls + bin.second * n_cls_fwd;
-          q[wg].push_back(int32_t(items.size()));
-          items.push_back(it);
-          wg_load[wg] = bin.first + placed;
-        }
-        bin.first += placed;
-        bins.push(bin);
-      }
-      return pieces;
-    };
-    // T starts at ceil(class cost / bins); cuts add item costs, so T is
-    // raised to the mean load each pass produced (a few passes settle it)
-    int64_t target = (cls_total + per_cls - 1) / per_cls;
-    for (int pass = 0; pass < 4; ++pass) {
-      plan(target, false);
-      const int64_t next = (total_placed + per_cls - 1) / per_cls + kItemCost / 2;
-      if (next == target) break;
-      target = next;
+    std::vector<int64_t> load;
+    for (const Piece& pc : job.pass(job.auto_target(), &load)) {
+      const Unit& u = units[ids[pc.unit]];
+      const auto& vis = qt_vis[u.qt];
+      Item it{u.head, u.qt, pc.k1 > pc.k0 ? vis[u.k0 + pc.k0] : 0,
+              pc.k1 > pc.k0 ? vis[u.k0 + pc.k1 - 1] + 1 : 0, -1, 0, pc.cost};
+      if (pc.k0 == 0 && p->with_draft && u.draft_cost > 0) it.flags |= skv::kItemDraft;
+      q[cls + pc.bin * n_cls_fwd].push_back(int32_t(items.size()));
+      items.push_back(it);
     }
-    plan(target, true);
+    for (int32_t b = 0; b < per_cls; ++b) wg_load[cls + b * n_cls_fwd] = load[b];
   }
   // query tiles with several items write partial slots, merged afterwards
   std::vector<int32_t> split_rec;  // S_WORDS per split query tile
@@ -466,47 +535,50 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
     const int64_t rows = int64_t(std::max(0, b1 - b0)) * skv::kBlock * g.G;
     return kKvItemCost + kKvRowCost * ((rows + skv::kTileK - 1) / skv::kTileK);
   };
+  // The context items of every kv head cover the same tile pairs: build
+  // them once.
+  std::vector<KvItem> pairs;
+  for (int32_t t = 0; t < nt; t += 2) {
+    const int32_t n2 = std::min(2, nt - t);
+    int32_t bmin = g.nb, bmax = -1;
+    for (int32_t u = t; u < t + n2; ++u)
+      if (tile_bmin[u] >= 0) {
+        bmin = std::min(bmin, tile_bmin[u]);
+        bmax = std::max(bmax, tile_bmax[u]);
+      }
+    if (bmax < 0) {  // no block sees these keys: zero gradients
+      bmin = 0;
+      bmax = -1;
+    }
+    pairs.push_back({0, t, n2, 0, 0, bmin, bmax + 1, kv_cost(bmin, bmax + 1)});
+    // row tiles inside [b0, b1) whose anchor blocks all see every key of
+    // the item: they need neither the per-row intervals nor masks
+    const int64_t kmin = tiles[t].pos;
+    const int64_t kend = int64_t(tiles[t + n2 - 1].pos) + tiles[t + n2 - 1].len;
+    const int64_t rpb = int64_t(skv::kBlock) * g.G;  // rows per anchor block
+    const int64_t r_begin = int64_t(bmin) * rpb, r_end = int64_t(bmax + 1) * rpb;
+    const int64_t n_rt = (std::max<int64_t>(0, r_end - r_begin) + skv::kTileK - 1) / skv::kTileK;
+    auto whole = [&](int64_t rt) {
+      const int64_t r0 = r_begin + rt * skv::kTileK;
+      if (r0 + skv::kTileK > r_end) return false;
+      for (int64_t b = r0 / rpb; b <= (r0 + skv::kTileK - 1) / rpb; ++b)
+        if (!(L[b] <= kmin && A[b] >= kend)) return false;
+      return true;
+    };
+    // the kernels decode the high half with a signed shift: 15 bits
+    if (n_rt < (int64_t(1) << 15)) {
+      int64_t w0 = 0;
+      while (w0 < n_rt && !whole(w0)) ++w0;
+      int64_t w1 = w0;
+      while (w1 < n_rt && whole(w1)) ++w1;
+      if (w1 > w0) pairs.back().whole = int32_t(w0 | (w1 << 16));
+    }
+  }
   std::vector<KvItem> kv;
   for (int32_t h = 0; h < g.hkv; ++h) {
-    for (int32_t t = 0; t < nt; t += 2) {
-      const int32_t n2 = std::min(2, nt - t);
-      int32_t bmin = g.nb, bmax = -1;
-      for (int32_t u = t; u < t + n2; ++u)
-        for (int32_t b = 0; b < g.nb; ++b)
-          if (std::max<int64_t>(L[b], tiles[u].pos) <
-              std::min<int64_t>(A[b], int64_t(tiles[u].pos) + tiles[u].len)) {
-            bmin = std::min(bmin, b);
-            bmax = std::max(bmax, b);
-          }
-      if (bmax < 0) {  // no block sees these keys: zero gradients
-        bmin = 0;
-        bmax = -1;
-      }
-      kv.push_back({h, t, n2, 0, 0, bmin, bmax + 1, kv_cost(bmin, bmax + 1)});
-      // row tiles inside [b0, b1) whose anchor blocks all see every key of
-      // the item: they need neither the per-row intervals nor masks
-      {
-        const int64_t kmin = tiles[t].pos;
-        const int64_t kend = int64_t(tiles[t + n2 - 1].pos) + tiles[t + n2 - 1].len;
-        const int64_t rpb = int64_t(skv::kBlock) * g.G;  // rows per anchor block
-        const int64_t r_begin = int64_t(bmin) * rpb, r_end = int64_t(bmax + 1) * rpb;
-        const int64_t n_rt = (std::max<int64_t>(0, r_end - r_begin) + skv::kTileK - 1) / skv::kTileK;
-        auto whole = [&](int64_t rt) {
-          const int64_t r0 = r_begin + rt * skv::kTileK;
-          if (r0 + skv::kTileK > r_end) return false;
-          for (int64_t b = r0 / rpb; b <= (r0 + skv::kTileK - 1) / rpb; ++b)
-            if (!(L[b] <= kmin && A[b] >= kend)) return false;
-          return true;
-        };
-        // the kernels decode the high half with a signed shift: 15 bits
-        if (n_rt < (int64_t(1) << 15)) {
-          int64_t w0 = 0;
-          while (w0 < n_rt && !whole(w0)) ++w0;
-          int64_t w1 = w0;
-          while (w1 < n_rt && whole(w1)) ++w1;
-          if (w1 > w0) kv.back().whole = int32_t(w0 | (w1 << 16));
-        }
-      }
+    for (KvItem it : pairs) {
+      it.head = h;
+      kv.push_back(it);
     }
     if (p->with_draft) {
       for (int32_t tok = 0; tok < g.nq; tok += skv::kKvGroup) {
@@ -751,6 +823,51 @@ skv_status skv_plan_lpt(const int32_t* anchors, const int32_t* lo, int32_t nb,
   });
 }
 
+skv_status skv_plan_lpt_split(const int64_t* extra, const int32_t* steps, int32_t n_units,
+                              int64_t item_cost, int64_t step_cost, int32_t n_bins,
+                              int64_t target, int32_t capacity, int32_t* out_pieces,
+                              int64_t* out_cost, int32_t* out_n, int64_t* out_target,
+                              int64_t* out_load) {
+  return guarded([&] {
+    require(n_units >= 0, "n_units must be >= 0");
+    require(n_units == 0 || (extra && steps), "extra/steps must not be NULL");
+    require(n_bins >= 1, "n_bins must be >= 1");
+    require(item_cost >= 0 && step_cost >= 0, "item_cost/step_cost must be >= 0");
+    require(target >= 0, "target must be >= 0 (0 = automatic)");
+    require(capacity >= 0 && out_n && (capacity == 0 || (out_pieces && out_cost)),
+            "out_pieces/out_cost/out_n must not be NULL");
+    SplitJob job;
+    job.item_cost = item_cost;
+    job.step_cost = step_cost;
+    job.m = n_bins;
+    __int128 total = 0;
+    for (int32_t u = 0; u < n_units; ++u) {
+      require(extra[u] >= 0 && steps[u] >= 0, "extra/steps must be >= 0");
+      total += __int128(item_cost) + extra[u] + __int128(step_cost) * steps[u];
+      require(total <= (__int128(1) << 60), "total cost must not exceed 2^60");
+      job.extra.push_back(extra[u]);
+      job.steps.push_back(steps[u]);
+    }
+    const int64_t t = target == 0 ? job.auto_target() : target;
+    std::vector<int64_t> load;
+    const std::vector<Piece> pieces = job.pass(t, &load);
+    *out_n = int32_t(pieces.size());
+    if (out_target) *out_target = t;
+    if (out_load) std::memcpy(out_load, load.data(), size_t(n_bins) * 8);
+    if (int64_t(pieces.size()) > capacity)
+      fail(SKV_ERR_WORKSPACE, "capacity too small: need " + std::to_string(pieces.size()) +
+                                  " pieces");
+    for (size_t i = 0; i < pieces.size(); ++i) {
+      int32_t* w = out_pieces + 4 * i;
+      w[0] = pieces[i].unit;
+      w[1] = pieces[i].k0;
+      w[2] = pieces[i].k1;
+      w[3] = pieces[i].bin;
+      out_cost[i] = pieces[i].cost;
+    }
+  });
+}
+
 skv_status skv_schedule_build(const skv_problem* p, int32_t n_workgroups,
                               int32_t* image, int64_t capacity_words,
                               skv_schedule_info* info) {
@@ -842,6 +959,33 @@ skv_status skv_merge_lse(int32_t n_parts, int64_t rows, int32_t d, const void* O
                                 O_out, out_dtype == SKV_BF16, LSE_out,
                                 static_cast<hipStream_t>(stream)),
               "merge launch");
+  });
+}
+
+skv_status skv_dq_finalize(int32_t n_parts, int64_t elems, const float* parts,
+                           int64_t part_stride, void* dq_out, int32_t out_dtype,
+                           void* stream) {
+  return guarded([&] {
+    require(n_parts >= 1 && elems >= 0, "need n_parts >= 1 and elems >= 0");
+    if (!(out_dtype == SKV_BF16 || out_dtype == SKV_F32))
+      fail(SKV_ERR_UNSUPPORTED, "out_dtype must be SKV_BF16 or SKV_F32");
+    require(n_parts == 1 || (part_stride >= elems && part_stride % 4 == 0),
+            "part_stride must be >= elems and a multiple of 4");
+    if (elems == 0) return;
+    require(parts && dq_out, "pointers must not be NULL");
+    require_aligned({parts, dq_out}, 16, "parts/dq_out");
+    const int64_t span = (int64_t(n_parts) - 1) * (n_parts > 1 ? part_stride : 0) + elems;
+    require(span <= INT64_MAX / 4, "shares too large");
+    const char* ib = reinterpret_cast<const char*>(parts);
+    const char* ob = static_cast<const char*>(dq_out);
+    const int64_t out_bytes = elems * int64_t(elem_size(out_dtype));
+    const bool disjoint = ob + out_bytes <= ib || ib + span * 4 <= ob;
+    require(disjoint || (ob == ib && out_dtype == SKV_F32),
+            "dq_out must not overlap the shares (an fp32 dq_out may be share 0 itself)");
+    check_hip(skv::launch_dq_finalize(n_parts, elems, n_parts > 1 ? part_stride : 0, parts,
+                                      dq_out, out_dtype == SKV_BF16,
+                                      static_cast<hipStream_t>(stream)),
+              "dq_finalize launch");
   });
 }
 

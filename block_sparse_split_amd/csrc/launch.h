@@ -3,7 +3,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace skv {
+
+// A kernel's dynamic-LDS limit, raised once per device (the setting lasts
+// for the process), so launches do not repeat the runtime call.  One static
+// instance per kernel.
+struct LdsLimit {
+  std::atomic<uint64_t> done{0};  // bit d: set on device d (d < 64)
+  hipError_t ensure(const void* fn, int bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+  }
+};
 
 struct FwdArgs {
   const int32_t* sched;     // device schedule image
@@ -59,6 +78,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // size; *out gets the current device's copy.
 constexpr int64_t kNoAllocScratchBytes = int64_t(64) << 20;
 hipError_t noalloc_scratch(void** out);
+// dQ finalize: out[i] = sum over k < n of parts[k * stride + i], i < elems.
+hipError_t launch_dq_finalize(int32_t n, int64_t elems, int64_t stride, const float* parts,
+                              void* out, bool out_bf16, hipStream_t s);
 hipError_t launch_merge(int32_t n_parts, int64_t rows, int32_t d, const void* O_parts,
                         bool in_bf16, const float* LSE_parts, void* O_out, bool out_bf16,
                         float* LSE_out, hipStream_t stream);

@@ -184,6 +184,42 @@ hipError_t launch_merge_split_d(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// dQ finalize: the sum of n fp32 dQ shares (one per shard whose keys the
+// queries saw), converted to the output type.  HBM-bound like the merge:
+// each thread owns 8 consecutive elements and adds the shares in index
+// order, so the bits do not depend on the launch shape.  The last thread
+// of a ragged tail goes element by element.
+__device__ __forceinline__ void store1(float* p, float x) { *p = x; }
+__device__ __forceinline__ void store1(__bf16* p, float x) { *p = f32_to_bf16(x); }
+
+template <typename TO>
+__global__ __launch_bounds__(kThreads) void dq_finalize_kernel(int32_t n, int64_t elems,
+                                                               int64_t stride,
+                                                               const float* __restrict__ parts,
+                                                               TO* __restrict__ out) {
+  const int64_t i = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 8;
+  if (i >= elems) return;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  if (i + 8 <= elems) {
+#pragma unroll 4
+    for (int32_t k = 0; k < n; ++k) {
+      float x[8];
+      Vec8<float>::load(parts + k * stride + i, x);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += x[j];
+    }
+    Vec8<TO>::store(out + i, acc);
+  } else {
+    for (int64_t j = 0; j < elems - i; ++j) {
+      float a = 0.f;
+      for (int32_t k = 0; k < n; ++k) a += parts[k * stride + i + j];
+      store1(out + i + j, a);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_merge(int32_t n, int64_t rows, int32_t d, const void* O, bool in_bf16,
@@ -194,6 +230,21 @@ hipError_t launch_merge(int32_t n, int64_t rows, int32_t d, const void* O, bool 
 
 hipError_t launch_merge_split(const FwdArgs& a, hipStream_t s) {
   return a.d == 128 ? launch_merge_split_d<128>(a, s) : launch_merge_split_d<64>(a, s);
+}
+
+hipError_t launch_dq_finalize(int32_t n, int64_t elems, int64_t stride, const float* parts,
+                              void* out, bool out_bf16, hipStream_t s) {
+  const int64_t blocks = (elems + 8 * kThreads - 1) / (8 * kThreads);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (blocks == 0) return hipSuccess;
+  const dim3 g(static_cast<unsigned>(blocks)), b(kThreads);
+  if (out_bf16)
+    SKV_LAUNCH("dq_finalize", dq_finalize_kernel<__bf16>, g, b, 0, s, n, elems, stride, parts,
+               static_cast<__bf16*>(out));
+  else
+    SKV_LAUNCH("dq_finalize", dq_finalize_kernel<float>, g, b, 0, s, n, elems, stride, parts,
+               static_cast<float*>(out));
+  return hipGetLastError();
 }
 
 }  // namespace skv

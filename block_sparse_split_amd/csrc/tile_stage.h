@@ -64,16 +64,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Start and end of a workgroup on the constant-rate (100 MHz) clock, for
-// measuring the realised balance of a plan; `clk` is null unless a caller
-// asked for the stamps (then each workgroup writes its pair).
+// measuring the realised balance of a plan, with the hardware ids of where
+// it ran (XCC_ID and HW_ID registers: XCD, shader engine, CU, SIMD); `clk`
+// is null unless a caller asked for the stamps (then each workgroup writes
+// its four words).
 __device__ __forceinline__ uint64_t wg_clock_now() { return __builtin_amdgcn_s_memrealtime(); }
 __device__ __forceinline__ void wg_clock_record(unsigned long long* clk, uint64_t t0) {
   if (clk == nullptr) return;
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
-    clk[2 * blockIdx.x] = t0;
-    clk[2 * blockIdx.x + 1] = t1;
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // HW_REG_XCC_ID, 32 bits
+    const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_REG_HW_ID, 32 bits
+    clk[4 * blockIdx.x] = t0;
+    clk[4 * blockIdx.x + 1] = t1;
+    clk[4 * blockIdx.x + 2] = xcc;
+    clk[4 * blockIdx.x + 3] = hw;
   }
 }
 

@@ -52,11 +52,11 @@ bool timing_on() { return g_state.on; }
 unsigned long long* wg_clock_region(int k, int32_t n_wg, bool* fits) {
   *fits = true;
   if (!g_clock) return nullptr;
-  if (g_clock_bytes < int64_t(kClockKernels) * n_wg * 16) {
+  if (g_clock_bytes < int64_t(kClockKernels) * n_wg * 32) {
     *fits = false;
     return nullptr;
   }
-  return g_clock + int64_t(k) * n_wg * 2;
+  return g_clock + int64_t(k) * n_wg * 4;
 }
 
 void timing_begin(const char* name, hipStream_t stream) {

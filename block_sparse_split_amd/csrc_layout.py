@@ -45,3 +45,5 @@ T_WORDS = _ENUMS["T_WORDS"]
 I_WORDS = _ENUMS["I_WORDS"]
 S_WORDS = _ENUMS["S_WORDS"]
 K_WORDS = _ENUMS["K_WORDS"]
+# word index of each item field (I_HEAD -> "HEAD", ...)
+I = {k[2:]: v for k, v in _ENUMS.items() if k.startswith("I_") and k != "I_WORDS"}

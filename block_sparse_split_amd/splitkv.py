@@ -75,6 +75,9 @@ def lib():
     L.skv_plan_lpt_costs.argtypes = [_i64p, ctypes.c_int32, ctypes.c_int32, _i32p, _i64p]
     L.skv_plan_lpt.argtypes = [_i32p, _i32p, ctypes.c_int32, _i32p, _i32p, ctypes.c_int32,
                                ctypes.c_int32, ctypes.c_int32, _i32p, _i64p, _i64p]
+    L.skv_plan_lpt_split.argtypes = [_i64p, _i32p, ctypes.c_int32, ctypes.c_int64,
+                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
+                                     ctypes.c_int32, _i32p, _i64p, _i32p, _i64p, _i64p]
     L.skv_schedule_build.argtypes = [ctypes.POINTER(SkvProblem), ctypes.c_int32, _i32p,
                                      ctypes.c_int64, ctypes.POINTER(SkvScheduleInfo)]
     L.skv_attn_fwd_partial.argtypes = [ctypes.POINTER(SkvProblem),
@@ -85,6 +88,8 @@ def lib():
                                                ctypes.POINTER(SkvScheduleInfo), _vp, _vp,
                                                _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp,
                                                _vp]
+    L.skv_dq_finalize.argtypes = [ctypes.c_int32, ctypes.c_int64, _vp, ctypes.c_int64, _vp,
+                                  ctypes.c_int32, _vp]
     L.skv_merge_lse.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _vp,
                                 ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, _vp]
     L.skv_attn_bwd.argtypes = [ctypes.POINTER(SkvProblem), ctypes.POINTER(SkvScheduleInfo),
@@ -98,9 +103,11 @@ def lib():
     L.skv_timing_result.argtypes = [ctypes.c_int32, ctypes.c_char_p, ctypes.c_int32, _i64p,
                                     ctypes.POINTER(ctypes.c_double)]
     L.skv_timing_wg_clock.argtypes = [_vp, ctypes.c_int64]
-    for name in ("skv_chunk_costs", "skv_plan_lpt_costs", "skv_plan_lpt", "skv_schedule_build",
-                 "skv_attn_fwd_partial", "skv_attn_fwd_partial_noalloc", "skv_merge_lse", "skv_attn_bwd", "skv_timing_enable",
-                 "skv_timing_collect", "skv_timing_result", "skv_timing_wg_clock"):
+    for name in ("skv_chunk_costs", "skv_plan_lpt_costs", "skv_plan_lpt", "skv_plan_lpt_split",
+                 "skv_schedule_build", "skv_attn_fwd_partial", "skv_attn_fwd_partial_noalloc",
+                 "skv_merge_lse", "skv_dq_finalize", "skv_attn_bwd", "skv_timing_enable",
+                 "skv_timing_collect",
+                 "skv_timing_result", "skv_timing_wg_clock"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -141,6 +148,29 @@ def skv_plan_lpt_costs(costs, n_bins):
     _check("skv_plan_lpt_costs", lib().skv_plan_lpt_costs(
         cp, len(c), n_bins, bins.ctypes.data_as(_i32p), load.ctypes.data_as(_i64p)))
     return bins, load
+
+
+NO_CUT = 2 ** 63 - 1  # skv_plan_lpt_split target that never cuts
+
+
+def skv_plan_lpt_split(extra, steps, item_cost, step_cost, n_bins, target=0):
+    """LPT with splitting; returns (pieces [n, 4] = (unit, k0, k1, bin) in
+    placement order, cost [n], target used, load [n_bins])."""
+    e, ep = _i64(extra)
+    st, sp = _i32(steps)
+    if len(e) != len(st):
+        raise ValueError("extra and steps must have the same length")
+    cap = len(st) + n_bins
+    pieces = np.zeros((cap, 4), np.int32)
+    cost = np.zeros(cap, np.int64)
+    n = ctypes.c_int32(0)
+    t = ctypes.c_int64(0)
+    load = np.zeros(n_bins, np.int64)
+    _check("skv_plan_lpt_split", lib().skv_plan_lpt_split(
+        ep, sp, len(st), int(item_cost), int(step_cost), int(n_bins), int(target), cap,
+        pieces.ctypes.data_as(_i32p), cost.ctypes.data_as(_i64p), ctypes.byref(n),
+        ctypes.byref(t), load.ctypes.data_as(_i64p)))
+    return pieces[:n.value], cost[:n.value], t.value, load
 
 
 def skv_plan_lpt(anchors, lo, chunk_pos, chunk_len, tile_k, n_bins):
@@ -290,6 +320,25 @@ def skv_merge_lse(O_parts, LSE_parts, O_out, LSE_out, stream=None):
         _ptr(LSE_parts, "LSE_parts", torch.float32, (k,) + tuple(O_parts.shape[1:-1])),
         _ptr(O_out, "O_out", None, tuple(O_parts.shape[1:])), _dtype_code(O_out),
         _ptr(LSE_out, "LSE_out", torch.float32, tuple(O_parts.shape[1:-1])), _stream(stream)))
+
+
+def skv_dq_finalize(parts, dq_out, stream=None):
+    """Sum fp32 dQ shares parts[0..n-1] (a [n, ...] fp32 device tensor whose
+    shares are contiguous; dim 0 may be padded, e.g. a slice of a longer
+    buffer) into dq_out ([...], fp32 or bf16)."""
+    torch = _torch()
+    if not parts.is_cuda or parts.dtype != torch.float32:
+        raise ValueError("parts must be a float32 device tensor")
+    if parts.dim() < 1 or parts.shape[0] < 1:
+        raise ValueError("parts must be [n, ...] with n >= 1")
+    if not parts[0].is_contiguous():
+        raise ValueError("each share must be contiguous")
+    elems = parts[0].numel()
+    stride = parts.stride(0) if parts.shape[0] > 1 else elems
+    out = _ptr(dq_out, "dq_out", None, tuple(parts.shape[1:]))
+    _check("skv_dq_finalize", lib().skv_dq_finalize(
+        parts.shape[0], elems, ctypes.c_void_p(parts.data_ptr()) if elems else None, stride,
+        out, _dtype_code(dq_out), _stream(stream)))
 
 
 def skv_attn_bwd(problem: Problem, info, schedule, Q, K, V, Kd, Vd, O, dO, LSE, dQ, dK, dV,

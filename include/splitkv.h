@@ -113,6 +113,38 @@ skv_status skv_plan_lpt(const int32_t* anchors, const int32_t* lo, int32_t nb,
                         int32_t* out_bin, int64_t* out_cost,
                         int64_t* out_load);
 
+/* LPT with splitting: the placement the work schedule below uses for the
+ * forward / dQ items of each XCD class (exported for tests and tools).
+ * Same sources as above, plus the exact merge of partials (rit.work blog,
+ * section "Split-KV moves queries, not keys and values"), which makes a
+ * unit of work divisible.  Unit u is steps[u] >= 0 equal steps; a piece
+ * [k0, k1) of it costs item_cost + step_cost * (k1 - k0), plus extra[u] on
+ * the unit's first piece (k0 == 0).  Pending pieces are taken largest cost
+ * first (ties: lower unit, then lower k0), each to the least-loaded bin
+ * (ties: lower bin).  A piece that would lift that bin above `target` is
+ * cut after the longest step prefix that fits when it has >= 2 steps and
+ * the bin has room for its fixed part plus one step; the remainder returns
+ * to the pending set and pays item_cost again.  Otherwise the bin takes
+ * the piece whole.  A cut leaves its bin within one step of target, so no
+ * bin is cut twice and there are at most n_units + n_bins pieces.
+ *   target: 0 = chosen as the schedule does (ceil(total / n_bins), then
+ *   reset to the mean load a pass produced plus item_cost / 2 until it
+ *   repeats, at most four passes); INT64_MAX = never cut (plain LPT of the
+ *   units, as skv_plan_lpt_costs).
+ *   out_pieces: host int32 [capacity][4] = (unit, k0, k1, bin) in
+ *   placement order; out_cost: host int64 [capacity]; *out_n: pieces;
+ *   *out_target (may be NULL): the target used; out_load: host int64
+ *   [n_bins] or NULL.  Costs are in the caller's units.
+ * Errors: SKV_ERR_INVALID_ARG (NULL, negative values, total cost above
+ * 2^60), SKV_ERR_WORKSPACE (capacity below *out_n, which is still set). */
+skv_status skv_plan_lpt_split(const int64_t* extra, const int32_t* steps,
+                              int32_t n_units, int64_t item_cost,
+                              int64_t step_cost, int32_t n_bins,
+                              int64_t target, int32_t capacity,
+                              int32_t* out_pieces, int64_t* out_cost,
+                              int32_t* out_n, int64_t* out_target,
+                              int64_t* out_load);
+
 /* ------------------------------------------------------------------------
  * Problem description and the in-GPU work schedule.
  * ---------------------------------------------------------------------- */
@@ -159,12 +191,20 @@ typedef struct skv_schedule_info {
 
 /* Build the work schedule of one problem for n_workgroups persistent
  * workgroups (0 = the current device's compute-unit count; this call then
- * queries the device).  Forward work is cut into items (kv head, 256-row
- * query tile, run of visible 64-key tiles); item cost counts visible
- * (anchor block, key tile) pairs as in skv_chunk_costs, and items are
- * placed by LPT on workgroups.  Work of one kv head is kept on the
- * workgroups of the same XCD class so its keys/values share an L2.
- * Backward dK/dV items are (kv head, 64-key tile) placed the same way.
+ * queries the device).  Forward / dQ work is cut into units (kv head,
+ * 256-row query tile, run of consecutive 64-key tiles that some row of the
+ * tile sees); the first unit of a query tile also takes its draft keys.
+ * Item costs are in time units fitted to measured per-workgroup times, not
+ * in the (anchor block, key tile) pairs of skv_chunk_costs: a key step
+ * (64 keys) costs the same however many of the tile's anchor blocks see
+ * it, and each item pays a fixed part.  Units are placed by
+ * skv_plan_lpt_split (item_cost 44, step_cost 8, automatic target), so a
+ * unit may be cut into several items whose partials are merged in the
+ * forward call.  Work of one kv head is kept on the workgroups of one XCD
+ * class (workgroup w runs on XCD w mod 8) so its keys/values share an L2.
+ * Backward dK/dV items (kv head, two 64-key tiles) and draft groups (kv
+ * head, 128 draft tokens) cost 13 plus 5 per 64-row tile of the anchor
+ * blocks that see them, and are placed by plain LPT per XCD class.
  *   image: host int32 buffer of capacity_words, or NULL to only fill
  *   `info` (size query).  The caller copies the image to device memory
  *   and passes that copy, with `info`, to the device calls below.  The
@@ -243,6 +283,8 @@ skv_status skv_merge_lse(int32_t n_parts, int64_t rows, int32_t d,
  *   dKd, dVd [Nq, hkv, d] (grad_dtype): draft-key gradients, only with
  *       with_draft = 1 (else ignored, may be NULL).
  *   workspace: >= info->bwd_workspace_bytes.
+ * The backward takes bf16 inputs only (problem dtype SKV_BF16); an fp32
+ * problem returns SKV_ERR_UNSUPPORTED (the fp32 path is forward-only).
  * Errors as skv_attn_fwd_partial. */
 skv_status skv_attn_bwd(const skv_problem* p, const skv_schedule_info* info,
                         const int32_t* schedule, const void* Q, const void* K,
@@ -251,6 +293,24 @@ skv_status skv_attn_bwd(const skv_problem* p, const skv_schedule_info* info,
                         float* dQ, void* dK, void* dV, void* dKd, void* dVd,
                         int32_t grad_dtype, void* workspace,
                         int64_t workspace_bytes, void* stream);
+
+/* dQ finalize: the sum of n_parts fp32 dQ shares, converted to out_dtype
+ * (rit.work blog, section "Split-KV moves queries, not keys and values":
+ * the participants return the query gradients to the query owner, who adds
+ * them).  Share k is the `elems` floats at parts + k * part_stride (device,
+ * 16-byte aligned; part_stride >= elems and a multiple of 4 when
+ * n_parts > 1), e.g. the skv_attn_bwd dQ outputs of the shards, or what a
+ * reduce-scatter delivered.  Shares are added in index order in fp32, so
+ * the result does not depend on the launch; out_dtype SKV_BF16 rounds the
+ * fp32 sum to nearest even once.  dq_out: device, 16-byte aligned, `elems`
+ * values of out_dtype; it must not overlap the shares, except that an fp32
+ * dq_out may be share 0 itself (in place).  elems = 0 launches nothing.
+ * Async on `stream`.
+ * Errors: SKV_ERR_INVALID_ARG, SKV_ERR_UNSUPPORTED (out_dtype),
+ * SKV_ERR_HIP. */
+skv_status skv_dq_finalize(int32_t n_parts, int64_t elems, const float* parts,
+                           int64_t part_stride, void* dq_out, int32_t out_dtype,
+                           void* stream);
 
 /* ------------------------------------------------------------------------
  * Benchmark support: per-kernel timing with HIP events.
@@ -276,14 +336,17 @@ skv_status skv_timing_result(int32_t k, char* name, int32_t name_cap, int64_t* l
  * on the workgroups (the pages' load-balance claim, measured rather than
  * planned).  While `buffer` (device memory, 8-byte aligned, owned by the
  * caller) is set on the calling thread, the bf16 forward, dQ and dK/dV
- * kernels each write, per workgroup w, the pair (start, end) of the GPU's
- * constant 100 MHz clock as two uint64 at [2w, 2w + 1] of their region:
- * forward at 0, dQ at 2 n_wg, dK/dV at 4 n_wg (n_wg = the schedule's
- * workgroup count).  Each launch overwrites its region.  NULL turns it off
- * (the default).  A device call whose n_wg needs more than `bytes`
- * (3 * n_wg * 16) fails with SKV_ERR_INVALID_ARG before launching.  The
- * buffer must stay allocated until it is cleared (NULL) or replaced: the
- * library keeps only the pointer.  Launches on other threads do not see it.
+ * kernels each write, per workgroup w, four uint64 at [4w, 4w + 3] of their
+ * region: start and end on the GPU's constant 100 MHz clock, then the
+ * hardware XCC_ID and HW_ID register values of the wave that wrote them
+ * (XCC_ID's low bits give the XCD; HW_ID holds the wave, SIMD, CU and
+ * shader-engine ids).  Regions: forward at 0, dQ at 4 n_wg, dK/dV at 8 n_wg (n_wg =
+ * the schedule's workgroup count).  Each launch overwrites its region.
+ * NULL turns it off (the default).  A device call whose n_wg needs more
+ * than `bytes` (3 * n_wg * 32) fails with SKV_ERR_INVALID_ARG before
+ * launching.  The buffer must stay allocated until it is cleared (NULL) or
+ * replaced: the library keeps only the pointer.  Launches on other threads
+ * do not see it.
  * Errors: SKV_ERR_INVALID_ARG for a misaligned buffer, negative bytes or a
  * pointer that is not device (or managed) memory. */
 skv_status skv_timing_wg_clock(void* buffer, int64_t bytes);

@@ -19,12 +19,12 @@ routines, hand-worked fixtures under ``tests/golden/``).  No function is
 "parity unpinned".
 """
 from .attention_fp64 import (BLOCK, visible_context, attention_partial,
-                             attention, merge_lse, attention_bwd)
+                             attention, merge_lse, attention_bwd, dq_finalize)
 from .planner import (chunk_costs, tile_pairs_visible, plan_lpt,
                       plan_contiguous, imbalance, makespan)
 
 __all__ = [
     "BLOCK", "visible_context", "attention_partial", "attention", "merge_lse",
-    "attention_bwd", "chunk_costs", "tile_pairs_visible",
+    "attention_bwd", "dq_finalize", "chunk_costs", "tile_pairs_visible",
     "plan_lpt", "plan_contiguous", "imbalance", "makespan",
 ]

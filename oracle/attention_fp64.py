@@ -127,6 +127,15 @@ def merge_lse(O_parts, LSE_parts):
     return O, lse
 
 
+def dq_finalize(dQ_parts):
+    """The query gradient from the shards' shares dQ_parts [S, ...]: their
+    sum.  Each shard's share covers the keys it holds, and the query
+    gradients are the ones returned to the query owner (rit.work blog,
+    section "Split-KV moves queries, not keys and values"), who adds them.
+    """
+    return _f64(dQ_parts).sum(axis=0)
+
+
 def attention_bwd(Q, K, V, pos, anchors, lo, scale, O, dO, LSE, Kd=None,
                   Vd=None, blocks=None):
     """Gradients of sum(O * dO) for the keys of one subset.

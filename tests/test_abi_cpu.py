@@ -1,6 +1,7 @@
 """CPU checks of the C-ABI library: exports, argument errors, the planner
-(bit-exact against the oracle) and the in-GPU schedule (coverage and LPT
-placement re-derived with the oracle).  No device call is made here."""
+(bit-exact against the oracle) and the in-GPU schedule (coverage checked
+with the oracle's tile visibility; placement re-derived from units built
+with it).  No device call is made here."""
 import ctypes
 import os
 import re
@@ -66,6 +67,17 @@ def test_invalid_arguments_return_status_codes():
     assert L.skv_merge_lse(0, 4, 128, None, 1, None, None, 1, None, None) == -1
     assert L.skv_merge_lse(2, 4, 96, None, 1, None, None, 1, None, None) == -2
     assert L.skv_merge_lse(2, 0, 128, None, 1, None, None, 1, None, None) == 0
+    # dQ finalize argument checks need no device either
+    V = ctypes.c_void_p
+    assert L.skv_dq_finalize(0, 64, V(4096), 64, V(8192), 1, None) == -1       # no shares
+    assert L.skv_dq_finalize(2, 64, V(4096), 64, V(8192), 9, None) == -2       # out dtype
+    assert L.skv_dq_finalize(2, 64, V(4096), 66, V(1 << 20), 1, None) == -1    # stride % 4
+    assert L.skv_dq_finalize(2, 64, V(4096), 32, V(1 << 20), 1, None) == -1    # stride < elems
+    assert L.skv_dq_finalize(2, 64, V(4100), 64, V(1 << 20), 1, None) == -1    # misaligned
+    assert L.skv_dq_finalize(2, 64, V(4096), 64, V(4096 + 256), 1, None) == -1  # overlap
+    assert L.skv_dq_finalize(2, 64, V(4096), 64, V(4096), 1, None) == -1       # bf16 in place
+    assert L.skv_dq_finalize(2, 64, None, 64, V(8192), 1, None) == -1          # NULL
+    assert L.skv_dq_finalize(3, 0, None, 0, None, 1, None) == 0                # nothing to do
 
 
 def test_error_text_clears_after_success():
@@ -180,91 +192,46 @@ def _check_lpt_per_class(costs, heads, qoff, queue, n_wg, n_cls):
 STEP_COST, ITEM_COST = 8, 44  # time units of a key step and of an item's fixed part
 
 
-def _lpt_split_items(w, g, tiles, n_wg, n_cls, with_draft):
-    """Independent re-derivation of the forward item plan: per XCD class,
-    runs of consecutive visible tiles of each (kv head, query tile) are
-    placed largest-first on the least-loaded workgroup.  A piece costs
-    ITEM_COST plus STEP_COST per key step (its tiles, and for the first run
-    of a query tile its draft steps).  A run that would pass the class target
-    T is cut after the longest tile prefix that fits, if the bin has room
-    for the piece's fixed part and one step; otherwise the bin takes it
-    whole.  T starts at ceil(total / bins) and is re-set (at most four times,
-    until it repeats) to the mean load of a pass plus ITEM_COST // 2.
-    Returns the items (head, qt, t0, t1, flags, cost) in emission order and
-    the per-workgroup queues."""
-    import heapq
+def _fwd_items_via_split_plan(w, g, tiles, n_wg, n_cls, with_draft):
+    """The forward item plan re-derived from its parts: units from the
+    oracle's tile visibility (per kv head and query tile, runs of
+    consecutive tiles that some anchor block of the query tile sees; a query
+    tile that sees none still makes one empty unit; the first run carries
+    the draft steps, one per 64 draft keys), placed per XCD class by
+    skv_plan_lpt_split, which tests/test_plan_split_cpu.py pins on its own.
+    Returns the items (head, qt, t0, t1, flags, cost) in emission order, the
+    per-workgroup queues and each class's target."""
     G = w.hq // w.hkv
     tpq = QTILE // G
     qtph = -(-w.nq * G // QTILE)
-    vis = []
-    for qt in range(qtph):
-        b0 = qt * tpq // BLOCK
-        b1 = min(w.nb, -(-((qt + 1) * tpq) // BLOCK))
-        c = [oracle.tile_pairs_visible(g.anchors[b0:b1], g.lo[b0:b1], t[1], t[1] + t[2])
-             for t in tiles]
-        vis.append([i for i, x in enumerate(c) if x > 0])
-    units = []  # (head, qt, k0, k1, draft cost)
+    units = []  # (head, qt, tiles of the run, draft cost)
     for h in range(w.hkv):
         for qt in range(qtph):
             b0 = qt * tpq // BLOCK
             b1 = min(w.nb, -(-((qt + 1) * tpq) // BLOCK))
+            vis = [i for i, t in enumerate(tiles)
+                   if oracle.tile_pairs_visible(g.anchors[b0:b1], g.lo[b0:b1], t[1],
+                                                t[1] + t[2]) > 0]
             dc = STEP_COST * -(-((b1 - b0) * BLOCK) // 64) if with_draft else 0
-            v = vis[qt]
-            if not v:
-                units.append((h, qt, 0, 0, dc))
-                continue
-            i, first = 0, True
-            while i < len(v):
-                j = i + 1
-                while j < len(v) and v[j] == v[j - 1] + 1:
-                    j += 1
-                units.append((h, qt, i, j, dc if first else 0))
-                first, i = False, j
+            runs = np.split(np.array(vis, np.int64),
+                            np.nonzero(np.diff(vis) != 1)[0] + 1) if vis else [[]]
+            for j, r in enumerate(runs):
+                units.append((h, qt, list(r), dc if j == 0 else 0))
     per = n_wg // n_cls
-    items, queues = [], [[] for _ in range(n_wg)]
-
-    def cost(u, k0):
-        return ITEM_COST + (u[4] if k0 == u[2] else 0) + STEP_COST * (u[3] - k0)
-
-    def plan(c, target, emit):
-        pend = [(-cost(u, u[2]), ui, u[2]) for ui, u in enumerate(units) if u[0] % n_cls == c]
-        heapq.heapify(pend)
-        bins = [(0, b) for b in range(per)]
-        placed_total = 0
-        while pend:
-            negc, ui, k0 = heapq.heappop(pend)
-            u = units[ui]
-            load, b = heapq.heappop(bins)
-            k_end, placed = u[3], -negc
-            head = ITEM_COST + (u[4] if k0 == u[2] else 0)
-            if load - negc > target and u[3] - k0 > 1 and target - load >= head + STEP_COST:
-                acc, k = head, k0
-                while k < u[3] and acc + STEP_COST <= target - load:
-                    acc += STEP_COST
-                    k += 1
-                if k < u[3]:
-                    k_end, placed = k, acc
-                    heapq.heappush(pend, (-cost(u, k), ui, k))
-            placed_total += placed
-            if emit:
-                v = vis[u[1]]
-                t0, t1 = (v[k0], v[k_end - 1] + 1) if u[3] > u[2] else (0, 0)
-                flags = 1 if (k0 == u[2] and with_draft and u[4] > 0) else 0
-                queues[c + b * n_cls].append(len(items))
-                items.append((u[0], u[1], t0, t1, flags, placed))
-            heapq.heappush(bins, (load + placed, b))
-        return placed_total
-
+    items, queues, targets = [], [[] for _ in range(n_wg)], []
     for c in range(n_cls):
-        total = sum(cost(u, u[2]) for u in units if u[0] % n_cls == c)
-        target = -(-total // per)
-        for _ in range(4):
-            nxt = -(-plan(c, target, False) // per) + ITEM_COST // 2
-            if nxt == target:
-                break
-            target = nxt
-        plan(c, target, True)
-    return items, queues
+        ids = [i for i, u in enumerate(units) if u[0] % n_cls == c]
+        pieces, cost, target, _ = skv.skv_plan_lpt_split(
+            [units[i][3] for i in ids], [len(units[i][2]) for i in ids], ITEM_COST, STEP_COST,
+            per, 0)
+        targets.append(target)
+        for (u, k0, k1, b), cst in zip(pieces.tolist(), cost.tolist()):
+            h, qt, run, dc = units[ids[u]]
+            t0, t1 = (run[k0], run[k1 - 1] + 1) if k1 > k0 else (0, 0)
+            flags = 1 if (k0 == 0 and with_draft and dc > 0) else 0
+            queues[c + b * n_cls].append(len(items))
+            items.append((h, qt, t0, t1, flags, cst))
+    return items, queues, targets
 
 
 def _schedule_case(name, seed, shard_of=None, n_wg=256, **over):
@@ -455,7 +422,8 @@ def test_schedule_covers_visible_work_once_and_is_lpt(case):
             assert v[0] == -1
     # queues: each item once, LPT per XCD class re-derived by the oracle
     assert sorted(queue.tolist()) == list(range(len(items)))
-    want_items, want_q = _lpt_split_items(w, g, tiles, n_wg, h["NCLASS"], prob.c.with_draft)
+    want_items, want_q, _ = _fwd_items_via_split_plan(w, g, tiles, n_wg, h["NCLASS"],
+                                                      prob.c.with_draft)
     assert len(want_items) == len(items)
     for got, want in zip(items, want_items):
         assert (got[0], got[1], got[2], got[3], got[5], got[6]) == want

@@ -39,17 +39,22 @@ def test_plan_imbalances_match_oracle(name, scale):
 
 
 def test_balance_stats_from_workgroup_stamps():
-    """Synthetic stamps: 16 workgroups, XCD class 3 runs 10 % longer; the
-    realised imbalance, span and per-XCD means follow by hand."""
+    """Synthetic stamps: 16 workgroups, XCD 3 runs 10 % longer; the realised
+    imbalance, span, per-XCD means (by the stamped XCC_ID), placement share
+    and CU count follow by hand."""
     import bench
     n = 16
     runs = []
     for shift in (0, 1000):
-        r = np.zeros((3, n, 2), np.int64)
+        r = np.zeros((3, n, 4), np.int64)
         for k in range(3):
             for w in range(n):
                 d = 1100 if w % 8 == 3 else 1000          # ticks (10 / 11 us)
-                r[k, w] = (shift + 5 * w, shift + 5 * w + d)
+                # XCC_ID w mod 8, except workgroup 5 which reports XCD 3;
+                # HW_ID: CU w // 8, SE 1
+                xcc = 3 if w == 5 else w % 8
+                r[k, w] = (shift + 5 * w, shift + 5 * w + d, 0x100 | xcc,
+                           (1 << 13) | ((w // 8) << 8))
         runs.append(r)
     planned = {"fwd_bf16": 0.01, "bwd_dq": 0.02, "bwd_dkdv": 0.03}
     out = bench.balance_stats(runs, planned)
@@ -61,4 +66,35 @@ def test_balance_stats_from_workgroup_stamps():
         assert abs(v["mean_workgroup_us"] - mean) < 1e-12
         # last end: workgroup 11 (class 3) at 5 * 11 + 1100 ticks
         assert abs(v["kernel_span_us_median"] - (55 + 1100) / 100.0) < 1e-12
-        assert v["xcd_mean_us"] == [10.0, 10.0, 10.0, 11.0, 10.0, 10.0, 10.0, 10.0]
+        # XCD 3 holds workgroups 3, 11 (11 us) and 5 (10 us); XCD 5 only 13
+        assert v["xcd_mean_us"] == [10.0, 10.0, 10.0, 32.0 / 3, 10.0, 10.0, 10.0, 10.0]
+        assert v["on_xcd_w_mod_8"] == 15 / 16
+        # (XCD, SE, CU): workgroups 5 and 3 share (3, 1, 0)
+        assert v["distinct_cus_per_run"] == 15
+    only = bench.balance_stats(runs, planned, ("fwd_bf16",))
+    assert list(only) == ["fwd_bf16"]
+
+
+def test_item_pair_loads_by_hand():
+    """Two anchor blocks (G = 16: one block per 256-row query tile), one kv
+    head, three 64-key tiles; block 0 sees keys [0, 100), block 1 [0, 200).
+    Pair counts: query tile 0 sees tiles 0, 1 (2 pairs), query tile 1 sees
+    tiles 0, 1, 2 (3 pairs), plus one draft pair per block."""
+    import bench
+    from block_sparse_split_amd import splitkv as skv
+    from block_sparse_split_amd import workloads as wl
+
+    class G_:
+        anchors = np.array([100, 200], np.int32)
+        lo = np.array([0, 0], np.int32)
+    w = wl.scaled(wl.WORKLOADS["ctx32k_q2k"], hq=16, hkv=1, d=64, blocks_per_seq=2)
+    prob = skv.Problem(nb=2, hq=16, hkv=1, d=64, scale=0.125, dtype=skv.SKV_BF16,
+                       anchors=G_.anchors, lo=G_.lo, chunk_pos=[0], chunk_off=[0, 192],
+                       with_draft=True)
+    for n_wg in (1, 2, 5):
+        image, info = skv.skv_schedule_build(prob, n_wg)
+        loads = bench.item_pair_loads(image, G_, w)
+        assert len(loads) == n_wg
+        assert loads.sum() == (2 + 1) + (3 + 1)
+    image, info = skv.skv_schedule_build(prob, 1)
+    assert bench.item_pair_loads(image, G_, w).tolist() == [7]

@@ -119,18 +119,58 @@ def test_bwd_split_over_shards():
     O, L, full = oracle_fwd_bwd(w, g, t, allc, True)
     Od = to_dev(wl.round_to_bf16(O.astype(np.float32)), "bf16")
     Ld = torch.from_numpy(L.astype(np.float32)).cuda()
-    dq_sum = torch.zeros((w.nq, w.hq, w.d), device="cuda")
+    shares = torch.empty((w.n_shards, w.nq, w.hq, w.d), device="cuda")
     for r in range(w.n_shards):
         announce("bwd shard", r)
         dQ, dK, dV, dKd, dVd = gpu_bwd(w, g, t, ids[r], r == 0, Od, Ld, n_wg=32)
-        dq_sum += dQ
+        shares[r] = dQ
         rr = rows_of(t, g, ids[r])
         check_grad(dK, full[1][rr], f"dK shard {r}")
         check_grad(dV, full[2][rr], f"dV shard {r}")
         if r == 0:
             check_grad(dKd, full[3], "dKd")
             check_grad(dVd, full[4], "dVd")
-    check_grad(dq_sum, full[0], "sum of dQ shares")
+    announce("dq_finalize of the shard shares")
+    for dt in (torch.float32, torch.bfloat16):
+        dq = torch.full((w.nq, w.hq, w.d), float("nan"), dtype=dt, device="cuda")
+        skv.skv_dq_finalize(shares, dq)
+        torch.cuda.synchronize()
+        check_grad(dq, full[0], f"finalized dQ ({dt})")
+
+
+@pytest.mark.parametrize("n,shape,pad,odt", [
+    (1, (64, 32, 128), 0, "f32"), (3, (16, 4, 64), 0, "bf16"), (8, (37, 5, 3), 1, "f32"),
+    (64, (256, 8, 64), 0, "bf16"), (5, (1, 1, 7), 3, "bf16"), (2, (2, 2, 2), 0, "f32")])
+def test_dq_finalize_random_shares(n, shape, pad, odt):
+    """Sum of n fp32 shares (dim 0 padded by `pad` floats per share, then
+    rounded up to a multiple of 4) against the fp64 sum.  Bound from the
+    arithmetic: n - 1 fp32 additions in index order err by at most
+    (n - 1) 2^-24 sum_k |x_k|; a bf16 output adds one rounding, 2^-9 |sum|."""
+    rng = np.random.default_rng(n * 100 + pad)
+    elems = int(np.prod(shape))
+    stride = -(-(elems + pad) // 4) * 4
+    buf = torch.full((n, stride), float("nan"), device="cuda")
+    x = rng.standard_normal((n,) + shape).astype(np.float32)
+    buf[:, :elems] = torch.from_numpy(x.reshape(n, elems)).cuda()
+    parts = buf[:, :elems].view((n,) + shape)
+    dt = torch.bfloat16 if odt == "bf16" else torch.float32
+    out = torch.full(shape, float("nan"), dtype=dt, device="cuda")
+    announce("dq_finalize", n, shape, pad, odt)
+    skv.skv_dq_finalize(parts, out)
+    torch.cuda.synchronize()
+    want = oracle.dq_finalize(x)
+    got = out.float().cpu().numpy().astype(np.float64)
+    bound = (n - 1) * 2.0 ** -24 * np.abs(x.astype(np.float64)).sum(0)
+    if odt == "bf16":
+        bound = bound * (1 + 2.0 ** -8) + 2.0 ** -9 * np.abs(want)
+    assert np.all(np.abs(got - want) <= bound + 1e-30)
+    if odt == "f32" and n <= 8:
+        assert np.abs(got - want).max() <= 1e-5
+    if odt == "f32":
+        # in place: the output may be share 0 itself
+        skv.skv_dq_finalize(parts, parts[0])
+        torch.cuda.synchronize()
+        assert torch.equal(parts[0], out)
 
 
 def test_bwd_varlen_small():
@@ -305,7 +345,8 @@ def test_bwd_empty_and_draft_only_shards():
 
 def test_workgroup_clock_stamps():
     """With a per-workgroup clock buffer set, the forward, dQ and dK/dV
-    kernels stamp every workgroup (start <= end) and compute the same bits;
+    kernels stamp every workgroup (start <= end, plus the hardware ids of
+    where it ran) and compute the same bits;
     a buffer too small for the schedule is refused before any launch."""
     w, g, t = _small(8, blocks_per_seq=16)
     prob = shards.whole_context_problem(w, g)
@@ -327,11 +368,11 @@ def test_workgroup_clock_stamps():
 
     announce("workgroup clock stamps, 40 workgroups")
     ref = step()
-    clk = torch.zeros(3 * 40 * 2, dtype=torch.int64, device="cuda")
+    clk = torch.zeros(3 * 40 * 4, dtype=torch.int64, device="cuda")
     skv.skv_timing_wg_clock(clk)
     try:
         got = step()
-        small = torch.zeros(3 * 39 * 2, dtype=torch.int64, device="cuda")
+        small = torch.zeros(3 * 39 * 4, dtype=torch.int64, device="cuda")
         skv.skv_timing_wg_clock(small)
         with pytest.raises(skv.SplitKVError):
             step()
@@ -339,8 +380,12 @@ def test_workgroup_clock_stamps():
         skv.skv_timing_wg_clock(None)
     for x, r in zip(got, ref):
         assert torch.equal(x, r)
-    st = clk.view(3, 40, 2).cpu().numpy()
+    st = clk.view(3, 40, 4).cpu().numpy()
     assert np.all(st[:, :, 0] > 0) and np.all(st[:, :, 1] >= st[:, :, 0])
+    # hardware ids: an XCD in 0..7 and 32-bit register values
+    assert np.all((st[:, :, 2] & 15) < 8) and np.all(st[:, :, 2:] < 2 ** 32)
+    print("[stamps] workgroups on XCD w mod 8:",
+          float(np.mean((st[:, :, 2] & 15) == np.arange(40) % 8)), flush=True)
     # the three kernels run one after another on the stream
     assert st[0, :, 1].max() <= st[1, :, 0].min() + 1
     assert st[1, :, 1].max() <= st[2, :, 0].min() + 1

@@ -171,13 +171,18 @@ def test_merge_random_partials(k, rows, d, in_dt, out_dt):
     skv.skv_merge_lse(Od, Ld, Om, Lm)
     torch.cuda.synchronize()
     Oo, Lo = oracle.merge_lse(O, L)
-    tol_o = 2e-2 if out_dt == "bf16" else 1e-5
     Og = Om.float().cpu().numpy()
     Lg = Lm.cpu().numpy()
     assert np.array_equal(np.isneginf(Lg), np.isneginf(Lo))
     fin = np.isfinite(Lo)
     assert np.abs(Lg[fin] - Lo[fin]).max() <= 1e-5
-    assert np.abs(Og - Oo).max() <= tol_o * max(1.0, np.abs(Oo).max())
+    err = np.abs(Og - Oo).max()
+    print(f"[merge] k={k} O max-abs {err:.3g}", flush=True)
+    if out_dt == "f32":
+        assert err <= 1e-5
+    else:
+        # bf16 output: one rounding of a value of size max|O|
+        assert err <= 2e-2 * max(1.0, np.abs(Oo).max())
     assert np.all(Og[~fin] == 0)
 
 
@@ -284,6 +289,27 @@ def test_full_ctx1m_64_shards_then_64way_merge():
                                       t.Kd, t.Vd, blocks=blocks)
     rows = block_rows(blocks)
     compare(Om[rows], Lm[rows], Oo, Lo, "bf16", "ctx1m merged sampled")
+    del Ko, Vo, Oo, Lo
+
+    # The last anchor block sees (nearly) the whole 1M context.  One kv head
+    # (and its G query heads) keeps the fp64 oracle within host memory.
+    top = [len(g.anchors) - 1]
+    h = w.hkv - 1
+    G = w.hq // w.hkv
+    need = np.nonzero(g.chunk_pos < g.anchors[top].max())[0]
+    announce("ctx1m: oracle on block", top, "kv head", h, "over", len(need), "chunks")
+    Ko = np.concatenate([wl.draw_kv_chunks(w, g, 4, need[i:i + 256], "K")[:, h:h + 1]
+                         for i in range(0, len(need), 256)])
+    Vo = np.concatenate([wl.draw_kv_chunks(w, g, 4, need[i:i + 256], "V")[:, h:h + 1]
+                         for i in range(0, len(need), 256)])
+    pos = shards.shard_rows(g, need)
+    heads = slice(h * G, (h + 1) * G)
+    Oo, Lo = oracle.attention_partial(t.Q[:, heads], Ko, Vo, pos, g.anchors, g.lo,
+                                      wl.softmax_scale(w.d), t.Kd[:, h:h + 1],
+                                      t.Vd[:, h:h + 1], blocks=top)
+    assert pos.size > 1_000_000 - 8192
+    rows = block_rows(top)
+    compare(Om[rows][:, heads], Lm[rows][:, heads], Oo, Lo, "bf16", "ctx1m merged top block")
 
 
 def ids_of(ids, chunks):

@@ -288,19 +288,21 @@ def test_bwd_split_over_shards():
                             p["anchors"], p["lo"], p["scale"])
     full = _oracle_grads(p, dO)
     parts = _random_partition(np.random.default_rng(8), p["K"].shape[0], 3)
-    dq_sum = np.zeros_like(p["Q"])
+    shares = []
     for j, idx in enumerate(parts):
         wd = j == 0
         dq, dk, dv, dkd, dvd = oracle.attention_bwd(
             p["Q"], p["K"][idx], p["V"][idx], idx, p["anchors"], p["lo"],
             p["scale"], O, dO, L, p["Kd"] if wd else None, p["Vd"] if wd else None)
-        dq_sum += dq
+        shares.append(dq)
         np.testing.assert_allclose(dk, full[1][idx], atol=1e-12)
         np.testing.assert_allclose(dv, full[2][idx], atol=1e-12)
         if wd:
             np.testing.assert_allclose(dkd, full[3], atol=1e-12)
             np.testing.assert_allclose(dvd, full[4], atol=1e-12)
-    np.testing.assert_allclose(dq_sum, full[0], atol=1e-12)
+    # the finalized dQ of the shares is the unsplit dQ (and no share alone is)
+    np.testing.assert_allclose(oracle.dq_finalize(np.stack(shares)), full[0], atol=1e-12)
+    assert all(np.abs(sh - full[0]).max() > 1e-3 for sh in shares)
     # negative: the shard's partial statistics are not the ones to use
     idx = parts[1]
     o1, l1 = oracle.attention_partial(p["Q"], p["K"][idx], p["V"][idx], idx,
