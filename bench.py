@@ -628,7 +628,9 @@ def run_workload(args, workload):
                 "chunk_imbalance_256bins": chunk_imb, "plan_ms": 1e3 * float(np.median(plan_times)),
                 "workgroups": n_wg,
                 "realized": {k: {"imbalance_median": v["realized_imbalance_median"],
-                                 "on_xcd_w_mod_8": v["on_xcd_w_mod_8"],
+                                 "on_xcd_w_plus_c_mod_8": v["on_xcd_w_plus_c_mod_8"],
+                                 "xcd_rotation_per_run": v["xcd_rotation_per_run"],
+                                 "distinct_cus": v["distinct_cus_per_run"],
                                  "xcd_mean_us": v["xcd_mean_us"]}
                              for k, v in realized.items()}},
         "kernels": per_kernel,
@@ -745,8 +747,10 @@ def balance_stats(runs, planned, names=("fwd_bf16", "bwd_dq", "bwd_dkdv")):
     100 MHz ticks): workgroup durations in us, max/mean - 1 per run and its
     median, the span from the first start to the last end, the mean
     duration per XCD as the XCC_ID register reports it, the share of
-    workgroups w that ran on XCD w mod 8 (the placement the plan assumes)
-    and the number of distinct compute units (XCD, SE, CU) used."""
+    workgroups w that ran on XCD w mod 8 and on XCD (w + c) mod 8 for the
+    best single rotation c of each run (the plan only needs workgroups
+    w = w' mod 8 to share an XCD), and the number of distinct compute units
+    (XCD, SE, CU) used."""
     out = {}
     n = runs[0].shape[1]
     for k, name in enumerate(("fwd_bf16", "bwd_dq", "bwd_dkdv")):
@@ -766,6 +770,13 @@ def balance_stats(runs, planned, names=("fwd_bf16", "bwd_dq", "bwd_dkdv")):
                      "kernel_span_us_median": float(np.median(span)),
                      "xcd_mean_us": xcd_mean,
                      "on_xcd_w_mod_8": float(np.mean(xcc == (np.arange(n) % 8)[None, :])),
+                     # the dispatcher's round robin may start a launch on any
+                     # XCD: workgroup w on XCD (w + c) mod 8 for one c per run
+                     "xcd_rotation_per_run": [int(np.bincount(o, minlength=8).argmax())
+                                              for o in (xcc - np.arange(n)[None, :]) % 8],
+                     "on_xcd_w_plus_c_mod_8": float(np.mean([
+                         np.bincount(o, minlength=8).max() / n
+                         for o in (xcc - np.arange(n)[None, :]) % 8])),
                      "distinct_cus_per_run": int(np.median([len(np.unique(c)) for c in cu]))}
     return out
 

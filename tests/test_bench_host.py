@@ -69,10 +69,18 @@ def test_balance_stats_from_workgroup_stamps():
         # XCD 3 holds workgroups 3, 11 (11 us) and 5 (10 us); XCD 5 only 13
         assert v["xcd_mean_us"] == [10.0, 10.0, 10.0, 32.0 / 3, 10.0, 10.0, 10.0, 10.0]
         assert v["on_xcd_w_mod_8"] == 15 / 16
+        assert v["xcd_rotation_per_run"] == [0, 0]
+        assert v["on_xcd_w_plus_c_mod_8"] == 15 / 16
         # (XCD, SE, CU): workgroups 5 and 3 share (3, 1, 0)
         assert v["distinct_cus_per_run"] == 15
     only = bench.balance_stats(runs, planned, ("fwd_bf16",))
     assert list(only) == ["fwd_bf16"]
+    # every workgroup one XCD further on: rotation 1, all consistent
+    for r in runs:
+        r[:, :, 2] = 0x100 | ((np.arange(n) + 1) % 8)
+    v = bench.balance_stats(runs, planned)["bwd_dq"]
+    assert v["on_xcd_w_mod_8"] == 0.0
+    assert v["xcd_rotation_per_run"] == [1, 1] and v["on_xcd_w_plus_c_mod_8"] == 1.0
 
 
 def test_item_pair_loads_by_hand():

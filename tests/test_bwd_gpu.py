@@ -145,7 +145,8 @@ def test_dq_finalize_random_shares(n, shape, pad, odt):
     """Sum of n fp32 shares (dim 0 padded by `pad` floats per share, then
     rounded up to a multiple of 4) against the fp64 sum.  Bound from the
     arithmetic: n - 1 fp32 additions in index order err by at most
-    (n - 1) 2^-24 sum_k |x_k|; a bf16 output adds one rounding, 2^-9 |sum|."""
+    (n - 1) 2^-24 sum_k |x_k|; a bf16 output adds one rounding to nearest
+    (8 significant bits), at most 2^-8 of the value."""
     rng = np.random.default_rng(n * 100 + pad)
     elems = int(np.prod(shape))
     stride = -(-(elems + pad) // 4) * 4
@@ -162,7 +163,7 @@ def test_dq_finalize_random_shares(n, shape, pad, odt):
     got = out.float().cpu().numpy().astype(np.float64)
     bound = (n - 1) * 2.0 ** -24 * np.abs(x.astype(np.float64)).sum(0)
     if odt == "bf16":
-        bound = bound * (1 + 2.0 ** -8) + 2.0 ** -9 * np.abs(want)
+        bound = bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(want)
     assert np.all(np.abs(got - want) <= bound + 1e-30)
     if odt == "f32" and n <= 8:
         assert np.abs(got - want).max() <= 1e-5
