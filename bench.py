@@ -446,6 +446,9 @@ def main():
                     help="instead of the benchmark: per-workgroup start/end stamps of the "
                          "forward, dQ and dK/dV kernels over --steps steps; realised against "
                          "planned imbalance")
+    ap.add_argument("--no-subrecords", action="store_true",
+                    help="with the default workload, skip the sub-records of the varlen, "
+                         "512K rank-share and 1M merge workloads")
     ap.add_argument("--plan-sweep", action="store_true",
                     help="host only: time the chunk-level LPT plan (costs + placement) for "
                          "1K-4M chunks of 256 keys on 64 and 256 bins")
@@ -486,7 +489,70 @@ def main():
         return run_sweep(args)
     if args.wg_times:
         return wg_balance(args)
-    print(json.dumps(run_workload(args, args.workload)), flush=True)
+    rec = run_workload(args, args.workload)
+    if args.workload == "ctx32k_q2k" and not args.fwd_only and not args.no_subrecords:
+        rec["other_configs"] = other_configs(args)
+    print(json.dumps(rec), flush=True)
+
+
+def _summary(r):
+    """The figures of a workload record that a sub-record keeps."""
+    keep = ("value", "unit", "ms_per_step", "frac_of_bf16_peak", "fwd_tflops",
+            "fwd_frac_of_bf16_peak", "fwd_ms", "algorithmic_tflop_per_step", "config", "lpt",
+            "roofline", "hip_graph")
+    out = {k: r[k] for k in keep if k in r}
+    out["kernels_avg_ms"] = {k: v["avg_ms"] for k, v in r["kernels"].items()}
+    return out
+
+
+def other_configs(args):
+    """Sub-records for the other full-size workloads, timed in the same run:
+    the varlen fwd+bwd job, the 512K-context rank-0 share (forward) and the
+    64-way merge of the 1M-context job (the merge alone, on N(0,1) bf16
+    partials and N(0, 4) LSEs drawn on the device, seeded)."""
+    import argparse as _ap
+    import torch
+    from block_sparse_split_amd import splitkv as skv
+    from block_sparse_split_amd import workloads as wl
+    sub = _ap.Namespace(**vars(args))
+    sub.steps = max(3, args.steps // 2)
+    sub.no_cpu_baseline = True
+    sub.compare_plans = False
+    out = {}
+    for name, seed in (("varlen8_fwdbwd", 3), ("cp64_rank0_ctx512k", 2)):
+        sub.seed = seed
+        sub.fwd_only = False
+        log(f"sub-record {name}")
+        out[name] = _summary(run_workload(sub, name))
+        torch.cuda.empty_cache()
+    w, g, _ = wl.make("ctx1m_merge64", 4, tensors=False)
+    log("sub-record ctx1m_merge64 (64-way merge)")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    Op = torch.randn((w.n_shards, w.nq, w.hq, w.d), device="cuda", generator=gen,
+                     dtype=torch.bfloat16)
+    Lp = 2.0 * torch.randn((w.n_shards, w.nq, w.hq), device="cuda", generator=gen)
+    Om = torch.empty((w.nq, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+    Lm = torch.empty((w.nq, w.hq), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        skv.skv_merge_lse(Op, Lp, Om, Lm)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(sub.steps):
+        skv.skv_merge_lse(Op, Lp, Om, Lm)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / sub.steps
+    nbytes = Op.numel() * 2 + Lp.numel() * 4 + Om.numel() * 2 + Lm.numel() * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out["ctx1m_merge64"] = {"step": "64-way LSE merge", "partials": w.n_shards,
+                            "rows": w.nq * w.hq, "head_dim": w.d, "ms": ms,
+                            "algorithmic_bytes": nbytes, "gbs": gbs,
+                            "frac_of_hbm_peak": gbs / PEAK_HBM_GBS, "launches": sub.steps}
+    del Op, Lp, Om, Lm
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_workload(args, workload):
