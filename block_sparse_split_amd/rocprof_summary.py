@@ -9,6 +9,8 @@ sources.
               known number of bytes
   counters -- matrix-core utilisation per kernel from one `--pmc` run of the
               SQ/GRBM counters listed in MFMA_COUNTERS
+  l2       -- L2 (TCC) hits and misses per dispatch of each kernel from one
+              `--pmc TCC_HIT_sum TCC_MISS_sum` run
 
 Usage:
   python -m block_sparse_split_amd.rocprof_summary kernels STATS_CSV \\
@@ -17,6 +19,8 @@ Usage:
       --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV \\
       --copy-bytes N --workload NAME --command "..." [--out FILE]
   python -m block_sparse_split_amd.rocprof_summary counters CSV \\
+      --workload NAME --command "..." [--skip-first N] [--out FILE]
+  python -m block_sparse_split_amd.rocprof_summary l2 CSV \\
       --workload NAME --command "..." [--skip-first N] [--out FILE]
 """
 import argparse
@@ -35,6 +39,7 @@ SHORT = {
     "merge_split_kernel": "merge_split", "merge_kernel": "merge",
     "bwd_pre_kernel": "bwd_pre", "bwd_dq_kernel": "bwd_dq",
     "dq_reduce_kernel": "dq_reduce", "bwd_dkdv_kernel": "bwd_dkdv",
+    "dq_finalize_kernel": "dq_finalize",
 }
 
 
@@ -211,6 +216,37 @@ def cmd_counters(a):
     emit("\n".join(out) + "\n", a.out)
 
 
+def cmd_l2(a):
+    """L2 requests of each library kernel: hits and misses per dispatch
+    (each counter summed over its rows), the hit rate, and the miss count
+    times the 128-byte L2 line as an upper bound on the bytes the misses
+    bring in from beyond L2."""
+    per = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))
+    for row in csv.DictReader(open(a.csv)):
+        name = short_name(row["Kernel_Name"])
+        if name:
+            cn = row["Counter_Name"].replace("_sum", "")
+            per[name][row["Dispatch_Id"]][cn] += float(row["Counter_Value"])
+    out = [f"# L2 hits and misses per kernel on workload {a.workload}",
+           f"command: {a.command}",
+           f"kernel_source_sha256: {kernel_source_hash()}",
+           f"dispatches per kernel: first {a.skip_first} skipped as warm-up", "",
+           f"{'kernel':<12} {'disp':>4} {'hits/disp':>12} {'misses/disp':>12} {'hit_rate':>8} "
+           f"{'miss_MB':>8}"]
+    for name in sorted(per, key=lambda n: -sum(d.get("TCC_MISS", 0) for d in per[n].values())):
+        dids = sorted(per[name], key=int)[a.skip_first:]
+        if not dids:
+            continue
+        h = sum(per[name][d].get("TCC_HIT", 0.0) for d in dids) / len(dids)
+        m = sum(per[name][d].get("TCC_MISS", 0.0) for d in dids) / len(dids)
+        rate = h / (h + m) if h + m > 0 else float("nan")
+        out.append(f"{name:<12} {len(dids):>4} {h:>12.0f} {m:>12.0f} {100 * rate:>7.1f}% "
+                   f"{m * 128 / 1e6:>8.1f}")
+    out += ["", "miss_MB = misses x 128 B per dispatch (an upper bound: a miss may fetch "
+            "less than a line)"]
+    emit("\n".join(out) + "\n", a.out)
+
+
 def emit(text, out):
     if out:
         with open(out, "w") as f:
@@ -241,8 +277,15 @@ def main(argv=None):
     c.add_argument("--command", required=True)
     c.add_argument("--skip-first", type=int, default=0)
     c.add_argument("--out")
+    l2 = sub.add_parser("l2")
+    l2.add_argument("csv")
+    l2.add_argument("--workload", required=True)
+    l2.add_argument("--command", required=True)
+    l2.add_argument("--skip-first", type=int, default=0)
+    l2.add_argument("--out")
     a = ap.parse_args(argv)
-    {"kernels": cmd_kernels, "traffic": cmd_traffic, "counters": cmd_counters}[a.what](a)
+    {"kernels": cmd_kernels, "traffic": cmd_traffic, "counters": cmd_counters,
+     "l2": cmd_l2}[a.what](a)
 
 
 if __name__ == "__main__":

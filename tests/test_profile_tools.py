@@ -77,3 +77,20 @@ def test_kernels_summary_without_bench_figures(tmp_path):
              "--bench-json", str(bench_json), "--command", "cmd", "--out", str(out)])
     row = [l.split() for l in out.read_text().splitlines() if l.startswith("fwd_bf16")][-1]
     assert row == ["fwd_bf16", "2", "0.9500", "-"]
+
+
+def test_l2_summary(tmp_path):
+    """Hits and misses summed over rows per dispatch; warm-up skipped."""
+    name = "void skv::(anonymous namespace)::fwd_bf16_kernel<128>(skv::FwdArgs)"
+    rows = []
+    for did, (h, m) in ((1, (1.0, 1e9)), (2, (3e6, 1e6)), (3, (3e6, 1e6))):
+        for part in range(2):  # two rows per counter
+            rows.append((did, name, "TCC_HIT_sum", h / 2, 0, 1))
+            rows.append((did, name, "TCC_MISS_sum", m / 2, 0, 1))
+    src = tmp_path / "l2.csv"
+    out = tmp_path / "l2.txt"
+    _write_csv(src, rows)
+    rs.main(["l2", str(src), "--workload", "w", "--command", "cmd", "--skip-first", "1",
+             "--out", str(out)])
+    row = [l.split() for l in out.read_text().splitlines() if l.startswith("fwd_bf16")][0]
+    assert row == ["fwd_bf16", "2", "3000000", "1000000", "75.0%", "128.0"]
