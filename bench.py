@@ -301,7 +301,7 @@ def bench_tiny(args):
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_tiny(w, g, t, ids, flops),
         "context_from_pages": PAGES_CONTEXT,
     }
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def cpu_baseline_tiny(w, g, t, ids, flops):
@@ -484,7 +484,8 @@ def main():
     if args.workload == "ctx1m_merge64":
         return bench_merge64(args)
     if args.workload == "tiny_f32_ctx1k":
-        return bench_tiny(args)
+        print(json.dumps(bench_tiny(args)), flush=True)
+        return
     if args.sweep:
         return run_sweep(args)
     if args.wg_times:
@@ -506,10 +507,11 @@ def _summary(r):
 
 
 def other_configs(args):
-    """Sub-records for the other full-size workloads, timed in the same run:
-    the varlen fwd+bwd job, the 512K-context rank-0 share (forward) and the
-    64-way merge of the 1M-context job (the merge alone, on N(0,1) bf16
-    partials and N(0, 4) LSEs drawn on the device, seeded)."""
+    """Sub-records for the other workloads, timed in the same run: the tiny
+    fp32 job (4 shard forwards and their merge, seed 0), the varlen fwd+bwd
+    job, the 512K-context rank-0 share (forward) and the 64-way merge of the
+    1M-context job (the merge alone, on N(0,1) bf16 partials and N(0, 4)
+    LSEs drawn on the device, seeded)."""
     import argparse as _ap
     import torch
     from block_sparse_split_amd import splitkv as skv
@@ -519,6 +521,12 @@ def other_configs(args):
     sub.no_cpu_baseline = True
     sub.compare_plans = False
     out = {}
+    sub.seed = 0
+    log("sub-record tiny_f32_ctx1k")
+    r = bench_tiny(sub)
+    out["tiny_f32_ctx1k"] = {k: r[k] for k in ("value", "unit", "ms_per_step", "us_per_step",
+                                               "eager_us_per_step", "timed_as", "dtype", "config",
+                                               "lpt")}
     for name, seed in (("varlen8_fwdbwd", 3), ("cp64_rank0_ctx512k", 2)):
         sub.seed = seed
         sub.fwd_only = False
@@ -546,10 +554,14 @@ def other_configs(args):
     ms = e0.elapsed_time(e1) / sub.steps
     nbytes = Op.numel() * 2 + Lp.numel() * 4 + Om.numel() * 2 + Lm.numel() * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
+    from block_sparse_split_amd import shards
+    _, _, _, load = shards.lpt_shards(w, g, w.n_shards)
     out["ctx1m_merge64"] = {"step": "64-way LSE merge", "partials": w.n_shards,
                             "rows": w.nq * w.hq, "head_dim": w.d, "ms": ms,
                             "algorithmic_bytes": nbytes, "gbs": gbs,
-                            "frac_of_hbm_peak": gbs / PEAK_HBM_GBS, "launches": sub.steps}
+                            "frac_of_hbm_peak": gbs / PEAK_HBM_GBS, "launches": sub.steps,
+                            "lpt": {"shard_imbalance_64": float(load.max() / load.mean() - 1),
+                                    "chunk_imbalance_by_bins": plan_imbalances(g, w.tile_k)}}
     del Op, Lp, Om, Lm
     torch.cuda.empty_cache()
     return out
