@@ -72,9 +72,11 @@ typedef enum { SKV_F32 = 0, SKV_BF16 = 1 } skv_dtype;
 /* Last error text on this thread ("" after a successful call). */
 const char* skv_last_error(void);
 
-/* ABI version of this header (bumped on incompatible changes). */
+/* ABI version of this header (bumped on incompatible changes; 2: four
+ * words per workgroup in the clock-stamp buffer, skv_plan_lpt_split and
+ * skv_dq_finalize added). */
 int32_t skv_abi_version(void);
-#define SKV_ABI_VERSION 1
+#define SKV_ABI_VERSION 2
 
 /* ------------------------------------------------------------------------
  * Planner (host only, synchronous, deterministic).
