@@ -236,10 +236,24 @@ def bench_tiny(args):
     Om = torch.empty((w.nq, w.hq, w.d), dtype=torch.float32, device="cuda")
     Lm = torch.empty((w.nq, w.hq), dtype=torch.float32, device="cuda")
 
+    # the shards are independent (on a real job, different ranks): their
+    # forwards run concurrently on streams of their own, then the merge
+    side = [torch.cuda.Stream() for _ in parts]
+
     def step():
+        main = torch.cuda.current_stream()
+        start = torch.cuda.Event()
+        start.record(main)
+        done = []
         for r, (sh, K, V) in enumerate(parts):
+            side[r].wait_event(start)
             kd, vd = (Kd, Vd) if r == 0 else (None, None)
-            sh.fwd(Q, K, V, kd, vd, Op[r], Lp[r])
+            sh.fwd(Q, K, V, kd, vd, Op[r], Lp[r], side[r])
+            ev = torch.cuda.Event()
+            ev.record(side[r])
+            done.append(ev)
+        for ev in done:
+            main.wait_event(ev)
         skv.skv_merge_lse(Op, Lp, Om, Lm)
 
     for _ in range(max(1, args.warmup)):
@@ -293,7 +307,7 @@ def bench_tiny(args):
         "config": {"workload": w.name, "context": g.ctx, "draft_queries": w.nq,
                    "anchor_blocks": w.nb, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d,
                    "chunk": w.chunk, "shards": w.n_shards, "seed": args.seed,
-                   "step": "4 shard forwards (fp32) + 4-way merge"},
+                   "step": "4 shard forwards (fp32, concurrent streams) + 4-way merge"},
         "lpt": {"shard_imbalance_4": float(load.max() / load.mean() - 1)},
         "roofline": {"bound": "latency", "achieved": value, "peak": PEAK_F32_TFLOPS,
                      "unit": "TFLOP/s", "frac": value / PEAK_F32_TFLOPS, "kernel": "step",
