@@ -21,9 +21,13 @@
 // bf16 in place and feeds O^T += V^T P^T directly as the B operand; the V^T
 // operand comes from transposed LDS reads whose key order matches the
 // accumulator layout of S^T, so no register transpose is needed.  The
-// online softmax works in base 2 with the scale folded into one FMA and
-// rescales O only when the running maximum grows by more than 2^8, which is
-// exact (the same maximum is used for O and for the sum).  Tiles that
+// online softmax works in base 2 with the scale folded into one FMA.  It
+// first exponentiates against the maximum already in use and keeps the
+// result if no weight exceeds 2^16; only otherwise (and at a row's first
+// visible keys) does it take the step's row maximum, and it rescales O only
+// where that maximum grew by more than 2^8.  Both are exact: the same
+// maximum is used for O and for the sum, and it never exceeds the true
+// running maximum, so the sum stays at least 1.  Tiles that
 // straddle an anchor bound are masked per element; fully visible tiles skip
 // the mask, invisible ones skip the MFMAs.
 #include "launch.h"
@@ -273,31 +277,46 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
               if (kc < lo4 || kc >= hi4) sacc[kb][r] = kNegInf;
             }
         }
-        float mx = kNegInf;
+        // P = 2^(c s - m_used) with the maximum already in use: valid while
+        // every row has a finite m_used and no P exceeds 2^16, which the
+        // lane's partial sum bounds; otherwise the row maximum is taken and
+        // O is rescaled where it grew by more than 2^8.
+        auto exp_pass = [&](float msub) {
+          float ls = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-        mx = max_xor32(mx);
-        const float mt = mx * c;
-        const bool need = mt > m_used + 8.0f;
-        if (__any(need)) {
-          const float alpha = need ? exp2_fast(m_used - mt) : 1.0f;
-          l *= alpha;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-          if (need) m_used = mt;
-        }
-        const float msub = m_used == kNegInf ? 0.f : m_used;
+            for (int r = 0; r < 16; ++r) {
+              const float pv_ = exp2_fast(fmaf(sacc[kb][r], c, -msub));
+              ls += pv_;
+              pf[kb][r >> 3][r & 7] = f32_to_bf16(pv_);
+            }
+          return ls;
+        };
         float ls = 0.f;
+        bool slow = __any(m_used == kNegInf);
+        if (!slow) {
+          ls = exp_pass(m_used);
+          slow = __any(!(ls <= 65536.f));
+        }
+        if (slow) {
+          float mx = kNegInf;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pv_ = exp2_fast(fmaf(sacc[kb][r], c, -msub));
-            ls += pv_;
-            pf[kb][r >> 3][r & 7] = f32_to_bf16(pv_);
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+          mx = max_xor32(mx);
+          const float mt = mx * c;
+          const bool need = mt > m_used + 8.0f;
+          if (__any(need)) {
+            const float alpha = need ? exp2_fast(m_used - mt) : 1.0f;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+            if (need) m_used = mt;
           }
+          ls = exp_pass(m_used == kNegInf ? 0.f : m_used);
+        }
         l += ls;
       }
     }

@@ -18,12 +18,13 @@ ABS_TOL = 2e-2
 REL_TOL = 2e-2  # of max |reference|
 
 
-def check_grad(got, want, what):
+def check_grad(got, want, what, abs_tol=ABS_TOL):
     got = got.float().cpu().numpy().astype(np.float64) if torch.is_tensor(got) else got
     assert np.all(np.isfinite(got)), f"{what}: non-finite"
     err = np.abs(got - want).max(initial=0.0)
     scale = np.abs(want).max(initial=0.0)
-    assert err <= ABS_TOL, f"{what}: max-abs {err:.3g} > {ABS_TOL}"
+    if abs_tol is not None:
+        assert err <= abs_tol, f"{what}: max-abs {err:.3g} > {abs_tol}"
     assert err <= REL_TOL * scale + 1e-7, f"{what}: max-abs {err:.3g} vs max|ref| {scale:.3g}"
     return err, scale
 
@@ -93,6 +94,51 @@ def test_fwd_then_bwd_chain_small(seed):
     _, _, want = oracle_fwd_bwd(w, g, t, allc, True)
     for name, a, b in zip(("dQ", "dK", "dV", "dKd", "dVd"), got, want):
         check_grad(a, b, name)
+
+
+@pytest.mark.parametrize("seed,n_wg", [(8, 1), (9, 64)])
+def test_fwd_bwd_wide_logits(seed, n_wg):
+    """Logits that grow along the context: key rows at position p are scaled
+    by 2^min(5, p // 600) (a power of two, so the bf16 inputs stay exact).
+    Each row's running maximum then rises by tens of units (log2) inside one
+    work item, which drives the forward's rescale of O and its recomputation
+    of P, and puts weights far below the maximum next to ones near it.
+
+    The bar follows from the arithmetic, because the fp32 error of S grows
+    with the logits: S sums d exact bf16 products in fp32, so it errs by at
+    most eps_s = d 2^-24 max|q| max|k|; a weight 2^(c S - m) then errs by a
+    factor of at most 2^(c eps_s) in numerator and denominator, P is rounded
+    to bf16 (8 significant bits: at most 2^-8 of the value) and so is O
+    (2^-8 |O|).  LSE errs by at most scale eps_s.  A missed or wrong rescale
+    is off by O(1) in both.  The gradients grow with the inputs (dQ reaches
+    about 1e2), so they are held to the relative bar alone."""
+    w, g, t = _small(seed)
+    pos = shards.shard_rows(g, t.chunk_ids)
+    t.K *= (2.0 ** np.minimum(5, pos // 600)).astype(np.float32)[:, None, None]
+    allc = np.arange(len(g.chunk_pos))
+    announce("fwd+bwd wide logits", seed, n_wg)
+    O, L, _ = gpu_fwd(w, g, t, allc, True, n_wg=n_wg)
+    Oo, Lo, want = oracle_fwd_bwd(w, g, t, allc, True)
+    assert np.nanmax(Lo) > 100.0   # the logits really are wide
+    scale = wl.softmax_scale(w.d)
+    c = scale * np.log2(np.e)
+    kmax = max(np.linalg.norm(t.K, axis=-1).max(), np.linalg.norm(t.Kd, axis=-1).max())
+    eps_s = w.d * 2.0 ** -24 * np.linalg.norm(t.Q, axis=-1).max() * kmax
+    vmax = max(np.abs(t.V).max(), np.abs(t.Vd).max())
+    o_bar = vmax * (2.0 ** -8 + 2 * np.log(2) * c * eps_s) + 2.0 ** -8 * np.abs(Oo).max()
+    l_bar = scale * eps_s + 1e-5
+    Og = O.float().cpu().numpy().astype(np.float64)
+    Lg = L.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(Lg), np.isneginf(Lo))
+    fin = np.isfinite(Lo)
+    dl = np.abs(Lg[fin] - Lo[fin]).max()
+    do = np.abs(Og - Oo).max()
+    announce("O err", do, "bar", o_bar, "LSE err", dl, "bar", l_bar)
+    assert dl <= l_bar, f"LSE max-abs {dl:.3g} > {l_bar:.3g}"
+    assert do <= o_bar, f"O max-abs {do:.3g} > {o_bar:.3g}"
+    got = gpu_bwd(w, g, t, allc, True, O, L, n_wg=n_wg)
+    for name, a, b in zip(("dQ", "dK", "dV", "dKd", "dVd"), got, want):
+        check_grad(a, b, f"wide logits {name}", abs_tol=None)
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(4, 4, 64), (16, 1, 128), (8, 4, 128), (16, 2, 64)])
