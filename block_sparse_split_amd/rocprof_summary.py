@@ -11,6 +11,10 @@ sources.
               SQ/GRBM counters listed in MFMA_COUNTERS
   l2       -- L2 (TCC) hits and misses per dispatch of each kernel from one
               `--pmc TCC_HIT_sum TCC_MISS_sum` run
+  balance  -- the table of a `bench.py --wg-times` JSON line (planned against
+              realised workgroup imbalance, placement and per-XCD means)
+  sweep    -- the table of a `bench.py --sweep context|budget` JSON line
+  plans    -- the table of a `bench.py --compare-plans` JSON line
 
 Usage:
   python -m block_sparse_split_amd.rocprof_summary kernels STATS_CSV \\
@@ -22,6 +26,10 @@ Usage:
       --workload NAME --command "..." [--skip-first N] [--out FILE]
   python -m block_sparse_split_amd.rocprof_summary l2 CSV \\
       --workload NAME --command "..." [--skip-first N] [--out FILE]
+  python -m block_sparse_split_amd.rocprof_summary balance|plans JSON \\
+      --command "..." [--out FILE]
+  python -m block_sparse_split_amd.rocprof_summary sweep JSON --over "..." \\
+      --command "..." [--out FILE]
 """
 import argparse
 import csv
@@ -247,6 +255,73 @@ def cmd_l2(a):
     emit("\n".join(out) + "\n", a.out)
 
 
+def _last_json(path):
+    return json.loads(open(path).read().strip().splitlines()[-1])
+
+
+def cmd_balance(a):
+    r = _last_json(a.json)
+    out = [f"# per-workgroup balance of the forward, dQ and dK/dV kernels on workload "
+           f"{r['workload']}",
+           f"command: {a.command}",
+           f"kernel_source_sha256: {kernel_source_hash()}",
+           f"clock: {r['clock']}; workgroups: {r['workgroups']}; steps: {r['steps']}", "",
+           "kernel      planned  realised  mean_us  span_us  on XCD (w+c)%8  CUs   "
+           "mean time per XCD (XCC_ID register), relative"]
+    for k, v in r["kernels"].items():
+        m = v["mean_workgroup_us"]
+        rel = " ".join(f"{(x / m - 1) * 100:+.1f}%" for x in v["xcd_mean_us"])
+        out.append(f"{k:<10} {v['planned_imbalance'] * 100:7.2f}% "
+                   f"{v['realized_imbalance_median'] * 100:8.2f}% {m:8.1f} "
+                   f"{v['kernel_span_us_median']:8.1f}  {v['on_xcd_w_plus_c_mod_8'] * 100:5.1f}% "
+                   f"(c={v['xcd_rotation_per_run'][0]})  {v['distinct_cus_per_run']:4d}   {rel}")
+    out += ["", "planned = max/mean - 1 of the plan's workgroup loads (time units); realised = "
+            "median over",
+            "the steps of max/mean - 1 of the workgroups' measured durations; span = last end - "
+            "first start.",
+            "on XCD (w+c)%8: share of workgroups w whose XCC_ID is (w + c) mod 8 for one "
+            "rotation c per",
+            "launch (c printed for the first step); CUs: distinct (XCD, SE, CU) triples per "
+            "launch."]
+    emit("\n".join(out) + "\n", a.out)
+
+
+def cmd_sweep(a):
+    r = _last_json(a.json)
+    out = [f"# fwd+bwd throughput over {a.over} (bf16, 32 q-heads / 8 kv-heads, d 128, seed 1)",
+           f"command: {a.command}",
+           f"kernel_source_sha256: {kernel_source_hash()}", "",
+           "context  draft_q  ms/step  TFLOP/s fwd+bwd  frac bf16  TFLOP/s fwd  fwd_ms  "
+           "item imb  plan_ms"]
+    for p in r["points"]:
+        out.append(f"{p['context']:7d} {p['draft_queries']:8d} {p['ms_per_step']:8.3f} "
+                   f"{p['tflops_fwd_bwd']:16.1f} {p['frac_of_bf16_peak']:10.3f} "
+                   f"{p['tflops_fwd']:12.1f} {p['fwd_ms']:7.3f} "
+                   f"{p['item_imbalance_256cu'] * 100:8.2f}% {p['plan_ms']:8.3f}")
+    out += ["", "eager launches with one HIP event pair per kernel; the step is the forward "
+            "partial, its",
+            "split-tile merge and the backward; item imb = planned imbalance of the forward "
+            "items (time units)."]
+    emit("\n".join(out) + "\n", a.out)
+
+
+def cmd_plans(a):
+    r = _last_json(a.json)
+    c = r["in_gpu_plan_comparison"]
+    out = ["# in-GPU item plan: LPT with splitting against a contiguous equal-count plan of "
+           "the same items",
+           f"workload: {r['config']['workload']} (seed {r['config']['seed']})",
+           f"command: {a.command}",
+           f"kernel_source_sha256: {kernel_source_hash()}", "",
+           "kernel     lpt_ms  contiguous_ms  gain"]
+    for k in ("fwd_bf16", "bwd_dq"):
+        out.append(f"{k:<9} {c[k]['lpt_ms']:7.3f} {c[k]['contiguous_ms']:14.3f} "
+                   f"{c[k]['gain']:5.2f}x")
+    out += ["", c["plan"] + "; items sorted by (kv head, query tile, first tile), one run per "
+            "workgroup;", "both plans compute every item exactly once, only the queues differ."]
+    emit("\n".join(out) + "\n", a.out)
+
+
 def emit(text, out):
     if out:
         with open(out, "w") as f:
@@ -283,9 +358,16 @@ def main(argv=None):
     l2.add_argument("--command", required=True)
     l2.add_argument("--skip-first", type=int, default=0)
     l2.add_argument("--out")
+    for name in ("balance", "plans", "sweep"):
+        b = sub.add_parser(name)
+        b.add_argument("json")
+        b.add_argument("--command", required=True)
+        if name == "sweep":
+            b.add_argument("--over", required=True, help="what the sweep varies, for the title")
+        b.add_argument("--out")
     a = ap.parse_args(argv)
     {"kernels": cmd_kernels, "traffic": cmd_traffic, "counters": cmd_counters,
-     "l2": cmd_l2}[a.what](a)
+     "l2": cmd_l2, "balance": cmd_balance, "sweep": cmd_sweep, "plans": cmd_plans}[a.what](a)
 
 
 if __name__ == "__main__":

@@ -89,6 +89,48 @@ def test_f32_d128_and_ragged():
         compare(O, L, Oo, Lo, "f32", f"shard {r}")
 
 
+@pytest.mark.parametrize("d,n_wg", [(64, 1), (128, 7)])
+def test_f32_wide_logits(d, n_wg):
+    """The fp32 path under logits that grow along the context (key rows at
+    position p scaled by 2^min(5, p // 300), exact in fp32), so each row's
+    running maximum rises by tens of units (log2) inside one work item and
+    the rescale of O runs mid-item.  The bar follows from the arithmetic:
+    S sums d fp32 products, each rounded once, so it errs by at most eps_s =
+    (d + 1) 2^-24 max|q| max|k|, a factor of at most 2^(c eps_s) on each
+    weight in numerator and denominator; O and the sum add n fp32 terms
+    each (n visible keys, at most (n - 1) 2^-24 of the sum of magnitudes);
+    LSE errs by at most scale eps_s plus the sum's relative error.  A missed
+    or wrong rescale is off by O(1)."""
+    w = wl.scaled(wl.WORKLOADS["tiny_f32_ctx1k"], hq=4, hkv=2, d=d, ctx=2048, chunk=128,
+                  blocks_per_seq=6, anchor_lo=256, anchor_hi=2048)
+    w, g, t = wl.make(w, 12)
+    pos = shards.shard_rows(g, t.chunk_ids)
+    t.K *= (2.0 ** np.minimum(5, pos // 300)).astype(np.float32)[:, None, None]
+    allc = np.arange(len(g.chunk_pos))
+    announce("f32 wide logits", d, n_wg)
+    O, L, _ = gpu_fwd(w, g, t, allc, True, n_wg=n_wg)
+    Oo, Lo = oracle_partial(w, g, t, allc, True)
+    assert np.nanmax(Lo) > 100.0
+    scale = wl.softmax_scale(d)
+    c = scale * np.log2(np.e)
+    kmax = max(np.linalg.norm(t.K, axis=-1).max(), np.linalg.norm(t.Kd, axis=-1).max())
+    eps_s = (d + 1) * 2.0 ** -24 * np.linalg.norm(t.Q, axis=-1).max() * kmax
+    n = g.ctx + 16
+    vmax = max(np.abs(t.V).max(), np.abs(t.Vd).max())
+    sum_rel = (n - 1) * 2.0 ** -24
+    o_bar = vmax * (2 * np.log(2) * c * eps_s + 2 * sum_rel) + 1e-6
+    l_bar = scale * eps_s + sum_rel + 1e-6
+    Og = O.cpu().numpy().astype(np.float64)
+    Lg = L.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(Lg), np.isneginf(Lo))
+    fin = np.isfinite(Lo)
+    dl = np.abs(Lg[fin] - Lo[fin]).max()
+    do = np.abs(Og - Oo).max()
+    announce("O err", do, "bar", o_bar, "LSE err", dl, "bar", l_bar)
+    assert dl <= l_bar, f"LSE max-abs {dl:.3g} > {l_bar:.3g}"
+    assert do <= o_bar, f"O max-abs {do:.3g} > {o_bar:.3g}"
+
+
 @pytest.mark.parametrize("seed", [3, 4])
 def test_bf16_varlen_small(seed):
     """Packed sequences with ragged chunk tails and late-skewed anchors."""

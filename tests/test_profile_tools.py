@@ -94,3 +94,46 @@ def test_l2_summary(tmp_path):
              "--out", str(out)])
     row = [l.split() for l in out.read_text().splitlines() if l.startswith("fwd_bf16")][0]
     assert row == ["fwd_bf16", "2", "3000000", "1000000", "75.0%", "128.0"]
+
+
+def _json_line(path, rec):
+    import json
+    path.write_text("some log line\n" + json.dumps(rec) + "\n")
+
+
+def test_bench_tables(tmp_path):
+    """The balance, sweep and plan tables read the last JSON line of a bench
+    run and print its figures as percentages / relative XCD means."""
+    k = {"planned_imbalance": 0.005, "realized_imbalance_median": 0.04,
+         "mean_workgroup_us": 100.0, "kernel_span_us_median": 110.0,
+         "xcd_mean_us": [101.0, 99.0] + [100.0] * 6, "on_xcd_w_plus_c_mod_8": 1.0,
+         "xcd_rotation_per_run": [3, 3], "distinct_cus_per_run": 256}
+    src = tmp_path / "wg.json"
+    _json_line(src, {"workload": "w", "clock": "c", "workgroups": 256, "steps": 2,
+                     "kernels": {"bwd_dq": k}})
+    out = tmp_path / "b.txt"
+    rs.main(["balance", str(src), "--command", "cmd", "--out", str(out)])
+    row = [l.split() for l in out.read_text().splitlines() if l.startswith("bwd_dq")][0]
+    assert row[1:5] == ["0.50%", "4.00%", "100.0", "110.0"]
+    assert row[5:7] == ["100.0%", "(c=3)"] and row[7] == "256"
+    assert row[8:10] == ["+1.0%", "-1.0%"]
+
+    src = tmp_path / "sw.json"
+    _json_line(src, {"points": [{"context": 4096, "draft_queries": 512, "ms_per_step": 0.5,
+                                 "tflops_fwd_bwd": 400.0, "frac_of_bf16_peak": 0.16,
+                                 "tflops_fwd": 500.0, "fwd_ms": 0.1,
+                                 "item_imbalance_256cu": 0.02, "plan_ms": 0.3}]})
+    rs.main(["sweep", str(src), "--over", "context", "--command", "cmd", "--out", str(out)])
+    text = out.read_text()
+    assert text.startswith("# fwd+bwd throughput over context")
+    row = [l.split() for l in text.splitlines() if l.startswith("   4096")][0]
+    assert row == ["4096", "512", "0.500", "400.0", "0.160", "500.0", "0.100", "2.00%", "0.300"]
+
+    src = tmp_path / "cmp.json"
+    cmp = {"plan": "contiguous runs",
+           "fwd_bf16": {"lpt_ms": 1.0, "contiguous_ms": 1.5, "gain": 1.5},
+           "bwd_dq": {"lpt_ms": 2.0, "contiguous_ms": 3.0, "gain": 1.5}}
+    _json_line(src, {"config": {"workload": "w", "seed": 1}, "in_gpu_plan_comparison": cmp})
+    rs.main(["plans", str(src), "--command", "cmd", "--out", str(out)])
+    rows = [l.split() for l in out.read_text().splitlines() if l.startswith(("fwd_", "bwd_"))]
+    assert rows == [["fwd_bf16", "1.000", "1.500", "1.50x"], ["bwd_dq", "2.000", "3.000", "1.50x"]]
