@@ -38,12 +38,16 @@ namespace {
 // rho = token * G + h % G.  Writes, at [g * Nq * G + rho]: -D (the dP
 // accumulators start from it, so they end as dP - D), LSE * log2(e) (+inf
 // for a row that sees no key) and the row's visible context interval
-// [lo, anchor) of its anchor block.
+// [lo, anchor) of its anchor block.  It also zeroes the per-XCD queue
+// counters of the dQ and dK/dV kernels that follow it on the stream.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const int32_t* sched, const __bf16* O,
                                                       const __bf16* dO, const float* LSE,
                                                       float* nDrm, float* L2rm, int32_t* LOrm,
-                                                      int32_t* HIrm, int64_t rows, int hq, int G) {
+                                                      int32_t* HIrm, int64_t rows, int hq, int G,
+                                                      uint32_t* xcd_count) {
+  if (xcd_count != nullptr && blockIdx.x == 0 && threadIdx.x < 2 * kXcds)
+    xcd_count[threadIdx.x] = 0u;
   constexpr int TPR = D / 8;
   constexpr int RPB = 256 / TPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
@@ -143,7 +147,8 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
   const sched_t tiles = S + S[H_OFF_TILES];
   const sched_t items = S + S[H_OFF_ITEMS];
   const sched_t queue = S + S[H_OFF_QUEUE];
-  const int qbeg = S[S[H_OFF_QOFF] + blockIdx.x], qend = S[S[H_OFF_QOFF] + blockIdx.x + 1];
+  const int vq = claim_queue(S, a.xcd_count);
+  const int qbeg = S[S[H_OFF_QOFF] + vq], qend = S[S[H_OFF_QOFF] + vq + 1];
   const float c = a.scale * kLog2e;
   const __bf16* Qg = static_cast<const __bf16*>(a.Q);
   const __bf16* dOg = static_cast<const __bf16*>(a.dO);
@@ -293,7 +298,7 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
         }
     }
   }
-  wg_clock_record(a.wg_clock_dq, t_wg);
+  wg_clock_record(a.wg_clock_dq, t_wg, vq);
 }
 
 // Sum the dQ partial slots of split query tiles.
@@ -359,7 +364,7 @@ struct KvCfg {
 // The two roles run separate copies of the whole item loop, so that the
 // compiler never keeps one role's loop state live in the other's.
 template <int D, bool PW>
-__device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
+__device__ __forceinline__ void dkdv_role(const BwdArgs& a, int vq) {
   using C = KvCfg<D>;
   // distinct (empty) markers keep the optimiser from merging the two roles'
   // code back into one path with selects
@@ -380,7 +385,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
   const sched_t tiles = S + S[H_OFF_TILES];
   const sched_t kvs = S + S[H_OFF_KV];
   const sched_t queue = S + S[H_OFF_KVQUEUE];
-  const int qbeg = S[S[H_OFF_KVQOFF] + blockIdx.x], qend = S[S[H_OFF_KVQOFF] + blockIdx.x + 1];
+  const int qbeg = S[S[H_OFF_KVQOFF] + vq], qend = S[S[H_OFF_KVQOFF] + vq + 1];
   const float c = a.scale * kLog2e;
   const __bf16* Qg = static_cast<const __bf16*>(a.Q);
   const __bf16* dOg = static_cast<const __bf16*>(a.dO);
@@ -662,9 +667,10 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a) {
 template <int D>
 __global__ __launch_bounds__(KvCfg<D>::kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const uint64_t t_wg = wg_clock_now();
-  if (threadIdx.x < 256) dkdv_role<D, true>(a);
-  else dkdv_role<D, false>(a);
-  wg_clock_record(a.wg_clock_kv, t_wg);
+  const int vq = claim_queue(sched_const(a.sched), a.xcd_count ? a.xcd_count + kXcds : nullptr);
+  if (threadIdx.x < 256) dkdv_role<D, true>(a, vq);
+  else dkdv_role<D, false>(a, vq);
+  wg_clock_record(a.wg_clock_kv, t_wg, vq);
 }
 
 template <int D>
@@ -673,7 +679,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   constexpr int RPB = 256 / (D / 8);
   SKV_LAUNCH("bwd_pre", bwd_pre_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256), 0, s,
              a.sched, static_cast<const __bf16*>(a.O), static_cast<const __bf16*>(a.dO), a.LSE,
-             a.ws_nD, a.ws_L2, a.ws_LO, a.ws_HI, rows, a.hq, a.hq / a.hkv);
+             a.ws_nD, a.ws_L2, a.ws_LO, a.ws_HI, rows, a.hq, a.hq / a.hkv, a.xcd_count);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static LdsLimit lds_dq, lds_kv;

@@ -119,7 +119,8 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
   const sched_t tiles = S + S[H_OFF_TILES];
   const sched_t items = S + S[H_OFF_ITEMS];
   const sched_t queue = S + S[H_OFF_QUEUE];
-  const int qbeg = S[S[H_OFF_QOFF] + blockIdx.x], qend = S[S[H_OFF_QOFF] + blockIdx.x + 1];
+  const int vq = claim_queue(S, a.xcd_count);
+  const int qbeg = S[S[H_OFF_QOFF] + vq], qend = S[S[H_OFF_QOFF] + vq + 1];
   const float c = a.scale * kLog2e;
   const __bf16* Qg = static_cast<const __bf16*>(a.Q);
   const uint32_t lds0 = lds_addr(smem);
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(FwdCfg<D>::kThreads, 1) void fwd_bf16_kernel(FwdArg
       }
     }
   }
-  wg_clock_record(a.wg_clock, t_wg);
+  wg_clock_record(a.wg_clock, t_wg, vq);
 }
 
 // ---------------------------------------------------------------------------
@@ -397,7 +398,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
   const sched_t tiles = S + S[H_OFF_TILES];
   const sched_t items = S + S[H_OFF_ITEMS];
   const sched_t queue = S + S[H_OFF_QUEUE];
-  const int qbeg = S[S[H_OFF_QOFF] + blockIdx.x], qend = S[S[H_OFF_QOFF] + blockIdx.x + 1];
+  const int vq = claim_queue(S, a.xcd_count);
+  const int qbeg = S[S[H_OFF_QOFF] + vq], qend = S[S[H_OFF_QOFF] + vq + 1];
   const float c = a.scale * kLog2e;
   const float* Qg = static_cast<const float*>(a.Q);
 
@@ -560,8 +562,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_f32_kernel(FwdArgs a) {
   }
 }
 
+// Zeroes the forward's per-XCD queue counters before a launch that claims
+// queues by XCD.
+__global__ __launch_bounds__(64) void xcd_reset_kernel(uint32_t* count) {
+  if (threadIdx.x < kXcds) count[threadIdx.x] = 0u;
+}
+
 template <int D>
 hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
+  if (a.xcd_count != nullptr) {
+    SKV_LAUNCH("xcd_reset", xcd_reset_kernel, dim3(1), dim3(64), 0, stream, a.xcd_count);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (a.dtype_bf16) {
     constexpr int bytes = FwdCfg<D>::kLdsBytes;
     static LdsLimit lds;

@@ -241,6 +241,194 @@ struct SplitJob {
   }
 };
 
+// The same placement over bins of unequal speed (work per unit time): bin
+// b has speed speed[b] and its time is load / speed.  Pieces in the same
+// order go to the bin of least time (ties: lower bin), with the cut rule
+// above against a target time T (a bin's room is (T - time) * speed).
+// With every speed equal this is the placement above.
+struct SpeedJob {
+  std::vector<int64_t> extra;
+  std::vector<int32_t> steps;
+  std::vector<double> speed;
+  int64_t item_cost = 0, step_cost = 0;
+
+  int64_t cost(int32_t u, int32_t k0) const {
+    return item_cost + (k0 == 0 ? extra[u] : 0) + step_cost * (steps[u] - k0);
+  }
+
+  std::vector<Piece> pass(double target, std::vector<int64_t>* load_out) const {
+    struct Pending {
+      int64_t cost;
+      int32_t unit, k0;
+      bool operator<(const Pending& o) const {
+        if (cost != o.cost) return cost < o.cost;
+        if (unit != o.unit) return unit > o.unit;
+        return k0 > o.k0;
+      }
+    };
+    std::priority_queue<Pending> pend;
+    for (int32_t u = 0; u < int32_t(steps.size()); ++u) pend.push({cost(u, 0), u, 0});
+    const int32_t m = int32_t(speed.size());
+    std::vector<int64_t> load(m, 0);
+    std::vector<double> time(m, 0.0);
+    std::vector<Piece> out;
+    while (!pend.empty()) {
+      const Pending pc = pend.top();
+      pend.pop();
+      int32_t b = 0;
+      for (int32_t j = 1; j < m; ++j)
+        if (time[j] < time[b]) b = j;
+      const int32_t n = steps[pc.unit];
+      int32_t k_end = n;
+      int64_t placed = pc.cost;
+      const int64_t head = item_cost + (pc.k0 == 0 ? extra[pc.unit] : 0);
+      const double room = (target - time[b]) * speed[b];
+      if (time[b] + double(pc.cost) / speed[b] > target && n - pc.k0 > 1 &&
+          room >= double(head + step_cost)) {
+        int64_t acc = head;
+        int32_t k = pc.k0;
+        while (k < n && double(acc + step_cost) <= room) acc += step_cost, ++k;
+        if (k < n) {
+          k_end = k;
+          placed = acc;
+          pend.push({cost(pc.unit, k), pc.unit, k});
+        }
+      }
+      out.push_back({pc.unit, pc.k0, k_end, b, placed});
+      load[b] += placed;
+      time[b] = double(load[b]) / speed[b];
+    }
+    if (load_out) *load_out = std::move(load);
+    return out;
+  }
+
+  // The target whose pass finishes its slowest bin first, among T0 (1 +
+  // i / 400), i = 0 .. 16, with T0 = total cost / total speed, and the
+  // automatic target below (ties: the earlier candidate).
+  double best_target() const {
+    double total = 0, sp = 0;
+    for (int32_t u = 0; u < int32_t(steps.size()); ++u) total += double(cost(u, 0));
+    for (double v : speed) sp += v;
+    const double t0 = total / sp;
+    double best = auto_target(), best_end = finish(best);
+    for (int i = 0; i <= 16; ++i) {
+      const double t = t0 * (1.0 + i / 400.0);
+      const double e = finish(t);
+      if (e < best_end) best = t, best_end = e;
+    }
+    return best;
+  }
+
+  // time of the slowest bin of a pass at target T
+  double finish(double target) const {
+    std::vector<int64_t> load;
+    pass(target, &load);
+    double e = 0;
+    for (size_t b = 0; b < load.size(); ++b) e = std::max(e, double(load[b]) / speed[b]);
+    return e;
+  }
+
+  // T starts at total cost / total speed and is reset to the time a pass
+  // placed per unit of speed plus half an item on a bin of mean speed,
+  // until it repeats (at most four passes).
+  double auto_target() const {
+    double total = 0, sp = 0;
+    for (int32_t u = 0; u < int32_t(steps.size()); ++u) total += double(cost(u, 0));
+    for (double v : speed) sp += v;
+    const double half_item = 0.5 * double(item_cost) * double(speed.size()) / sp;
+    double target = total / sp;
+    for (int p = 0; p < 4; ++p) {
+      double placed = 0;
+      for (const Piece& pc : pass(target, nullptr)) placed += double(pc.cost);
+      const double next = placed / sp + half_item;
+      if (std::abs(next - target) <= 1e-9 * target) break;
+      target = next;
+    }
+    return target;
+  }
+};
+
+// Work shares of XCD classes of unequal total speed.  Class c (total bin
+// speed S_c) should hold total * S_c / sum S.  Each class above its share
+// by more than `tol` gives away units, largest first, each that still fits
+// the excess (so the small ones stay to pack its own workgroups); then,
+// with `steps`, the tail of its smallest remaining unit of two or more
+// steps that brings the excess nearest to zero (the tail pays `tail_fixed`
+// again).  Units given away go, largest first, to the class furthest below
+// its share.  Returns the new class of every unit (units appended by cuts
+// included) and fills *tails with (unit, steps kept) per cut.
+std::vector<int32_t> share_classes(std::vector<int64_t> cost, const std::vector<int32_t>& home,
+                                   const std::vector<double>& cls_speed,
+                                   const std::vector<int32_t>* steps, int64_t step_cost,
+                                   int64_t tail_fixed, double tol,
+                                   std::vector<std::pair<int32_t, int32_t>>* tails) {
+  const int32_t n_cls = int32_t(cls_speed.size());
+  std::vector<int32_t> where = home;
+  std::vector<double> have(n_cls, 0.0), want(n_cls, 0.0);
+  double total = 0, sp = 0;
+  for (size_t i = 0; i < cost.size(); ++i) have[home[i]] += double(cost[i]), total += double(cost[i]);
+  for (double v : cls_speed) sp += v;
+  for (int32_t c = 0; c < n_cls; ++c) want[c] = total * cls_speed[c] / sp;
+  std::vector<int32_t> given;
+  for (int32_t c = 0; c < n_cls; ++c) {
+    double excess = have[c] - want[c];
+    if (excess <= tol) continue;
+    // the class's own units (tails cut for earlier classes, appended to
+    // `cost`, are already given away)
+    std::vector<int32_t> ids;
+    for (size_t i = 0; i < home.size(); ++i)
+      if (home[i] == c) ids.push_back(int32_t(i));
+    std::stable_sort(ids.begin(), ids.end(), [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
+    std::vector<int32_t> kept;
+    for (int32_t i : ids) {
+      if (double(cost[i]) <= excess) {
+        given.push_back(i);
+        excess -= double(cost[i]);
+        have[c] -= double(cost[i]);
+      } else {
+        kept.push_back(i);
+      }
+    }
+    if (steps && excess > tol) {
+      for (auto it = kept.rbegin(); it != kept.rend(); ++it) {
+        const int32_t u = *it, n = (*steps)[u];
+        if (n < 2) continue;
+        // tail of t steps: moves tail_fixed + t * step_cost, the head keeps
+        // the rest (the unit's cost less t * step_cost)
+        const int64_t t = std::min<int64_t>(n - 1, std::max<int64_t>(
+            1, std::llround((excess - double(tail_fixed)) / double(step_cost))));
+        const int64_t moved = tail_fixed + t * step_cost;
+        tails->push_back({u, int32_t(n - t)});
+        cost[u] -= t * step_cost;
+        cost.push_back(moved);
+        where.push_back(c);
+        given.push_back(int32_t(cost.size() - 1));
+        have[c] -= double(t * step_cost);
+        break;
+      }
+    }
+  }
+  std::stable_sort(given.begin(), given.end(), [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
+  for (int32_t i : given) {
+    int32_t best = -1;
+    for (int32_t c = 0; c < n_cls; ++c)
+      if (best < 0 || want[c] - have[c] > want[best] - have[best]) best = c;
+    where[i] = best;
+    have[best] += double(cost[i]);
+  }
+  return where;
+}
+
+// Largest load scaled to a bin of mean speed: with it, max / (total / m) - 1
+// is the plan's imbalance in time.
+int64_t max_time_load(const std::vector<int64_t>& load, const std::vector<double>& speed) {
+  double sp = 0, worst = 0;
+  for (double v : speed) sp += v;
+  const double mean = sp / double(speed.size());
+  for (size_t b = 0; b < load.size(); ++b) worst = std::max(worst, double(load[b]) * mean / speed[b]);
+  return int64_t(std::llround(worst));
+}
+
 std::atomic<int32_t> g_cu_cache[64];
 
 int32_t device_cu_count() {
@@ -383,12 +571,33 @@ std::vector<std::vector<int32_t>> place(int32_t n_items, int32_t n_wg,
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
-                    int64_t capacity, skv_schedule_info* info) {
+// xcd_speed: NULL, or [3][kXcds] relative speeds (work per unit time) of
+// each XCD in the forward, dQ and dK/dV kernels; with it, queue v is
+// planned at the speed of XCD v % kXcds and the kernels claim queues by the
+// XCD they run on.
+void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
+                    int32_t* image, int64_t capacity, skv_schedule_info* info) {
   require(info != nullptr, "info must not be NULL");
   const Geometry g = check_problem(p);
   if (n_wg == 0) n_wg = device_cu_count();
   require(n_wg >= 1 && n_wg <= 65536, "n_workgroups must be in [1, 65536]");
+  const bool xcd = xcd_speed != nullptr;
+  std::vector<double> spd[3];
+  if (xcd) {
+    require(n_wg % skv::kXcds == 0, "per-XCD speeds need n_workgroups divisible by 8");
+    for (int k = 0; k < 3; ++k)
+      for (int32_t x = 0; x < skv::kXcds; ++x) {
+        const float v = xcd_speed[k * skv::kXcds + x];
+        require(std::isfinite(v) && v > 0.f, "XCD speeds must be finite and > 0");
+      }
+    for (int k = 0; k < 3; ++k)
+      for (int32_t b = 0; b < n_wg; ++b) spd[k].push_back(xcd_speed[k * skv::kXcds + b % skv::kXcds]);
+    // the forward and dQ kernels run the same items from the same queues
+    // (a query tile's partial slots are the same in both), so those queues
+    // are planned at the speed that gives a unit of work the mean of its
+    // two kernels' times
+    for (int32_t b = 0; b < n_wg; ++b) spd[0][b] = 2.0 / (1.0 / spd[0][b] + 1.0 / spd[1][b]);
+  }
   const std::vector<Tile> tiles = build_tiles(p);
   const int32_t nt = int32_t(tiles.size());
   const int32_t* A = p->anchors;
@@ -490,30 +699,104 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
   const int32_t per_cls = n_wg / n_cls_fwd;
   std::vector<std::vector<int32_t>> q(n_wg);
   std::vector<int64_t> wg_load(n_wg, 0);
-  for (int32_t cls = 0; cls < n_cls_fwd; ++cls) {
-    std::vector<int32_t> ids;  // units of this XCD class
-    SplitJob job;
-    job.item_cost = kItemCost;
-    job.step_cost = kStepCost;
-    job.m = per_cls;
-    for (int32_t ui = 0; ui < int32_t(units.size()); ++ui)
-      if (units[ui].head % n_cls_fwd == cls) {
-        ids.push_back(ui);
-        job.extra.push_back(units[ui].draft_cost);
-        job.steps.push_back(units[ui].k1 - units[ui].k0);
-      }
+  // Items of one plan: per-class SplitJob (the uniform plan), or with
+  // per-XCD speeds the classes first get work shares by their total speed
+  // (a class above its share passes units, and one unit's tail, to the
+  // classes below theirs) and each class's units are placed on its
+  // workgroups at their speeds.  With speeds both are built and the one
+  // whose slowest workgroup finishes first (at those speeds) is kept.
+  auto class_speed = [&](const std::vector<double>& speed) {
+    std::vector<double> cs(n_cls_fwd, 0.0);
+    for (int32_t b = 0; b < n_wg; ++b) cs[b % n_cls_fwd] += speed[b];
+    return cs;
+  };
+  struct FwdPlan {
+    std::vector<Item> items;
+    std::vector<std::vector<int32_t>> q;
     std::vector<int64_t> load;
-    for (const Piece& pc : job.pass(job.auto_target(), &load)) {
-      const Unit& u = units[ids[pc.unit]];
-      const auto& vis = qt_vis[u.qt];
-      Item it{u.head, u.qt, pc.k1 > pc.k0 ? vis[u.k0 + pc.k0] : 0,
-              pc.k1 > pc.k0 ? vis[u.k0 + pc.k1 - 1] + 1 : 0, -1, 0, pc.cost};
-      if (pc.k0 == 0 && p->with_draft && u.draft_cost > 0) it.flags |= skv::kItemDraft;
-      q[cls + pc.bin * n_cls_fwd].push_back(int32_t(items.size()));
-      items.push_back(it);
+  };
+  // pieces of `units` placed per class: where[u] is unit u's class, and
+  // the class's workgroups run at `speed` (nullptr: uniform SplitJob)
+  auto plan_fwd = [&](const std::vector<Unit>& us, const std::vector<int32_t>& where,
+                      const std::vector<double>* speed) {
+    FwdPlan pl;
+    pl.q.assign(n_wg, {});
+    pl.load.assign(n_wg, 0);
+    for (int32_t cls = 0; cls < n_cls_fwd; ++cls) {
+      std::vector<int32_t> ids;
+      std::vector<int64_t> extra;
+      std::vector<int32_t> steps;
+      for (int32_t ui = 0; ui < int32_t(us.size()); ++ui)
+        if (where[ui] == cls) {
+          ids.push_back(ui);
+          extra.push_back(us[ui].draft_cost);
+          steps.push_back(us[ui].k1 - us[ui].k0);
+        }
+      std::vector<int64_t> load;
+      std::vector<Piece> pieces;
+      if (speed) {
+        SpeedJob job;
+        job.item_cost = kItemCost;
+        job.step_cost = kStepCost;
+        job.extra = extra;
+        job.steps = steps;
+        for (int32_t b = cls; b < n_wg; b += n_cls_fwd) job.speed.push_back((*speed)[b]);
+        pieces = job.pass(job.best_target(), &load);
+      } else {
+        SplitJob job;
+        job.item_cost = kItemCost;
+        job.step_cost = kStepCost;
+        job.m = per_cls;
+        job.extra = extra;
+        job.steps = steps;
+        pieces = job.pass(job.auto_target(), &load);
+      }
+      for (const Piece& pc : pieces) {
+        const Unit& u = us[ids[pc.unit]];
+        const auto& vis = qt_vis[u.qt];
+        Item it{u.head, u.qt, pc.k1 > pc.k0 ? vis[u.k0 + pc.k0] : 0,
+                pc.k1 > pc.k0 ? vis[u.k0 + pc.k1 - 1] + 1 : 0, -1, 0, pc.cost};
+        if (pc.k0 == 0 && p->with_draft && u.draft_cost > 0) it.flags |= skv::kItemDraft;
+        pl.q[cls + pc.bin * n_cls_fwd].push_back(int32_t(pl.items.size()));
+        pl.items.push_back(it);
+      }
+      for (int32_t j = 0; j < int32_t(load.size()); ++j) pl.load[cls + j * n_cls_fwd] = load[j];
     }
-    for (int32_t b = 0; b < per_cls; ++b) wg_load[cls + b * n_cls_fwd] = load[b];
+    return pl;
+  };
+  auto slowest = [&](const std::vector<int64_t>& load, const std::vector<double>& speed) {
+    double t = 0;
+    for (int32_t b = 0; b < n_wg; ++b) t = std::max(t, double(load[b]) / speed[b]);
+    return t;
+  };
+  std::vector<int32_t> home_of(units.size());
+  for (size_t ui = 0; ui < units.size(); ++ui) home_of[ui] = units[ui].head % n_cls_fwd;
+  FwdPlan chosen = plan_fwd(units, home_of, nullptr);
+  if (xcd) {
+    std::vector<int64_t> ucost;
+    std::vector<int32_t> usteps;
+    for (const Unit& u : units) {
+      ucost.push_back(kItemCost + u.draft_cost + kStepCost * (u.k1 - u.k0));
+      usteps.push_back(u.k1 - u.k0);
+    }
+    std::vector<std::pair<int32_t, int32_t>> tails;
+    const std::vector<int32_t> where =
+        share_classes(ucost, home_of, class_speed(spd[0]), &usteps, kStepCost, kItemCost,
+                      double(kItemCost), &tails);
+    std::vector<Unit> us = units;
+    for (const auto& [u, k] : tails) {  // unit u keeps its first k steps
+      Unit tail = us[u];
+      tail.k0 = us[u].k0 + k;
+      tail.draft_cost = 0;
+      us[u].k1 = us[u].k0 + k;
+      us.push_back(tail);
+    }
+    FwdPlan sp = plan_fwd(us, where, &spd[0]);
+    if (slowest(sp.load, spd[0]) < slowest(chosen.load, spd[0])) chosen = std::move(sp);
   }
+  items = std::move(chosen.items);
+  q = std::move(chosen.q);
+  wg_load = std::move(chosen.load);
   // query tiles with several items write partial slots, merged afterwards
   std::vector<int32_t> split_rec;  // S_WORDS per split query tile
   int32_t n_slots = 0;
@@ -591,9 +874,48 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
   const int32_t n_cls = n_cls_fwd;
   int64_t max_bin = 0, kv_max_bin = 0;
   for (int64_t l : wg_load) max_bin = std::max(max_bin, l);
-  auto kq = place(int32_t(kv.size()), n_wg, n_cls,
-                  [&](int32_t i) { return kv[i].cost; },
-                  [&](int32_t i) { return kv[i].head; }, &kv_max_bin);
+  std::vector<std::vector<int32_t>> kq;
+  if (xcd) {
+    max_bin = max_time_load(wg_load, spd[0]);
+    std::vector<int64_t> cost, load(n_wg, 0);
+    std::vector<int32_t> home;
+    for (const KvItem& k : kv) {
+      cost.push_back(k.cost);
+      home.push_back(k.head % n_cls);
+    }
+    const std::vector<int32_t> where = share_classes(
+        cost, home, class_speed(spd[2]), nullptr, 0, 0, double(kKvItemCost), nullptr);
+    // LPT per class at the workgroups' speeds: largest first (stable), each
+    // to the class's workgroup of least time (ties: lower workgroup)
+    std::vector<std::vector<int32_t>> kq_sp(n_wg);
+    std::vector<int32_t> order(kv.size());
+    for (size_t i = 0; i < kv.size(); ++i) order[i] = int32_t(i);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
+    std::vector<double> time(n_wg, 0.0);
+    for (int32_t i : order) {
+      int32_t best = -1;
+      for (int32_t b = where[i]; b < n_wg; b += n_cls)
+        if (best < 0 || time[b] < time[best]) best = b;
+      kq_sp[best].push_back(i);
+      load[best] += cost[i];
+      time[best] = double(load[best]) / spd[2][best];
+    }
+    // keep the plain per-class plan if it finishes first at these speeds
+    std::vector<int64_t> load_u;
+    int64_t unused = 0;
+    kq = place(int32_t(kv.size()), n_wg, n_cls, [&](int32_t i) { return kv[i].cost; },
+               [&](int32_t i) { return kv[i].head; }, &unused);
+    load_u.assign(n_wg, 0);
+    for (int32_t b = 0; b < n_wg; ++b)
+      for (int32_t i : kq[b]) load_u[b] += kv[i].cost;
+    if (slowest(load, spd[2]) < slowest(load_u, spd[2])) kq = std::move(kq_sp);
+    else load = load_u;
+    kv_max_bin = max_time_load(load, spd[2]);
+  } else {
+    kq = place(int32_t(kv.size()), n_wg, n_cls, [&](int32_t i) { return kv[i].cost; },
+               [&](int32_t i) { return kv[i].head; }, &kv_max_bin);
+  }
   int64_t kv_total = 0;
   for (const auto& k : kv) kv_total += k.cost;
   int64_t item_total = 0;
@@ -647,11 +969,15 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
   require(words < (int64_t(1) << 31), "schedule image too large");
 
   const int64_t rows_slot = skv::kQTile;
+  // XCD mode: the per-XCD queue counters sit in the last kXcdCounterBytes
+  // (forward: 8 words; backward: 8 for dQ, then 8 for dK/dV)
   const int64_t fwd_ws = align_up(int64_t(n_slots) * rows_slot * g.d * 4, 256) +
-                         align_up(int64_t(n_slots) * rows_slot * 4, 256);
+                         align_up(int64_t(n_slots) * rows_slot * 4, 256) +
+                         (xcd ? kXcdCounterBytes : 0);
   // per-row statistics: per kv head, its rows plus kStatPad padding rows
   const int64_t bwd_ws = 4 * align_up(int64_t(g.hkv) * (g.rows_per_head + skv::kStatPad) * 4, 256) +
-                         align_up(int64_t(n_slots) * rows_slot * g.d * 4, 256);
+                         align_up(int64_t(n_slots) * rows_slot * g.d * 4, 256) +
+                         (xcd ? kXcdCounterBytes : 0);
   std::memset(info, 0, sizeof(*info));
   info->words = words;
   info->n_workgroups = n_wg;
@@ -667,6 +993,7 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
   info->item_cost_max_bin = max_bin;
   info->kv_cost_total = kv_total;
   info->kv_cost_max_bin = kv_max_bin;
+  info->xcd_mode = xcd ? 1 : 0;
   info->nb = g.nb;
   info->hq = g.hq;
   info->hkv = g.hkv;
@@ -706,6 +1033,7 @@ void build_schedule(const skv_problem* p, int32_t n_wg, int32_t* image,
   H[H_OFF_KVQOFF] = int32_t(off_kvqoff);
   H[H_OFF_KVQUEUE] = int32_t(off_kvqueue);
   H[H_NCLASS] = n_cls;
+  H[H_XCD] = xcd ? 1 : 0;
   std::memcpy(image + off_anchors, A, size_t(g.nb) * 4);
   std::memcpy(image + off_lo, L, size_t(g.nb) * 4);
   for (int32_t t = 0; t < nt; ++t) {
@@ -871,7 +1199,16 @@ skv_status skv_plan_lpt_split(const int64_t* extra, const int32_t* steps, int32_
 skv_status skv_schedule_build(const skv_problem* p, int32_t n_workgroups,
                               int32_t* image, int64_t capacity_words,
                               skv_schedule_info* info) {
-  return guarded([&] { build_schedule(p, n_workgroups, image, capacity_words, info); });
+  return guarded([&] { build_schedule(p, n_workgroups, nullptr, image, capacity_words, info); });
+}
+
+skv_status skv_schedule_build_xcd(const skv_problem* p, int32_t n_workgroups,
+                                  const float* xcd_speed, int32_t* image,
+                                  int64_t capacity_words, skv_schedule_info* info) {
+  return guarded([&] {
+    require(xcd_speed != nullptr, "xcd_speed must not be NULL");
+    build_schedule(p, n_workgroups, xcd_speed, image, capacity_words, info);
+  });
 }
 
 skv_status skv_attn_fwd_partial(const skv_problem* p, const skv_schedule_info* info,
@@ -910,6 +1247,14 @@ skv_status skv_attn_fwd_partial(const skv_problem* p, const skv_schedule_info* i
                    static_cast<char*>(workspace) +
                    align_up(int64_t(info->n_partial_slots) * skv::kQTile * p->d * 4, 256))
                          : nullptr;
+    if (info->xcd_mode) {
+      require(info->n_workgroups % skv::kXcds == 0 &&
+                  info->fwd_workspace_bytes >= skv::kXcdCounterBytes,
+              "inconsistent schedule info (per-XCD queues)");
+      a.xcd_count = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                                info->fwd_workspace_bytes -
+                                                skv::kXcdCounterBytes);
+    }
     bool fits = true;
     a.wg_clock = a.dtype_bf16 ? skv::wg_clock_region(skv::kClockFwd, a.n_wg, &fits) : nullptr;
     require(fits, "per-workgroup clock buffer too small for this schedule's workgroups");
@@ -1031,6 +1376,14 @@ skv_status skv_attn_bwd(const skv_problem* p, const skv_schedule_info* info,
     a.ws_HI = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 3 * stat_bytes);
     a.ws_dQ = reinterpret_cast<float*>(static_cast<char*>(workspace) + 4 * stat_bytes);
     a.stat_words = stat_bytes / 4;
+    if (info->xcd_mode) {
+      require(info->n_workgroups % skv::kXcds == 0 &&
+                  info->bwd_workspace_bytes >= 4 * stat_bytes + skv::kXcdCounterBytes,
+              "inconsistent schedule info (per-XCD queues)");
+      a.xcd_count = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                                info->bwd_workspace_bytes -
+                                                skv::kXcdCounterBytes);
+    }
     bool fits = true;
     a.wg_clock_dq = skv::wg_clock_region(skv::kClockDq, a.n_wg, &fits);
     a.wg_clock_kv = skv::wg_clock_region(skv::kClockKv, a.n_wg, &fits);

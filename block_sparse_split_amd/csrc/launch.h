@@ -24,6 +24,11 @@ struct LdsLimit {
   }
 };
 
+// Bytes at the end of a workspace that hold the per-XCD queue counters of a
+// schedule built for per-XCD speeds (forward: 8 words; backward: 8 for dQ,
+// then 8 for dK/dV).
+constexpr int64_t kXcdCounterBytes = 256;
+
 struct FwdArgs {
   const int32_t* sched;     // device schedule image
   const void* Q;            // [Nq, hq, d]
@@ -36,6 +41,7 @@ struct FwdArgs {
   float* ws_O;              // partial slots [n_slots, 256, d] fp32
   float* ws_LSE;            // [n_slots, 256]
   unsigned long long* wg_clock;  // per-workgroup (start, end) stamps, or null
+  uint32_t* xcd_count;      // per-XCD queue counters (schedule with per-XCD speeds), or null
   int32_t o_bf16, dtype_bf16;
   int32_t hq, hkv, d, nb, n_local;
   int32_t n_wg, n_split, n_slots;
@@ -66,6 +72,7 @@ struct BwdArgs {
   int64_t stat_words;       // distance between the -D, L2, LO and HI arrays
   unsigned long long* wg_clock_dq;  // per-workgroup (start, end) stamps, or null
   unsigned long long* wg_clock_kv;
+  uint32_t* xcd_count;      // dQ then dK/dV per-XCD queue counters, or null (zeroed by pre)
   int32_t grad_bf16, dtype_bf16;
   int32_t hq, hkv, d, nb, n_local;
   int32_t n_wg, n_split, n_slots, with_draft;

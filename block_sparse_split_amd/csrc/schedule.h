@@ -7,18 +7,24 @@
 // LPT queues, the list of query tiles whose key range is cut into several
 // items (their partials are merged after the main kernel), and the dK/dV
 // work items with their queues.
+//
+// Queues are indexed by a queue number v in [0, n_wg).  Normally workgroup
+// v runs queue v.  When H_XCD is set, queue v was planned for XCD v % 8 at
+// that XCD's measured speed, and each workgroup takes the next unclaimed
+// queue of the XCD it runs on (per-XCD counters zeroed before the launch).
 #pragma once
 #include <stdint.h>
 
 namespace skv {
 
 constexpr int32_t kMagic = 0x314B5653;  // "SVK1"
-constexpr int32_t kVersion = 1;
+constexpr int32_t kVersion = 2;
 constexpr int kBlock = 16;      // draft tokens per anchor block
 constexpr int kTileK = 64;      // keys per key tile
 constexpr int kQTile = 256;     // query rows (token x head of one kv head) per tile
 constexpr int kKvGroup = 128;   // keys per dK/dV item (two 64-key tiles)
 constexpr int kStatPad = 64;    // padding rows after each kv head's row statistics
+constexpr int kXcds = 8;        // XCDs of the device; queues of XCD x are v = x, x + 8, ...
 
 // Header word indices.
 enum Hdr : int {
@@ -26,6 +32,7 @@ enum Hdr : int {
   H_NTILES, H_QT_PER_HEAD, H_NITEMS, H_NWG, H_NSPLIT, H_NSLOTS, H_NKV,
   H_OFF_ANCHORS, H_OFF_LO, H_OFF_TILES, H_OFF_ITEMS, H_OFF_QOFF, H_OFF_QUEUE,
   H_OFF_SPLIT, H_OFF_KV, H_OFF_KVQOFF, H_OFF_KVQUEUE, H_NCLASS,
+  H_XCD,
   H_WORDS = 32
 };
 

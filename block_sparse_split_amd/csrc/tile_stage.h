@@ -69,18 +69,52 @@ __device__ __forceinline__ void wait_vmcnt() {
 // is null unless a caller asked for the stamps (then each workgroup writes
 // its four words).
 __device__ __forceinline__ uint64_t wg_clock_now() { return __builtin_amdgcn_s_memrealtime(); }
-__device__ __forceinline__ void wg_clock_record(unsigned long long* clk, uint64_t t0) {
+__device__ __forceinline__ uint32_t hw_xcc_id() {
+  return __builtin_amdgcn_s_getreg((31 << 11) | 20);  // HW_REG_XCC_ID, 32 bits
+}
+// Entry v of the stamps belongs to queue v (the workgroup that ran it).
+__device__ __forceinline__ void wg_clock_record(unsigned long long* clk, uint64_t t0, int v) {
   if (clk == nullptr) return;
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
-    const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // HW_REG_XCC_ID, 32 bits
+    const uint32_t xcc = hw_xcc_id();
     const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_REG_HW_ID, 32 bits
-    clk[4 * blockIdx.x] = t0;
-    clk[4 * blockIdx.x + 1] = t1;
-    clk[4 * blockIdx.x + 2] = xcc;
-    clk[4 * blockIdx.x + 3] = hw;
+    clk[4 * v] = t0;
+    clk[4 * v + 1] = t1;
+    clk[4 * v + 2] = xcc;
+    clk[4 * v + 3] = hw;
   }
+}
+
+// The queue this workgroup runs (see schedule.h): its own index, unless
+// the schedule has per-XCD queues and `count` (this kernel's kXcds per-XCD
+// counters, zero at launch) is given.  Then thread 0 reads the XCD it runs
+// on, x, and takes the next free queue of x, v = x + kXcds * slot, or of
+// the next XCD when all of x's are taken (a failed try only raises that
+// counter).  With n_wg workgroups claiming, counters starting at zero and
+// n_wg / kXcds queues per XCD, every workgroup finds a queue within kXcds
+// tries (if all its tries failed, every XCD's queues would be held by
+// other workgroups, n_wg of them) and no queue is taken twice.
+__device__ __forceinline__ int claim_queue(sched_t S, uint32_t* count) {
+  if (count == nullptr || S[H_XCD] == 0) return blockIdx.x;
+  __shared__ int v_claimed;
+  if (threadIdx.x == 0) {
+    const int per = S[H_NWG] / kXcds;
+    const int x = int(hw_xcc_id() & 0xF) % kXcds;
+    int v = blockIdx.x;  // kept only if the counters did not start at zero
+    for (int i = 0; i < kXcds; ++i) {
+      const int y = (x + i) % kXcds;
+      const uint32_t slot = atomicAdd(&count[y], 1u);
+      if (slot < uint32_t(per)) {
+        v = y + kXcds * int(slot);
+        break;
+      }
+    }
+    v_claimed = v;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(v_claimed);
 }
 
 __device__ __forceinline__ void block_barrier() {

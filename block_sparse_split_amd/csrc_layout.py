@@ -47,3 +47,5 @@ S_WORDS = _ENUMS["S_WORDS"]
 K_WORDS = _ENUMS["K_WORDS"]
 # word index of each item field (I_HEAD -> "HEAD", ...)
 I = {k[2:]: v for k, v in _ENUMS.items() if k.startswith("I_") and k != "I_WORDS"}
+# word index of each dK/dV item field (K_HEAD -> "HEAD", ...)
+K = {k[2:]: v for k, v in _ENUMS.items() if k.startswith("K_") and k != "K_WORDS"}

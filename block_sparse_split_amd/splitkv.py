@@ -20,6 +20,7 @@ LIB_PATH = os.environ.get("SKV_LIBRARY") or os.path.join(_HERE, "libsplitkv.so")
 
 SKV_F32 = 0
 SKV_BF16 = 1
+XCDS = 8          # XCDs of the device (per-XCD speeds are given per XCD)
 SKV_OK = 0
 STATUS_NAMES = {0: "SKV_OK", -1: "SKV_ERR_INVALID_ARG", -2: "SKV_ERR_UNSUPPORTED",
                 -3: "SKV_ERR_HIP", -4: "SKV_ERR_WORKSPACE"}
@@ -47,7 +48,7 @@ class SkvScheduleInfo(ctypes.Structure):
                 ("n_tiles", ctypes.c_int32), ("n_qtiles", ctypes.c_int32),
                 ("n_items", ctypes.c_int32), ("n_split_qtiles", ctypes.c_int32),
                 ("n_partial_slots", ctypes.c_int32), ("n_kv_items", ctypes.c_int32),
-                ("reserved", ctypes.c_int32),
+                ("xcd_mode", ctypes.c_int32),
                 ("fwd_workspace_bytes", ctypes.c_int64), ("bwd_workspace_bytes", ctypes.c_int64),
                 ("item_cost_total", ctypes.c_int64), ("item_cost_max_bin", ctypes.c_int64),
                 ("kv_cost_total", ctypes.c_int64), ("kv_cost_max_bin", ctypes.c_int64),
@@ -80,6 +81,9 @@ def lib():
                                      ctypes.c_int32, _i32p, _i64p, _i32p, _i64p, _i64p]
     L.skv_schedule_build.argtypes = [ctypes.POINTER(SkvProblem), ctypes.c_int32, _i32p,
                                      ctypes.c_int64, ctypes.POINTER(SkvScheduleInfo)]
+    L.skv_schedule_build_xcd.argtypes = [ctypes.POINTER(SkvProblem), ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_float), _i32p, ctypes.c_int64,
+                                         ctypes.POINTER(SkvScheduleInfo)]
     L.skv_attn_fwd_partial.argtypes = [ctypes.POINTER(SkvProblem),
                                        ctypes.POINTER(SkvScheduleInfo), _vp, _vp, _vp, _vp,
                                        _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int64,
@@ -104,7 +108,8 @@ def lib():
                                     ctypes.POINTER(ctypes.c_double)]
     L.skv_timing_wg_clock.argtypes = [_vp, ctypes.c_int64]
     for name in ("skv_chunk_costs", "skv_plan_lpt_costs", "skv_plan_lpt", "skv_plan_lpt_split",
-                 "skv_schedule_build", "skv_attn_fwd_partial", "skv_attn_fwd_partial_noalloc",
+                 "skv_schedule_build", "skv_schedule_build_xcd", "skv_attn_fwd_partial",
+                 "skv_attn_fwd_partial_noalloc",
                  "skv_merge_lse", "skv_dq_finalize", "skv_attn_bwd", "skv_timing_enable",
                  "skv_timing_collect",
                  "skv_timing_result", "skv_timing_wg_clock"):
@@ -221,6 +226,24 @@ def skv_schedule_build(problem: Problem, n_workgroups: int = 0):
     _check("skv_schedule_build", L.skv_schedule_build(
         ctypes.byref(problem.c), info.n_workgroups, image.ctypes.data_as(_i32p), len(image),
         ctypes.byref(info)))
+    return image, info
+
+
+def skv_schedule_build_xcd(problem: Problem, n_workgroups: int, xcd_speed):
+    """Schedule planned for per-XCD speeds: xcd_speed is [3, 8] (forward,
+    dQ, dK/dV kernels x XCD), relative work per unit time."""
+    sp = np.ascontiguousarray(np.asarray(xcd_speed, np.float32).reshape(-1))
+    if sp.size != 3 * XCDS:
+        raise ValueError(f"xcd_speed must hold 3 x {XCDS} values, got {sp.size}")
+    fp = sp.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    info = SkvScheduleInfo()
+    L = lib()
+    _check("skv_schedule_build_xcd", L.skv_schedule_build_xcd(
+        ctypes.byref(problem.c), n_workgroups, fp, None, 0, ctypes.byref(info)))
+    image = np.zeros(info.words, np.int32)
+    _check("skv_schedule_build_xcd", L.skv_schedule_build_xcd(
+        ctypes.byref(problem.c), info.n_workgroups, fp, image.ctypes.data_as(_i32p),
+        len(image), ctypes.byref(info)))
     return image, info
 
 
@@ -375,10 +398,14 @@ class Shard:
     Convenience wrapper for repeated calls (one schedule per batch serves
     every layer).  Allocation happens here, never inside the calls."""
 
-    def __init__(self, problem: Problem, device="cuda", n_workgroups: int = 0):
+    def __init__(self, problem: Problem, device="cuda", n_workgroups: int = 0,
+                 xcd_speed=None):
         torch = _torch()
         self.problem = problem
-        self.image, self.info = skv_schedule_build(problem, n_workgroups)
+        if xcd_speed is None:
+            self.image, self.info = skv_schedule_build(problem, n_workgroups)
+        else:
+            self.image, self.info = skv_schedule_build_xcd(problem, n_workgroups, xcd_speed)
         self.schedule = torch.from_numpy(self.image).to(device)
         nbytes = max(self.info.fwd_workspace_bytes, self.info.bwd_workspace_bytes, 256)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -395,6 +422,75 @@ class Shard:
             stream=None):
         skv_attn_bwd(self.problem, self.info, self.schedule, Q, K, V, Kd, Vd, O, dO, LSE, dQ,
                      dK, dV, dKd, dVd, grad_dtype, self.workspace, stream)
+
+
+def queue_loads(image):
+    """Planned load (item costs) of every queue of a schedule image, per
+    kernel: array [3, n_wg] for the forward, dQ (the forward's queues) and
+    dK/dV queues."""
+    from .csrc_layout import H, I, K, K_WORDS, I_WORDS
+    img = np.asarray(image)
+    h = {k: int(img[v]) for k, v in H.items()}
+    n = h["NWG"]
+    items = img[h["OFF_ITEMS"]: h["OFF_ITEMS"] + h["NITEMS"] * I_WORDS].reshape(-1, I_WORDS)
+    kv = img[h["OFF_KV"]: h["OFF_KV"] + h["NKV"] * K_WORDS].reshape(-1, K_WORDS)
+    cost_items = items[:, I["COST"]].astype(np.int64)
+    cost_kv = kv[:, K["COST"]].astype(np.int64)
+    out = np.zeros((3, n), np.int64)
+    for k, (qo, qq, cost) in enumerate(((h["OFF_QOFF"], h["OFF_QUEUE"], cost_items),
+                                        (h["OFF_QOFF"], h["OFF_QUEUE"], cost_items),
+                                        (h["OFF_KVQOFF"], h["OFF_KVQUEUE"], cost_kv))):
+        off = img[qo: qo + n + 1]
+        q = img[qq: qq + off[-1]]
+        for v in range(n):
+            out[k, v] = cost[q[off[v]: off[v + 1]]].sum()
+    return out
+
+
+def xcd_speeds_from_stamps(image, runs):
+    """Relative speed of each XCD in each kernel, from per-workgroup clock
+    stamps (skv_timing_wg_clock) of launches with this schedule: runs is a
+    list of [3, n_wg, 4] arrays (start, end, XCC_ID, HW_ID per queue).
+    speed[k, x] = planned load run on XCD x / time spent on XCD x, scaled
+    to mean 1 over the XCDs; a kernel without stamps gets 1."""
+    loads = queue_loads(image)
+    n = loads.shape[1]
+    work = np.zeros((3, XCDS))
+    time = np.zeros((3, XCDS))
+    for r in runs:
+        r = np.asarray(r).reshape(3, n, 4)
+        for k in range(3):
+            dur = (r[k, :, 1] - r[k, :, 0]).astype(np.float64)
+            ok = (r[k, :, 1] > 0) & (dur > 0)
+            x = (r[k, :, 2] & 0xF).astype(np.int64) % XCDS
+            np.add.at(work[k], x[ok], loads[k][ok])
+            np.add.at(time[k], x[ok], dur[ok])
+    speed = np.ones((3, XCDS))
+    for k in range(3):
+        if np.all(time[k] > 0) and np.all(work[k] > 0):
+            v = work[k] / time[k]
+            speed[k] = v / v.mean()
+    return speed
+
+
+def measure_xcd_speed(shard, step, steps: int = 4):
+    """Run `step` (a callable doing one forward + backward with `shard`)
+    `steps` times with per-workgroup stamps and return the per-XCD speeds
+    ([3, 8]) of its schedule's queues."""
+    torch = _torch()
+    n = shard.info.n_workgroups
+    clk = torch.zeros(3 * n * 4, dtype=torch.int64, device=shard.schedule.device)
+    runs = []
+    skv_timing_wg_clock(clk)
+    try:
+        for _ in range(steps):
+            clk.zero_()
+            step()
+            torch.cuda.synchronize()
+            runs.append(clk.view(3, n, 4).cpu().numpy().copy())
+    finally:
+        skv_timing_wg_clock(None)
+    return xcd_speeds_from_stamps(shard.image, runs)
 
 
 # ---------------------------------------------------------------- timing

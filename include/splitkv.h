@@ -74,9 +74,11 @@ const char* skv_last_error(void);
 
 /* ABI version of this header (bumped on incompatible changes; 2: four
  * words per workgroup in the clock-stamp buffer, skv_plan_lpt_split and
- * skv_dq_finalize added). */
+ * skv_dq_finalize added; 3: schedule image version 2 (a dQ queue of its
+ * own, per-XCD queues), skv_schedule_info.xcd_mode, clock stamps indexed by
+ * queue, skv_schedule_build_xcd added). */
 int32_t skv_abi_version(void);
-#define SKV_ABI_VERSION 2
+#define SKV_ABI_VERSION 3
 
 /* ------------------------------------------------------------------------
  * Planner (host only, synchronous, deterministic).
@@ -180,7 +182,7 @@ typedef struct skv_schedule_info {
   int32_t n_split_qtiles;      /* query tiles cut into several items        */
   int32_t n_partial_slots;     /* partial (O, LSE) slots for those tiles    */
   int32_t n_kv_items;          /* backward dK/dV work items                 */
-  int32_t reserved;
+  int32_t xcd_mode;            /* 1: queues planned per XCD (skv_schedule_build_xcd) */
   int64_t fwd_workspace_bytes; /* workspace for skv_attn_fwd_partial        */
   int64_t bwd_workspace_bytes; /* workspace for skv_attn_bwd                */
   int64_t item_cost_total;     /* sum of forward item costs                 */
@@ -217,6 +219,32 @@ typedef struct skv_schedule_info {
 skv_status skv_schedule_build(const skv_problem* p, int32_t n_workgroups,
                               int32_t* image, int64_t capacity_words,
                               skv_schedule_info* info);
+
+/* The same schedule planned for XCDs of unequal speed (arXiv abstract of
+ * the Split-KV paper: chunks are balanced by their realised cost; here the
+ * realised speed of the hardware that runs them enters the cost).
+ * xcd_speed[k * 8 + x] is the relative speed (work per unit time, any
+ * positive scale) of XCD x in kernel k: 0 the forward, 1 dQ, 2 dK/dV, for
+ * instance measured with skv_timing_wg_clock on a schedule without it.
+ * Queue v is planned at the speed of XCD v % 8, by LPT with splitting over
+ * bins of unequal speed: each piece goes to the bin of least time (load /
+ * speed) of its kv head's XCD class, unless a bin of another class is
+ * earlier by more than 1 % of a mean bin.  The forward and dQ kernels share
+ * their queues (and so a query tile's partial slots), planned at the speed
+ * that gives a unit of work the mean of its two kernels' times,
+ * 2 / (1 / s_fwd + 1 / s_dQ); dK/dV items are placed the same way at their
+ * own speeds, without cuts.  At run time each workgroup takes the next
+ * unclaimed queue of the
+ * XCD it runs on (the next XCD's if those are taken), so the plan holds
+ * whatever XCD the dispatcher starts a launch on.  The per-XCD counters
+ * live in the last 256 bytes of each workspace (counted in the workspace
+ * sizes); the device calls zero them before each launch.  info->xcd_mode
+ * is set.  Requires n_workgroups divisible by 8.
+ * Errors: as skv_schedule_build; SKV_ERR_INVALID_ARG for a NULL, zero,
+ * negative or non-finite speed or n_workgroups not divisible by 8. */
+skv_status skv_schedule_build_xcd(const skv_problem* p, int32_t n_workgroups,
+                                  const float* xcd_speed, int32_t* image,
+                                  int64_t capacity_words, skv_schedule_info* info);
 
 /* ------------------------------------------------------------------------
  * Device calls.
@@ -338,8 +366,10 @@ skv_status skv_timing_result(int32_t k, char* name, int32_t name_cap, int64_t* l
  * on the workgroups (the pages' load-balance claim, measured rather than
  * planned).  While `buffer` (device memory, 8-byte aligned, owned by the
  * caller) is set on the calling thread, the bf16 forward, dQ and dK/dV
- * kernels each write, per workgroup w, four uint64 at [4w, 4w + 3] of their
- * region: start and end on the GPU's constant 100 MHz clock, then the
+ * kernels each write, per queue v (the queue a workgroup ran: v is the
+ * workgroup index unless the schedule has per-XCD queues), four uint64 at
+ * [4v, 4v + 3] of their region: start and end on the GPU's constant 100 MHz
+ * clock, then the
  * hardware XCC_ID and HW_ID register values of the wave that wrote them
  * (XCC_ID's low bits give the XCD; HW_ID holds the wave, SIMD, CU and
  * shader-engine ids).  Regions: forward at 0, dQ at 4 n_wg, dK/dV at 8 n_wg (n_wg =

@@ -1,5 +1,6 @@
 """The host half of libsplitkv (argument checks, chunk costs, LPT, the split
-planner and the schedule image it lays out word by word) built with
+planner, the per-XCD planner and the schedule image it lays out word by
+word) built with
 AddressSanitizer and UndefinedBehaviorSanitizer by the host compiler, linked
 with the normally built device objects, and the CPU tests of the C ABI run
 against it in a child process.  An out-of-bounds write into the schedule
@@ -64,7 +65,8 @@ def test_cpu_abi_tests_are_clean_under_asan_and_ubsan(tmp_path):
     env["ASAN_OPTIONS"] = f"detect_leaks=0:halt_on_error=1:log_path={log}"
     env["UBSAN_OPTIONS"] = f"print_stacktrace=1:halt_on_error=1:log_path={log}"
     tests = [os.path.join(ROOT, "tests", f) for f in
-             ("test_abi_cpu.py", "test_plan_split_cpu.py", "test_bench_host.py")]
+             ("test_abi_cpu.py", "test_plan_split_cpu.py", "test_xcd_plan_cpu.py",
+              "test_bench_host.py")]
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "-m", "not gpu", *tests], capture_output=True, text=True, env=env,
                        cwd=ROOT, timeout=600)

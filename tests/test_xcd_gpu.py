@@ -1,0 +1,92 @@
+"""GPU checks of schedules planned for per-XCD speeds
+(skv_schedule_build_xcd): workgroups claim queues by the XCD they run on,
+every queue runs exactly once, and the forward, backward and
+allocation-free forward match the oracle as with the uniform plan."""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_split_amd import splitkv as skv
+from block_sparse_split_amd import shards
+from block_sparse_split_amd import workloads as wl
+from gpu_util import announce, compare, gpu_fwd, oracle_partial, to_dev
+from test_bwd_gpu import check_grad, oracle_fwd_bwd
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(seed, **over):
+    base = dict(ctx=4096, anchor_lo=1024, anchor_hi=4096, blocks_per_seq=16)
+    base.update(over)
+    return wl.make(wl.scaled(wl.WORKLOADS["ctx32k_q2k"], **base), seed, with_grad=True)
+
+
+def _speeds(seed):
+    rng = np.random.default_rng(seed)
+    return (1.0 + 0.08 * rng.uniform(-1, 1, (3, 8))).astype(np.float32)
+
+
+def _run(w, t, sh, noalloc=False):
+    dt = w.dtype
+    Q, K, V = to_dev(t.Q, dt), to_dev(t.K, dt), to_dev(t.V, dt)
+    Kd, Vd, dO = to_dev(t.Kd, dt), to_dev(t.Vd, dt), to_dev(t.dO, dt)
+    O = torch.full((w.nq, w.hq, w.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    LSE = torch.full((w.nq, w.hq), float("nan"), device="cuda")
+    dQ = torch.full((w.nq, w.hq, w.d), float("nan"), device="cuda")
+    dK, dV = torch.full_like(K, float("nan")), torch.full_like(V, float("nan"))
+    dKd, dVd = torch.full_like(Kd, float("nan")), torch.full_like(Vd, float("nan"))
+    if noalloc:
+        sh.fwd_noalloc(Q, K, V, Kd, Vd, O, LSE)
+    else:
+        sh.fwd(Q, K, V, Kd, Vd, O, LSE)
+    sh.bwd(Q, K, V, Kd, Vd, O, dO, LSE, dQ, dK, dV, dKd, dVd, skv.SKV_BF16)
+    torch.cuda.synchronize()
+    return O, LSE, dQ, dK, dV, dKd, dVd
+
+
+@pytest.mark.parametrize("seed,n_wg", [(1, 256), (2, 64), (3, 8)])
+def test_xcd_plan_forward_backward_parity(seed, n_wg):
+    """Forward (and its allocation-free form) and backward through an XCD
+    plan against the oracle; every queue of the three kernels is stamped
+    exactly once (each workgroup stamps the queue it claimed), so none was
+    skipped."""
+    w, g, t = _small(seed)
+    prob = shards.whole_context_problem(w, g)
+    sh = skv.Shard(prob, n_workgroups=n_wg, xcd_speed=_speeds(seed))
+    assert sh.info.xcd_mode == 1
+    announce("xcd plan parity", seed, n_wg)
+    clk = torch.zeros(3 * n_wg * 4, dtype=torch.int64, device="cuda")
+    skv.skv_timing_wg_clock(clk)
+    try:
+        got = _run(w, t, sh)
+    finally:
+        skv.skv_timing_wg_clock(None)
+    st = clk.view(3, n_wg, 4).cpu().numpy()
+    assert np.all(st[:, :, 0] > 0) and np.all(st[:, :, 1] >= st[:, :, 0])
+    print("[xcd] queues run on their own XCD:",
+          float(np.mean((st[:, :, 2] & 15) == np.arange(n_wg) % 8)), flush=True)
+    Oo, Lo, want = oracle_fwd_bwd(w, g, t, np.arange(len(g.chunk_pos)), True)
+    compare(got[0], got[1], Oo, Lo, "bf16", "xcd plan forward")
+    for name, a, b in zip(("dQ", "dK", "dV", "dKd", "dVd"), got[2:], want):
+        check_grad(a, b, f"xcd plan {name}")
+    # twice in a row (the counters are zeroed before every launch), and the
+    # allocation-free forward, give the same bits
+    again = _run(w, t, sh)
+    free = _run(w, t, sh, noalloc=True)
+    for x, y, z in zip(got, again, free):
+        assert torch.equal(x, y) and torch.equal(x, z)
+
+
+def test_xcd_plan_shard_partials():
+    """A context-parallel shard (no draft keys) planned per XCD: its
+    partial output and LSE against the oracle's partial attention."""
+    w = wl.scaled(wl.WORKLOADS["cp64_rank0_ctx512k"], ctx=8192, anchor_lo=2048,
+                  anchor_hi=8192, blocks_per_seq=8, chunk=512, n_shards=4)
+    w, g, t = wl.make(w, 6)
+    ids, _, _, _ = shards.lpt_shards(w, g, w.n_shards)
+    prob = shards.shard_problem(w, g, ids[2], False)
+    sh = skv.Shard(prob, n_workgroups=32, xcd_speed=_speeds(7))
+    announce("xcd plan shard partial")
+    O, L, _ = gpu_fwd(w, g, t, ids[2], False, shard=sh)
+    Oo, Lo = oracle_partial(w, g, t, ids[2], False)
+    compare(O, L, Oo, Lo, "bf16", "xcd shard")

@@ -1,0 +1,223 @@
+"""CPU checks of the schedule planned for XCDs of unequal speed
+(skv_schedule_build_xcd): it covers the same work once, balances time
+rather than load, keeps work in its kv head's XCD class unless moving it
+saves time, and the speed estimate inverts the stamps it is made from.  No
+device call is made."""
+import numpy as np
+import pytest
+
+import oracle
+from block_sparse_split_amd import splitkv as skv
+from block_sparse_split_amd import workloads as wl
+from block_sparse_split_amd import shards
+from block_sparse_split_amd.csrc_layout import H, I, K, T_WORDS, I_WORDS, K_WORDS, QTILE, BLOCK
+
+STEP_COST, ITEM_COST = 8, 44
+
+
+def _case(name, seed, shard_of=None, **over):
+    w = wl.scaled(wl.WORKLOADS[name], **over) if over else wl.WORKLOADS[name]
+    w, g, _ = wl.make(w, seed, tensors=False)
+    if shard_of is None:
+        return w, g, shards.whole_context_problem(w, g)
+    ids, _, _, _ = shards.lpt_shards(w, g, w.n_shards)
+    return w, g, shards.shard_problem(w, g, ids[shard_of], shard_of == 0)
+
+
+def _queues(image, off_key, q_key, n):
+    h = {k: int(image[v]) for k, v in H.items()}
+    off = image[h[off_key]: h[off_key] + h["NWG"] + 1]
+    q = image[h[q_key]: h[q_key] + n]
+    return [q[off[v]:off[v + 1]].tolist() for v in range(h["NWG"])]
+
+
+def _decode(image):
+    h = {k: int(image[v]) for k, v in H.items()}
+    tiles = image[h["OFF_TILES"]: h["OFF_TILES"] + h["NTILES"] * T_WORDS].reshape(-1, T_WORDS)
+    items = image[h["OFF_ITEMS"]: h["OFF_ITEMS"] + h["NITEMS"] * I_WORDS].reshape(-1, I_WORDS)
+    kv = image[h["OFF_KV"]: h["OFF_KV"] + h["NKV"] * K_WORDS].reshape(-1, K_WORDS)
+    return (h, tiles, items, kv, _queues(image, "OFF_QOFF", "OFF_QUEUE", h["NITEMS"]),
+            _queues(image, "OFF_KVQOFF", "OFF_KVQUEUE", h["NKV"]))
+
+
+def _speeds(seed, spread):
+    rng = np.random.default_rng(seed)
+    return (1.0 + spread * rng.uniform(-1, 1, (3, 8))).astype(np.float32)
+
+
+CASES = [
+    ("ctx32k_q2k", 1, None, 256, {}),
+    ("varlen8_fwdbwd", 3, None, 256, dict(len_median=2048, len_min=512, len_max=8192)),
+    ("ctx32k_q2k", 3, None, 64, dict(ctx=4096, anchor_lo=512, anchor_hi=4096, blocks_per_seq=24,
+                                     hq=32, hkv=2)),
+    ("cp64_rank0_ctx512k", 2, 5, 256, {}),
+    ("tiny_f32_ctx1k", 0, 0, 8, {}),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_xcd_plan_covers_the_work_once(case):
+    """Every (kv head, query tile, visible tile) in exactly one item, item
+    costs as in the uniform plan, every item in exactly one forward/dQ
+    queue and every dK/dV item in exactly one dK/dV queue."""
+    name, seed, shard_of, n_wg, over = case
+    w, g, prob = _case(name, seed, shard_of, **over)
+    image, info = skv.skv_schedule_build_xcd(prob, n_wg, _speeds(seed, 0.1))
+    assert info.xcd_mode == 1
+    h, tiles, items, kv, fq, kq = _decode(image)
+    assert h["XCD"] == 1 and h["NWG"] == n_wg
+    G = w.hq // w.hkv
+    qtph = -(-w.nq * G // QTILE)
+    seen = np.zeros((w.hkv, qtph, len(tiles)), np.int32)
+    draft = np.zeros((w.hkv, qtph), np.int32)
+    for it in items:
+        hd, qt, t0, t1 = it[I["HEAD"]], it[I["QT"]], it[I["T0"]], it[I["T1"]]
+        seen[hd, qt, t0:t1] += 1
+        draft[hd, qt] += it[I["FLAGS"]] & 1
+        b0 = qt * (QTILE // G) // BLOCK
+        b1 = min(w.nb, -(-((qt + 1) * (QTILE // G)) // BLOCK))
+        want = ITEM_COST + STEP_COST * (t1 - t0)
+        if it[I["FLAGS"]] & 1:
+            want += STEP_COST * -(-((b1 - b0) * BLOCK) // 64)
+        assert it[I["COST"]] == want
+    for qt in range(qtph):
+        b0 = qt * (QTILE // G) // BLOCK
+        b1 = min(w.nb, -(-((qt + 1) * (QTILE // G)) // BLOCK))
+        vis = np.array([oracle.tile_pairs_visible(g.anchors[b0:b1], g.lo[b0:b1], t[1],
+                                                  t[1] + t[2]) > 0 for t in tiles], bool)
+        for hd in range(w.hkv):
+            assert np.array_equal(seen[hd, qt] > 0, vis)
+            assert seen[hd, qt].max(initial=0) <= 1
+            assert draft[hd, qt] == int(prob.c.with_draft)
+    for qs, n in ((fq, len(items)), (kq, len(kv))):
+        assert sorted(i for q in qs for i in q) == list(range(n))
+    # partial slots: a query tile cut into several items numbers them
+    # consecutively, a single item writes its rows directly
+    per_qt = {}
+    for it in items:
+        per_qt.setdefault((it[0], it[1]), []).append(it[I["SLOT"]])
+    slots = sorted(s for v in per_qt.values() if len(v) > 1 for s in v)
+    assert slots == list(range(info.n_partial_slots))
+    assert all(v == [-1] for v in per_qt.values() if len(v) == 1)
+
+
+def _times(loads, speed8):
+    n = len(loads)
+    return loads / np.array([speed8[v % 8] for v in range(n)], np.float64)
+
+
+@pytest.mark.parametrize("name,seed,over", [("ctx32k_q2k", 1, {}),
+                                            ("varlen8_fwdbwd", 3, {}),
+                                            ("cp64_rank0_ctx512k", 2, {})])
+def test_xcd_plan_balances_time_at_unequal_speeds(name, seed, over):
+    """With XCD speeds 0.95-1.05 the slowest queue never finishes later
+    than in the uniform plan timed at the same speeds; where the items are
+    fine enough (the uniform plan balances equal speeds within 2 %), queue
+    time is balanced within 2.5 % while the uniform plan, at these speeds,
+    is off by several per cent.  The forward and dQ share their queues, planned so
+    that a unit of work gets the mean of its two kernels' times: that mean
+    is what is balanced (and each kernel's own time when their speeds
+    agree); dK/dV queues at their own speed.  info reports the
+    speed-normalised maximum."""
+    w, g, prob = _case(name, seed, 0 if name.startswith("cp64") else None, **over)
+    sp = _speeds(seed + 10, 0.05)
+    base, _ = skv.skv_schedule_build(prob, 256)
+    bloads = skv.queue_loads(base).astype(np.float64)
+    for same in (True, False):
+        if same:
+            sp[1] = sp[0]
+        image, info = skv.skv_schedule_build_xcd(prob, 256, sp)
+        loads = skv.queue_loads(image).astype(np.float64)
+        both = _times(loads[0], sp[0]) + _times(loads[1], sp[1])
+        both_base = _times(bloads[0], sp[0]) + _times(bloads[1], sp[1])
+        # (time at the speeds, uniform plan's time at the speeds, uniform
+        # plan's own load imbalance: the granularity of the items)
+        checks = [(both, both_base, bloads[0]),
+                  (_times(loads[2], sp[2]), _times(bloads[2], sp[2]), bloads[2])]
+        if same:
+            checks.append((_times(loads[0], sp[0]), _times(bloads[0], sp[0]), bloads[0]))
+        for t, tb, lu in checks:
+            # never slower than the uniform plan at these speeds (the
+            # builder keeps whichever finishes first) ...
+            assert t.max() <= tb.max() * (1 + 1e-9), (same, t.max(), tb.max())
+            # ... and where the items are fine enough for the uniform plan
+            # to balance equal speeds within 2 %, within 2.5 % here and
+            # clearly better than the uniform plan
+            grain = lu.max() / lu.mean() - 1
+            if grain < 0.02:
+                imb = t.max() / t.mean() - 1
+                imb_base = tb.max() / tb.mean() - 1
+                assert imb < 0.025, (same, imb, grain)
+                assert imb < imb_base - 0.01, (same, imb, imb_base)
+        s_fd = 2 / (1 / sp[0] + 1 / sp[1])
+        norm = loads[0] * s_fd.mean() / np.array([s_fd[v % 8] for v in range(256)])
+        assert abs(info.item_cost_max_bin - norm.max()) <= 1
+        assert info.item_cost_total == int(loads[0].sum())
+
+
+def test_xcd_plan_keeps_heads_home_at_equal_speeds():
+    """Eight kv heads on eight XCDs with equal work and equal speeds: no
+    forward/dQ or dK/dV work leaves its kv head's XCD class; at unequal
+    speeds only a few per cent of it does."""
+    w, g, prob = _case("ctx32k_q2k", 1)
+    for spread, bound in ((0.0, 0.0), (0.05, 0.08)):
+        image, _ = skv.skv_schedule_build_xcd(prob, 256, np.ones((3, 8)) + spread *
+                                              np.sin(np.arange(24)).reshape(3, 8))
+        h, tiles, items, kv, fq, kq = _decode(image)
+        ncls = h["NCLASS"]
+        for qs, heads, cost in ((fq, items[:, I["HEAD"]], items[:, I["COST"]]),
+                                (kq, kv[:, K["HEAD"]], kv[:, K["COST"]])):
+            away = sum(int(cost[i]) for v, q in enumerate(qs) for i in q
+                       if heads[i] % ncls != v % ncls)
+            assert away <= bound * cost.sum(), (spread, away / cost.sum())
+
+
+def test_xcd_plan_arguments():
+    w, g, prob = _case("tiny_f32_ctx1k", 0, 0)
+    ok = np.ones((3, 8), np.float32)
+    with pytest.raises(skv.SplitKVError, match="divisible by 8"):
+        skv.skv_schedule_build_xcd(prob, 12, ok)
+    for bad in (0.0, -1.0, np.nan, np.inf):
+        sp = ok.copy()
+        sp[1, 3] = bad
+        with pytest.raises(skv.SplitKVError, match="finite and > 0"):
+            skv.skv_schedule_build_xcd(prob, 8, sp)
+    with pytest.raises(ValueError):
+        skv.skv_schedule_build_xcd(prob, 8, np.ones(8))
+    # the C entry point refuses a NULL speed table
+    info = skv.SkvScheduleInfo()
+    import ctypes
+    st = skv.lib().skv_schedule_build_xcd(ctypes.byref(prob.c), 8, None, None, 0,
+                                          ctypes.byref(info))
+    assert skv.STATUS_NAMES[st] == "SKV_ERR_INVALID_ARG"
+    # without speeds the image keeps one queue set and no XCD claim
+    image, info = skv.skv_schedule_build(prob, 8)
+    h = {k: int(image[v]) for k, v in H.items()}
+    assert info.xcd_mode == 0 and h["XCD"] == 0
+
+
+def test_speeds_from_stamps_invert_a_known_speed():
+    """Stamps made from a known per-XCD speed (queue time = planned load /
+    speed of the XCD it ran on, under any rotation of queues to XCDs, with
+    a workgroup missing its stamp) give that speed back, scaled to mean 1."""
+    w, g, prob = _case("ctx32k_q2k", 2, None, ctx=4096, anchor_lo=512, anchor_hi=4096,
+                       blocks_per_seq=16)
+    image, info = skv.skv_schedule_build(prob, 64)
+    loads = skv.queue_loads(image)
+    assert loads.shape == (3, 64) and loads[0].sum() == info.item_cost_total
+    assert loads[2].sum() == info.kv_cost_total
+    true = np.array([[1.0, 1.1, 0.9, 1.0, 1.05, 0.95, 1.0, 1.0]] * 3)
+    true[2] = true[2][::-1]
+    runs = []
+    for c in (0, 3, 5):
+        r = np.zeros((3, 64, 4), np.int64)
+        for k in range(3):
+            for v in range(64):
+                x = (v + c) % 8
+                r[k, v, 0] = 1000
+                r[k, v, 1] = 1000 + int(round(1e4 * loads[k, v] / true[k, x]))
+                r[k, v, 2] = x | 0x100   # high bits of XCC_ID are ignored
+        r[1, 7] = 0                      # a queue without stamps is skipped
+        runs.append(r)
+    got = skv.xcd_speeds_from_stamps(image, runs)
+    np.testing.assert_allclose(got, true / true.mean(1, keepdims=True), rtol=1e-3)
