@@ -460,6 +460,10 @@ def main():
                     help="instead of the benchmark: per-workgroup start/end stamps of the "
                          "forward, dQ and dK/dV kernels over --steps steps; realised against "
                          "planned imbalance")
+    ap.add_argument("--uniform-plan", action="store_true",
+                    help="plan the in-GPU work without per-XCD speeds (by default the bench "
+                         "measures each XCD's speed on the uniform plan and times the plan "
+                         "made for them)")
     ap.add_argument("--no-subrecords", action="store_true",
                     help="with the default workload, skip the sub-records of the varlen, "
                          "512K rank-share and 1M merge workloads")
@@ -635,6 +639,20 @@ def run_workload(args, workload):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    xcd = None
+    if not args.uniform_plan and n_wg % 8 == 0:
+        # per-XCD speeds from stamps of the uniform plan, then the plan made
+        # for them (outside the timed region); the step below uses it
+        runs = stamp_runs(step, n_wg, 6, torch)
+        speed = xcd_speeds(sh.image, runs, args.fwd_only)
+        xcd = {"speed": np.round(speed, 4).tolist(),
+               "uniform_plan_realized": {
+                   k: v["realized_imbalance_median"] for k, v in
+                   realized_balance(step, sh.info, 0, torch, args.fwd_only, runs=runs).items()}}
+        sh = skv.Shard(prob, n_workgroups=n_wg, xcd_speed=speed)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
     skv.skv_timing_collect()  # discard anything recorded before
     skv.skv_timing_enable(True)
     start = torch.cuda.Event(enable_timing=True)
@@ -729,6 +747,9 @@ def run_workload(args, workload):
                 "kv_items": sh.info.n_kv_items, "kv_item_imbalance_256cu": kv_imb,
                 "chunk_imbalance_256bins": chunk_imb, "plan_ms": 1e3 * float(np.median(plan_times)),
                 "workgroups": n_wg,
+                "plan": ("per-XCD speeds measured from clock stamps of the uniform plan "
+                         "(skv_schedule_build_xcd)" if xcd else "uniform (skv_schedule_build)"),
+                "xcd": xcd,
                 "realized": {k: {"imbalance_median": v["realized_imbalance_median"],
                                  "on_xcd_w_plus_c_mod_8": v["on_xcd_w_plus_c_mod_8"],
                                  "xcd_rotation_per_run": v["xcd_rotation_per_run"],
@@ -883,12 +904,10 @@ def balance_stats(runs, planned, names=("fwd_bf16", "bwd_dq", "bwd_dkdv")):
     return out
 
 
-def realized_balance(step, info, steps, torch, fwd_only=False):
-    """Stamp every workgroup for `steps` steps (outside any timed region)
-    and return balance_stats for the forward, dQ and dK/dV kernels (the
-    forward only with fwd_only)."""
+def stamp_runs(step, n, steps, torch):
+    """Per-workgroup stamps of `steps` steps (outside any timed region): a
+    list of [3, n, 4] arrays (forward, dQ, dK/dV)."""
     from block_sparse_split_amd import splitkv as skv
-    n = info.n_workgroups
     clk = torch.zeros(3 * n * 4, dtype=torch.int64, device="cuda")
     runs = []
     skv.skv_timing_wg_clock(clk)
@@ -900,11 +919,36 @@ def realized_balance(step, info, steps, torch, fwd_only=False):
             runs.append(clk.view(3, n, 4).cpu().numpy().copy())
     finally:
         skv.skv_timing_wg_clock(None)
-    planned = {"fwd_bf16": info.item_cost_max_bin / (info.item_cost_total / n) - 1,
-               "bwd_dq": info.item_cost_max_bin / (info.item_cost_total / n) - 1,
-               "bwd_dkdv": info.kv_cost_max_bin / (info.kv_cost_total / n) - 1}
-    return balance_stats(runs, planned, ("fwd_bf16",) if fwd_only else
+    return runs
+
+
+def planned_imbalance(info):
+    n = info.n_workgroups
+    return {"fwd_bf16": info.item_cost_max_bin / (info.item_cost_total / n) - 1,
+            "bwd_dq": info.item_cost_max_bin / (info.item_cost_total / n) - 1,
+            "bwd_dkdv": info.kv_cost_max_bin / (info.kv_cost_total / n) - 1}
+
+
+def realized_balance(step, info, steps, torch, fwd_only=False, runs=None):
+    """Stamp every workgroup for `steps` steps (or take `runs`) and return
+    balance_stats for the forward, dQ and dK/dV kernels (the forward only
+    with fwd_only)."""
+    if runs is None:
+        runs = stamp_runs(step, info.n_workgroups, steps, torch)
+    return balance_stats(runs, planned_imbalance(info), ("fwd_bf16",) if fwd_only else
                          ("fwd_bf16", "bwd_dq", "bwd_dkdv"))
+
+
+def xcd_speeds(image, runs, fwd_only):
+    """Per-XCD speeds of the three kernels from stamps of a plan (its
+    queue loads over the time spent on each XCD); a forward-only run gives
+    dQ the forward's speeds and dK/dV equal ones."""
+    from block_sparse_split_amd import splitkv as skv
+    sp = skv.xcd_speeds_from_stamps(image, runs)
+    if fwd_only:
+        sp[1] = sp[0]
+        sp[2] = 1.0
+    return sp
 
 
 def wg_balance(args):
@@ -933,14 +977,26 @@ def wg_balance(args):
 
     for _ in range(max(1, args.warmup)):
         step()
-    out = realized_balance(step, sh.info, args.steps, torch)
-    for name, v in out.items():
-        log(f"{name}: planned {v['planned_imbalance'] * 100:.2f} %, realised "
-            f"{v['realized_imbalance_median'] * 100:.2f} % (median of {args.steps}), "
-            f"mean {v['mean_workgroup_us']:.1f} us")
+    prob = shards.whole_context_problem(w, g)
+    runs = stamp_runs(step, n, args.steps, torch)
+    plans = {"uniform": realized_balance(step, sh.info, 0, torch, runs=runs)}
+    speed = xcd_speeds(sh.image, runs, False)
+    if n % 8 == 0:
+        # the same steps with the plan made for the XCD speeds just measured
+        sh = skv.Shard(prob, n_workgroups=n, xcd_speed=speed)
+        for _ in range(max(1, args.warmup)):
+            step()
+        plans["xcd"] = realized_balance(step, sh.info, args.steps, torch)
+    for plan, out in plans.items():
+        for name, v in out.items():
+            log(f"{plan} {name}: planned {v['planned_imbalance'] * 100:.2f} %, realised "
+                f"{v['realized_imbalance_median'] * 100:.2f} % (median of {args.steps}), "
+                f"mean {v['mean_workgroup_us']:.1f} us")
     print(json.dumps({"metric": "workgroup_balance", "workload": w.name, "workgroups": n,
                       "clock": "s_memrealtime, 100 MHz", "steps": args.steps,
-                      "kernels": out}), flush=True)
+                      "xcd_speed": np.round(speed, 4).tolist(),
+                      "kernels": plans["uniform"], "kernels_xcd_plan": plans.get("xcd")}),
+          flush=True)
 
 
 def plan_sweep():

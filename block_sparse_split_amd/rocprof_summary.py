@@ -265,24 +265,37 @@ def cmd_balance(a):
            f"{r['workload']}",
            f"command: {a.command}",
            f"kernel_source_sha256: {kernel_source_hash()}",
-           f"clock: {r['clock']}; workgroups: {r['workgroups']}; steps: {r['steps']}", "",
-           "kernel      planned  realised  mean_us  span_us  on XCD (w+c)%8  CUs   "
-           "mean time per XCD (XCC_ID register), relative"]
-    for k, v in r["kernels"].items():
-        m = v["mean_workgroup_us"]
-        rel = " ".join(f"{(x / m - 1) * 100:+.1f}%" for x in v["xcd_mean_us"])
-        out.append(f"{k:<10} {v['planned_imbalance'] * 100:7.2f}% "
-                   f"{v['realized_imbalance_median'] * 100:8.2f}% {m:8.1f} "
-                   f"{v['kernel_span_us_median']:8.1f}  {v['on_xcd_w_plus_c_mod_8'] * 100:5.1f}% "
-                   f"(c={v['xcd_rotation_per_run'][0]})  {v['distinct_cus_per_run']:4d}   {rel}")
-    out += ["", "planned = max/mean - 1 of the plan's workgroup loads (time units); realised = "
-            "median over",
-            "the steps of max/mean - 1 of the workgroups' measured durations; span = last end - "
-            "first start.",
-            "on XCD (w+c)%8: share of workgroups w whose XCC_ID is (w + c) mod 8 for one "
-            "rotation c per",
-            "launch (c printed for the first step); CUs: distinct (XCD, SE, CU) triples per "
-            "launch."]
+           f"clock: {r['clock']}; workgroups: {r['workgroups']}; steps: {r['steps']}"]
+    plans = [("uniform plan (skv_schedule_build)", r["kernels"])]
+    if r.get("kernels_xcd_plan"):
+        plans.append(("plan for per-XCD speeds (skv_schedule_build_xcd), speeds measured "
+                      "on the uniform plan's steps", r["kernels_xcd_plan"]))
+    for title, kernels in plans:
+        out += ["", f"## {title}"]
+        if kernels is r.get("kernels_xcd_plan"):
+            for name, sp in zip(("forward", "dQ", "dK/dV"), r["xcd_speed"]):
+                out.append(f"speed {name:<6} " + " ".join(f"{x:.3f}" for x in sp))
+        out.append("kernel      planned  realised  mean_us  span_us  on XCD (w+c)%8  CUs   "
+                   "mean time per XCD (XCC_ID register), relative")
+        for k, v in kernels.items():
+            m = v["mean_workgroup_us"]
+            rel = " ".join(f"{(x / m - 1) * 100:+.1f}%" for x in v["xcd_mean_us"])
+            out.append(f"{k:<10} {v['planned_imbalance'] * 100:7.2f}% "
+                       f"{v['realized_imbalance_median'] * 100:8.2f}% {m:8.1f} "
+                       f"{v['kernel_span_us_median']:8.1f}  "
+                       f"{v['on_xcd_w_plus_c_mod_8'] * 100:5.1f}% "
+                       f"(c={v['xcd_rotation_per_run'][0]})  {v['distinct_cus_per_run']:4d}   "
+                       f"{rel}")
+    out += ["", "planned = max/mean - 1 of the plan's workgroup loads (time units; in the "
+            "per-XCD plan,",
+            "each XCD's loads over its speed); realised = median over the steps of max/mean - 1 of "
+            "the measured",
+            "durations of the queues; span = last end - first start.",
+            "on XCD (w+c)%8: share of queues v whose XCC_ID is (v + c) mod 8 for one rotation "
+            "c per launch",
+            "(c printed for the first step; in the per-XCD plan, queue v is planned for XCD "
+            "v mod 8 and",
+            "claimed there, so c = 0); CUs: distinct (XCD, SE, CU) triples per launch."]
     emit("\n".join(out) + "\n", a.out)
 
 

@@ -110,13 +110,23 @@ def test_bench_tables(tmp_path):
          "xcd_rotation_per_run": [3, 3], "distinct_cus_per_run": 256}
     src = tmp_path / "wg.json"
     _json_line(src, {"workload": "w", "clock": "c", "workgroups": 256, "steps": 2,
-                     "kernels": {"bwd_dq": k}})
+                     "kernels": {"bwd_dq": k},
+                     "kernels_xcd_plan": {"bwd_dq": dict(k, realized_imbalance_median=0.02)},
+                     "xcd_speed": [[1.0] * 8, [1.05] + [1.0] * 7, [0.9] * 8]})
     out = tmp_path / "b.txt"
     rs.main(["balance", str(src), "--command", "cmd", "--out", str(out)])
-    row = [l.split() for l in out.read_text().splitlines() if l.startswith("bwd_dq")][0]
-    assert row[1:5] == ["0.50%", "4.00%", "100.0", "110.0"]
-    assert row[5:7] == ["100.0%", "(c=3)"] and row[7] == "256"
-    assert row[8:10] == ["+1.0%", "-1.0%"]
+    lines = out.read_text().splitlines()
+    uni, xcd = [l.split() for l in lines if l.startswith("bwd_dq")]
+    assert uni[1:5] == ["0.50%", "4.00%", "100.0", "110.0"]
+    assert uni[5:7] == ["100.0%", "(c=3)"] and uni[7] == "256"
+    assert uni[8:10] == ["+1.0%", "-1.0%"]
+    assert xcd[1:3] == ["0.50%", "2.00%"]
+    assert [l.split()[2] for l in lines if l.startswith("speed")] == ["1.000", "1.050", "0.900"]
+    # a record without the per-XCD plan prints the uniform table only
+    _json_line(src, {"workload": "w", "clock": "c", "workgroups": 256, "steps": 2,
+                     "kernels": {"bwd_dq": k}})
+    rs.main(["balance", str(src), "--command", "cmd", "--out", str(out)])
+    assert sum(l.startswith("bwd_dq") for l in out.read_text().splitlines()) == 1
 
     src = tmp_path / "sw.json"
     _json_line(src, {"points": [{"context": 4096, "draft_queries": 512, "ms_per_step": 0.5,
