@@ -640,7 +640,8 @@ def run_workload(args, workload):
         step()
     torch.cuda.synchronize()
     xcd = None
-    if not args.uniform_plan and n_wg % 8 == 0:
+    # (--compare-plans reorders the uniform plan's queues: it keeps that plan)
+    if not args.uniform_plan and not args.compare_plans and n_wg % 8 == 0:
         # per-XCD speeds from stamps of the uniform plan, then the plan made
         # for them (outside the timed region); the step below uses it
         runs = stamp_runs(step, n_wg, 6, torch)
@@ -820,9 +821,14 @@ def compare_item_plans(sh, step, kernels_lpt, args, torch):
     tile) and cut into equal-count runs, one per workgroup (no cost model).
     Both plans compute every item exactly once; only the queues differ."""
     from block_sparse_split_amd import splitkv as skv
+    from block_sparse_split_amd.csrc_layout import H
     img = sh.image.copy()
-    n_items, n_wg = int(img[11]), int(img[12])
-    off_items, off_qoff, off_queue = int(img[19]), int(img[20]), int(img[21])
+    n_items, n_wg = int(img[H["NITEMS"]]), int(img[H["NWG"]])
+    off_items, off_qoff, off_queue = (int(img[H["OFF_ITEMS"]]), int(img[H["OFF_QOFF"]]),
+                                      int(img[H["OFF_QUEUE"]]))
+    # the comparison reorders the forward's queues, which dQ shares in a
+    # plan made without per-XCD speeds
+    assert int(img[H["OFF_DQ_QUEUE"]]) == off_queue
     items = img[off_items:off_items + 8 * n_items].reshape(n_items, 8)
     order = np.lexsort((items[:, 2], items[:, 1], items[:, 0])).astype(np.int32)
     img[off_queue:off_queue + n_items] = order
@@ -925,7 +931,7 @@ def stamp_runs(step, n, steps, torch):
 def planned_imbalance(info):
     n = info.n_workgroups
     return {"fwd_bf16": info.item_cost_max_bin / (info.item_cost_total / n) - 1,
-            "bwd_dq": info.item_cost_max_bin / (info.item_cost_total / n) - 1,
+            "bwd_dq": info.dq_cost_max_bin / (info.dq_cost_total / n) - 1,
             "bwd_dkdv": info.kv_cost_max_bin / (info.kv_cost_total / n) - 1}
 
 

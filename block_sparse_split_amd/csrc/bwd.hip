@@ -145,10 +145,10 @@ __global__ __launch_bounds__(DqCfg<D>::kThreads, 1) void bwd_dq_kernel(BwdArgs a
   const sched_t anchors = S + S[H_OFF_ANCHORS];
   const sched_t los = S + S[H_OFF_LO];
   const sched_t tiles = S + S[H_OFF_TILES];
-  const sched_t items = S + S[H_OFF_ITEMS];
-  const sched_t queue = S + S[H_OFF_QUEUE];
+  const sched_t items = S + S[H_OFF_DQ_ITEMS];
+  const sched_t queue = S + S[H_OFF_DQ_QUEUE];
   const int vq = claim_queue(S, a.xcd_count);
-  const int qbeg = S[S[H_OFF_QOFF] + vq], qend = S[S[H_OFF_QOFF] + vq + 1];
+  const int qbeg = S[S[H_OFF_DQ_QOFF] + vq], qend = S[S[H_OFF_DQ_QOFF] + vq + 1];
   const float c = a.scale * kLog2e;
   const __bf16* Qg = static_cast<const __bf16*>(a.Q);
   const __bf16* dOg = static_cast<const __bf16*>(a.dO);
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const int32_t* S, const 
   constexpr int TPR = D / 8;
   constexpr int RPB = 256 / TPR;
   constexpr int BPT = kQTile / RPB;
-  const int32_t* rec = S + S[H_OFF_SPLIT] + (blockIdx.x / BPT) * S_WORDS;
+  const int32_t* rec = S + S[H_OFF_DQ_SPLIT] + (blockIdx.x / BPT) * S_WORDS;
   const int head = rec[S_HEAD], qt = rec[S_QT], slot0 = rec[S_SLOT0], ns = rec[S_NSLOT];
   const int rloc = (blockIdx.x % BPT) * RPB + threadIdx.x / TPR;
   const int c = (threadIdx.x % TPR) * 8;

@@ -592,11 +592,6 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
       }
     for (int k = 0; k < 3; ++k)
       for (int32_t b = 0; b < n_wg; ++b) spd[k].push_back(xcd_speed[k * skv::kXcds + b % skv::kXcds]);
-    // the forward and dQ kernels run the same items from the same queues
-    // (a query tile's partial slots are the same in both), so those queues
-    // are planned at the speed that gives a unit of work the mean of its
-    // two kernels' times
-    for (int32_t b = 0; b < n_wg; ++b) spd[0][b] = 2.0 / (1.0 / spd[0][b] + 1.0 / spd[1][b]);
   }
   const std::vector<Tile> tiles = build_tiles(p);
   const int32_t nt = int32_t(tiles.size());
@@ -771,8 +766,11 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
   };
   std::vector<int32_t> home_of(units.size());
   for (size_t ui = 0; ui < units.size(); ++ui) home_of[ui] = units[ui].head % n_cls_fwd;
-  FwdPlan chosen = plan_fwd(units, home_of, nullptr);
-  if (xcd) {
+  // the uniform plan, or with speeds the per-XCD plan if its slowest
+  // workgroup finishes first at those speeds
+  auto best_plan = [&](const std::vector<double>* speed) {
+    FwdPlan chosen = plan_fwd(units, home_of, nullptr);
+    if (speed == nullptr) return chosen;
     std::vector<int64_t> ucost;
     std::vector<int32_t> usteps;
     for (const Unit& u : units) {
@@ -781,7 +779,7 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
     }
     std::vector<std::pair<int32_t, int32_t>> tails;
     const std::vector<int32_t> where =
-        share_classes(ucost, home_of, class_speed(spd[0]), &usteps, kStepCost, kItemCost,
+        share_classes(ucost, home_of, class_speed(*speed), &usteps, kStepCost, kItemCost,
                       double(kItemCost), &tails);
     std::vector<Unit> us = units;
     for (const auto& [u, k] : tails) {  // unit u keeps its first k steps
@@ -791,25 +789,43 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
       us[u].k1 = us[u].k0 + k;
       us.push_back(tail);
     }
-    FwdPlan sp = plan_fwd(us, where, &spd[0]);
-    if (slowest(sp.load, spd[0]) < slowest(chosen.load, spd[0])) chosen = std::move(sp);
-  }
-  items = std::move(chosen.items);
-  q = std::move(chosen.q);
-  wg_load = std::move(chosen.load);
-  // query tiles with several items write partial slots, merged afterwards
-  std::vector<int32_t> split_rec;  // S_WORDS per split query tile
-  int32_t n_slots = 0;
-  {
+    FwdPlan sp = plan_fwd(us, where, speed);
+    if (slowest(sp.load, *speed) < slowest(chosen.load, *speed)) chosen = std::move(sp);
+    return chosen;
+  };
+  // query tiles with several items write partial slots, merged afterwards:
+  // one split record (S_WORDS) per such tile; returns the slot count
+  auto assign_slots = [&](std::vector<Item>& its, std::vector<int32_t>& rec) {
+    int32_t slots = 0;
     std::vector<std::vector<int32_t>> of(int64_t(g.hkv) * g.qt_per_head);
-    for (int32_t i = 0; i < int32_t(items.size()); ++i)
-      of[int64_t(items[i].head) * g.qt_per_head + items[i].qt].push_back(i);
+    for (int32_t i = 0; i < int32_t(its.size()); ++i)
+      of[int64_t(its[i].head) * g.qt_per_head + its[i].qt].push_back(i);
     for (int64_t k = 0; k < int64_t(of.size()); ++k) {
       if (of[k].size() < 2) continue;
-      split_rec.insert(split_rec.end(), {int32_t(k / g.qt_per_head), int32_t(k % g.qt_per_head),
-                                         n_slots, int32_t(of[k].size())});
-      for (int32_t i : of[k]) items[i].slot = n_slots++;
+      rec.insert(rec.end(), {int32_t(k / g.qt_per_head), int32_t(k % g.qt_per_head), slots,
+                             int32_t(of[k].size())});
+      for (int32_t i : of[k]) its[i].slot = slots++;
     }
+    return slots;
+  };
+  {
+    FwdPlan chosen = best_plan(xcd ? &spd[0] : nullptr);
+    items = std::move(chosen.items);
+    q = std::move(chosen.q);
+    wg_load = std::move(chosen.load);
+  }
+  std::vector<int32_t> split_rec;
+  const int32_t n_slots = assign_slots(items, split_rec);
+  // dQ runs the forward's items from the forward's queues, except with
+  // per-XCD speeds: the two kernels' XCD speeds differ, so dQ then gets a
+  // plan of its own (its own cuts, queues, partial slots and split records)
+  const bool dq_own = xcd;
+  FwdPlan dq;
+  std::vector<int32_t> dq_split_rec;
+  int32_t dq_slots = n_slots;
+  if (dq_own) {
+    dq = best_plan(&spd[1]);
+    dq_slots = assign_slots(dq.items, dq_split_rec);
   }
   // dK/dV items: two consecutive tiles per item (one if a lone tile is
   // left), plus draft groups of 128 draft tokens.  An item walks the 64-row
@@ -920,6 +936,12 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
   for (const auto& k : kv) kv_total += k.cost;
   int64_t item_total = 0;
   for (const auto& it : items) item_total += it.cost;
+  int64_t dq_total = item_total, dq_max_bin = max_bin;
+  if (dq_own) {
+    dq_total = 0;
+    for (const auto& it : dq.items) dq_total += it.cost;
+    dq_max_bin = max_time_load(dq.load, spd[1]);
+  }
 
   // Steps of an item that every row of its query tile sees whole: the
   // first maximal run of full-length tiles inside [max lo, min anchor) of
@@ -965,6 +987,15 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
   const int64_t off_kv = off; off += int64_t(kv.size()) * K_WORDS;
   const int64_t off_kvqoff = off; off += n_wg + 1;
   const int64_t off_kvqueue = off; off += int64_t(kv.size());
+  // dQ sections: the forward's unless dQ has a plan of its own
+  int64_t off_dq_items = off_items, off_dq_qoff = off_qoff, off_dq_queue = off_queue,
+          off_dq_split = off_split;
+  if (dq_own) {
+    off_dq_items = off; off += int64_t(dq.items.size()) * I_WORDS;
+    off_dq_qoff = off; off += n_wg + 1;
+    off_dq_queue = off; off += int64_t(dq.items.size());
+    off_dq_split = off; off += int64_t(dq_split_rec.size());
+  }
   const int64_t words = off;
   require(words < (int64_t(1) << 31), "schedule image too large");
 
@@ -976,7 +1007,7 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
                          (xcd ? kXcdCounterBytes : 0);
   // per-row statistics: per kv head, its rows plus kStatPad padding rows
   const int64_t bwd_ws = 4 * align_up(int64_t(g.hkv) * (g.rows_per_head + skv::kStatPad) * 4, 256) +
-                         align_up(int64_t(n_slots) * rows_slot * g.d * 4, 256) +
+                         align_up(int64_t(dq_slots) * rows_slot * g.d * 4, 256) +
                          (xcd ? kXcdCounterBytes : 0);
   std::memset(info, 0, sizeof(*info));
   info->words = words;
@@ -994,6 +1025,11 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
   info->kv_cost_total = kv_total;
   info->kv_cost_max_bin = kv_max_bin;
   info->xcd_mode = xcd ? 1 : 0;
+  info->n_dq_items = dq_own ? int32_t(dq.items.size()) : info->n_items;
+  info->n_dq_split_qtiles = dq_own ? int32_t(dq_split_rec.size() / S_WORDS) : info->n_split_qtiles;
+  info->n_dq_partial_slots = dq_slots;
+  info->dq_cost_total = dq_total;
+  info->dq_cost_max_bin = dq_max_bin;
   info->nb = g.nb;
   info->hq = g.hq;
   info->hkv = g.hkv;
@@ -1034,6 +1070,10 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
   H[H_OFF_KVQUEUE] = int32_t(off_kvqueue);
   H[H_NCLASS] = n_cls;
   H[H_XCD] = xcd ? 1 : 0;
+  H[H_OFF_DQ_ITEMS] = int32_t(off_dq_items);
+  H[H_OFF_DQ_QOFF] = int32_t(off_dq_qoff);
+  H[H_OFF_DQ_QUEUE] = int32_t(off_dq_queue);
+  H[H_OFF_DQ_SPLIT] = int32_t(off_dq_split);
   std::memcpy(image + off_anchors, A, size_t(g.nb) * 4);
   std::memcpy(image + off_lo, L, size_t(g.nb) * 4);
   for (int32_t t = 0; t < nt; ++t) {
@@ -1042,24 +1082,32 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
     w[T_POS] = tiles[t].pos;
     w[T_LEN] = tiles[t].len;
   }
-  for (size_t i = 0; i < items.size(); ++i) {
-    int32_t* w = image + off_items + int64_t(i) * I_WORDS;
-    w[I_HEAD] = items[i].head;
-    w[I_QT] = items[i].qt;
-    w[I_T0] = items[i].t0;
-    w[I_T1] = items[i].t1;
-    w[I_SLOT] = items[i].slot;
-    w[I_FLAGS] = items[i].flags;
-    w[I_COST] = int32_t(std::min<int64_t>(items[i].cost, INT32_MAX));
-    w[I_WHOLE] = whole_steps(items[i]);
-  }
-  int32_t pos = 0;
-  for (int32_t w = 0; w < n_wg; ++w) {
-    image[off_qoff + w] = pos;
-    for (int32_t it : q[w]) image[off_queue + pos++] = it;
-  }
-  image[off_qoff + n_wg] = pos;
-  std::copy(split_rec.begin(), split_rec.end(), image + off_split);
+  auto write_plan = [&](const std::vector<Item>& its, const std::vector<std::vector<int32_t>>& qs,
+                        const std::vector<int32_t>& rec, int64_t o_items, int64_t o_qoff,
+                        int64_t o_queue, int64_t o_split) {
+    for (size_t i = 0; i < its.size(); ++i) {
+      int32_t* w = image + o_items + int64_t(i) * I_WORDS;
+      w[I_HEAD] = its[i].head;
+      w[I_QT] = its[i].qt;
+      w[I_T0] = its[i].t0;
+      w[I_T1] = its[i].t1;
+      w[I_SLOT] = its[i].slot;
+      w[I_FLAGS] = its[i].flags;
+      w[I_COST] = int32_t(std::min<int64_t>(its[i].cost, INT32_MAX));
+      w[I_WHOLE] = whole_steps(its[i]);
+    }
+    int32_t at = 0;
+    for (int32_t w = 0; w < n_wg; ++w) {
+      image[o_qoff + w] = at;
+      for (int32_t it : qs[w]) image[o_queue + at++] = it;
+    }
+    image[o_qoff + n_wg] = at;
+    std::copy(rec.begin(), rec.end(), image + o_split);
+  };
+  write_plan(items, q, split_rec, off_items, off_qoff, off_queue, off_split);
+  if (dq_own)
+    write_plan(dq.items, dq.q, dq_split_rec, off_dq_items, off_dq_qoff, off_dq_queue,
+               off_dq_split);
   for (size_t i = 0; i < kv.size(); ++i) {
     int32_t* w = image + off_kv + int64_t(i) * K_WORDS;
     w[K_HEAD] = kv[i].head;
@@ -1072,7 +1120,7 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
     w[K_COST] = int32_t(std::min<int64_t>(kv[i].cost, INT32_MAX));
     w[K_WHOLE] = kv[i].whole;
   }
-  pos = 0;
+  int32_t pos = 0;
   for (int32_t w = 0; w < n_wg; ++w) {
     image[off_kvqoff + w] = pos;
     for (int32_t it : kq[w]) image[off_kvqueue + pos++] = it;
@@ -1365,8 +1413,8 @@ skv_status skv_attn_bwd(const skv_problem* p, const skv_schedule_info* info,
     a.n_local = info->n_local;
     a.scale = p->scale;
     a.n_wg = info->n_workgroups;
-    a.n_split = info->n_split_qtiles;
-    a.n_slots = info->n_partial_slots;
+    a.n_split = info->n_dq_split_qtiles;
+    a.n_slots = info->n_dq_partial_slots;
     a.with_draft = p->with_draft;
     const int64_t stat_bytes = align_up(
         int64_t(p->hkv) * (int64_t(p->nb) * 16 * (p->hq / p->hkv) + skv::kStatPad) * 4, 256);

@@ -6,7 +6,10 @@
 // the shard's key tiles, the forward/dQ work items with their per-workgroup
 // LPT queues, the list of query tiles whose key range is cut into several
 // items (their partials are merged after the main kernel), and the dK/dV
-// work items with their queues.
+// work items with their queues.  The dQ kernel reads its items, queues and
+// split records through the H_OFF_DQ_* words: they point at the forward's
+// sections, or at dQ's own when the schedule was planned per XCD (the two
+// kernels' XCD speeds differ, so each gets its own cuts and queues).
 //
 // Queues are indexed by a queue number v in [0, n_wg).  Normally workgroup
 // v runs queue v.  When H_XCD is set, queue v was planned for XCD v % 8 at
@@ -18,7 +21,7 @@
 namespace skv {
 
 constexpr int32_t kMagic = 0x314B5653;  // "SVK1"
-constexpr int32_t kVersion = 2;
+constexpr int32_t kVersion = 3;
 constexpr int kBlock = 16;      // draft tokens per anchor block
 constexpr int kTileK = 64;      // keys per key tile
 constexpr int kQTile = 256;     // query rows (token x head of one kv head) per tile
@@ -32,9 +35,10 @@ enum Hdr : int {
   H_NTILES, H_QT_PER_HEAD, H_NITEMS, H_NWG, H_NSPLIT, H_NSLOTS, H_NKV,
   H_OFF_ANCHORS, H_OFF_LO, H_OFF_TILES, H_OFF_ITEMS, H_OFF_QOFF, H_OFF_QUEUE,
   H_OFF_SPLIT, H_OFF_KV, H_OFF_KVQOFF, H_OFF_KVQUEUE, H_NCLASS,
-  H_XCD,
+  H_XCD, H_OFF_DQ_ITEMS, H_OFF_DQ_QOFF, H_OFF_DQ_QUEUE, H_OFF_DQ_SPLIT,
   H_WORDS = 32
 };
+static_assert(H_OFF_DQ_SPLIT < H_WORDS, "header words overflow the header");
 
 // Key tile: 4 words.
 enum TileW : int { T_ROW = 0, T_POS, T_LEN, T_PAD, T_WORDS = 4 };

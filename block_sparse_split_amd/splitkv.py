@@ -53,7 +53,10 @@ class SkvScheduleInfo(ctypes.Structure):
                 ("item_cost_total", ctypes.c_int64), ("item_cost_max_bin", ctypes.c_int64),
                 ("kv_cost_total", ctypes.c_int64), ("kv_cost_max_bin", ctypes.c_int64),
                 ("nb", ctypes.c_int32), ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
-                ("d", ctypes.c_int32), ("n_local", ctypes.c_int32), ("with_draft", ctypes.c_int32)]
+                ("d", ctypes.c_int32), ("n_local", ctypes.c_int32), ("with_draft", ctypes.c_int32),
+                ("n_dq_items", ctypes.c_int32), ("n_dq_split_qtiles", ctypes.c_int32),
+                ("n_dq_partial_slots", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("dq_cost_total", ctypes.c_int64), ("dq_cost_max_bin", ctypes.c_int64)]
 
 
 _lib = None
@@ -426,22 +429,22 @@ class Shard:
 
 def queue_loads(image):
     """Planned load (item costs) of every queue of a schedule image, per
-    kernel: array [3, n_wg] for the forward, dQ (the forward's queues) and
-    dK/dV queues."""
+    kernel: array [3, n_wg] for the forward, dQ and dK/dV queues (dQ's are
+    the forward's unless the image gives dQ sections of its own)."""
     from .csrc_layout import H, I, K, K_WORDS, I_WORDS
     img = np.asarray(image)
     h = {k: int(img[v]) for k, v in H.items()}
     n = h["NWG"]
-    items = img[h["OFF_ITEMS"]: h["OFF_ITEMS"] + h["NITEMS"] * I_WORDS].reshape(-1, I_WORDS)
-    kv = img[h["OFF_KV"]: h["OFF_KV"] + h["NKV"] * K_WORDS].reshape(-1, K_WORDS)
-    cost_items = items[:, I["COST"]].astype(np.int64)
-    cost_kv = kv[:, K["COST"]].astype(np.int64)
+
     out = np.zeros((3, n), np.int64)
-    for k, (qo, qq, cost) in enumerate(((h["OFF_QOFF"], h["OFF_QUEUE"], cost_items),
-                                        (h["OFF_QOFF"], h["OFF_QUEUE"], cost_items),
-                                        (h["OFF_KVQOFF"], h["OFF_KVQUEUE"], cost_kv))):
+    plans = ((h["OFF_ITEMS"], h["OFF_QOFF"], h["OFF_QUEUE"], I_WORDS, I["COST"]),
+             (h["OFF_DQ_ITEMS"], h["OFF_DQ_QOFF"], h["OFF_DQ_QUEUE"], I_WORDS, I["COST"]),
+             (h["OFF_KV"], h["OFF_KVQOFF"], h["OFF_KVQUEUE"], K_WORDS, K["COST"]))
+    for k, (oi, qo, qq, words, cw) in enumerate(plans):
         off = img[qo: qo + n + 1]
         q = img[qq: qq + off[-1]]
+        n_items = int(q.max()) + 1 if len(q) else 0
+        cost = img[oi: oi + n_items * words].reshape(-1, words)[:, cw].astype(np.int64)
         for v in range(n):
             out[k, v] = cost[q[off[v]: off[v + 1]]].sum()
     return out

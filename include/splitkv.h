@@ -74,11 +74,12 @@ const char* skv_last_error(void);
 
 /* ABI version of this header (bumped on incompatible changes; 2: four
  * words per workgroup in the clock-stamp buffer, skv_plan_lpt_split and
- * skv_dq_finalize added; 3: schedule image version 2 (a dQ queue of its
- * own, per-XCD queues), skv_schedule_info.xcd_mode, clock stamps indexed by
- * queue, skv_schedule_build_xcd added). */
+ * skv_dq_finalize added; 3: per-XCD queues, skv_schedule_info.xcd_mode,
+ * clock stamps indexed by queue, skv_schedule_build_xcd added; 4: schedule
+ * image version 3 (dQ sections of its own in xcd_mode) and the
+ * skv_schedule_info.n_dq_* / dq_cost_* fields). */
 int32_t skv_abi_version(void);
-#define SKV_ABI_VERSION 3
+#define SKV_ABI_VERSION 4
 
 /* ------------------------------------------------------------------------
  * Planner (host only, synchronous, deterministic).
@@ -191,6 +192,14 @@ typedef struct skv_schedule_info {
   int64_t kv_cost_max_bin;
   /* geometry the image was built for (checked by the device calls) */
   int32_t nb, hq, hkv, d, n_local, with_draft;
+  /* dQ plan: the forward's items and queues, except in xcd_mode, where dQ
+   * is planned on its own at the dQ kernel's XCD speeds */
+  int32_t n_dq_items;          /* dQ work items                             */
+  int32_t n_dq_split_qtiles;   /* query tiles cut into several dQ items     */
+  int32_t n_dq_partial_slots;  /* fp32 dQ partial slots for those tiles     */
+  int32_t reserved;
+  int64_t dq_cost_total;       /* sum of dQ item costs                      */
+  int64_t dq_cost_max_bin;     /* largest workgroup load (dQ items)         */
 } skv_schedule_info;
 
 /* Build the work schedule of one problem for n_workgroups persistent
@@ -226,17 +235,21 @@ skv_status skv_schedule_build(const skv_problem* p, int32_t n_workgroups,
  * xcd_speed[k * 8 + x] is the relative speed (work per unit time, any
  * positive scale) of XCD x in kernel k: 0 the forward, 1 dQ, 2 dK/dV, for
  * instance measured with skv_timing_wg_clock on a schedule without it.
- * Queue v is planned at the speed of XCD v % 8, by LPT with splitting over
- * bins of unequal speed: each piece goes to the bin of least time (load /
- * speed) of its kv head's XCD class, unless a bin of another class is
- * earlier by more than 1 % of a mean bin.  The forward and dQ kernels share
- * their queues (and so a query tile's partial slots), planned at the speed
- * that gives a unit of work the mean of its two kernels' times,
- * 2 / (1 / s_fwd + 1 / s_dQ); dK/dV items are placed the same way at their
- * own speeds, without cuts.  At run time each workgroup takes the next
- * unclaimed queue of the
- * XCD it runs on (the next XCD's if those are taken), so the plan holds
- * whatever XCD the dispatcher starts a launch on.  The per-XCD counters
+ * Queue v is planned at the speed of XCD v % 8.  Each XCD class (the
+ * workgroups that hold one kv head's work) first gets a share of the work
+ * in proportion to its total speed: classes above their share pass whole
+ * units (the largest that fit) and at most one unit's tail to the classes
+ * below theirs.  Each class then places its units on its workgroups by
+ * LPT with splitting at their speeds (each piece to the workgroup of least
+ * time, load / speed), at the target of a small grid whose slowest
+ * workgroup finishes first.  That plan is kept only if its slowest
+ * workgroup finishes before the uniform plan's at the same speeds.  The
+ * forward and dQ are planned separately at their own speeds (each with its
+ * own cuts, queues and partial slots; info->n_dq_* and dq_cost_* describe
+ * dQ's); dK/dV items are shared out the same way and placed by LPT at
+ * their speeds, without cuts.  At run time each workgroup takes the next
+ * unclaimed queue of the XCD it runs on (the next XCD's if those are
+ * taken), so the plan holds whatever XCD the dispatcher starts a launch on.  The per-XCD counters
  * live in the last 256 bytes of each workspace (counted in the workspace
  * sizes); the device calls zero them before each launch.  info->xcd_mode
  * is set.  Requires n_workgroups divisible by 8.

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     L = skv.lib()
     for name in declared:
         assert hasattr(L, name)
-    assert L.skv_abi_version() == 3
+    assert L.skv_abi_version() == 4
 
 
 def test_invalid_arguments_return_status_codes():

@@ -1,8 +1,9 @@
 """CPU checks of the schedule planned for XCDs of unequal speed
-(skv_schedule_build_xcd): it covers the same work once, balances time
-rather than load, keeps work in its kv head's XCD class unless moving it
-saves time, and the speed estimate inverts the stamps it is made from.  No
-device call is made."""
+(skv_schedule_build_xcd): the forward, dQ and dK/dV plans each cover the
+same work once, balance time rather than load at their own kernel's
+speeds, keep work in its kv head's XCD class unless moving it saves time,
+and the speed estimate inverts the stamps it is made from.  No device call
+is made."""
 import numpy as np
 import pytest
 
@@ -40,6 +41,15 @@ def _decode(image):
             _queues(image, "OFF_KVQOFF", "OFF_KVQUEUE", h["NKV"]))
 
 
+def _decode_dq(image, info):
+    """dQ's items, queues and split records (dQ's own sections)."""
+    h = {k: int(image[v]) for k, v in H.items()}
+    n = info.n_dq_items
+    items = image[h["OFF_DQ_ITEMS"]: h["OFF_DQ_ITEMS"] + n * I_WORDS].reshape(-1, I_WORDS)
+    split = image[h["OFF_DQ_SPLIT"]: h["OFF_DQ_SPLIT"] + 4 * info.n_dq_split_qtiles]
+    return items, _queues(image, "OFF_DQ_QOFF", "OFF_DQ_QUEUE", n), split.reshape(-1, 4)
+
+
 def _speeds(seed, spread):
     rng = np.random.default_rng(seed)
     return (1.0 + spread * rng.uniform(-1, 1, (3, 8))).astype(np.float32)
@@ -64,41 +74,57 @@ def test_xcd_plan_covers_the_work_once(case):
     w, g, prob = _case(name, seed, shard_of, **over)
     image, info = skv.skv_schedule_build_xcd(prob, n_wg, _speeds(seed, 0.1))
     assert info.xcd_mode == 1
-    h, tiles, items, kv, fq, kq = _decode(image)
+    h, tiles, items_f, kv, fq_f, kq = _decode(image)
     assert h["XCD"] == 1 and h["NWG"] == n_wg
+    items_d, fq_d, split_d = _decode_dq(image, info)
+    # dQ has sections of its own, after the forward's
+    assert h["OFF_DQ_ITEMS"] > h["OFF_ITEMS"] and h["OFF_DQ_SPLIT"] > h["OFF_SPLIT"]
     G = w.hq // w.hkv
     qtph = -(-w.nq * G // QTILE)
-    seen = np.zeros((w.hkv, qtph, len(tiles)), np.int32)
-    draft = np.zeros((w.hkv, qtph), np.int32)
-    for it in items:
-        hd, qt, t0, t1 = it[I["HEAD"]], it[I["QT"]], it[I["T0"]], it[I["T1"]]
-        seen[hd, qt, t0:t1] += 1
-        draft[hd, qt] += it[I["FLAGS"]] & 1
-        b0 = qt * (QTILE // G) // BLOCK
-        b1 = min(w.nb, -(-((qt + 1) * (QTILE // G)) // BLOCK))
-        want = ITEM_COST + STEP_COST * (t1 - t0)
-        if it[I["FLAGS"]] & 1:
-            want += STEP_COST * -(-((b1 - b0) * BLOCK) // 64)
-        assert it[I["COST"]] == want
-    for qt in range(qtph):
-        b0 = qt * (QTILE // G) // BLOCK
-        b1 = min(w.nb, -(-((qt + 1) * (QTILE // G)) // BLOCK))
-        vis = np.array([oracle.tile_pairs_visible(g.anchors[b0:b1], g.lo[b0:b1], t[1],
-                                                  t[1] + t[2]) > 0 for t in tiles], bool)
-        for hd in range(w.hkv):
-            assert np.array_equal(seen[hd, qt] > 0, vis)
-            assert seen[hd, qt].max(initial=0) <= 1
-            assert draft[hd, qt] == int(prob.c.with_draft)
-    for qs, n in ((fq, len(items)), (kq, len(kv))):
-        assert sorted(i for q in qs for i in q) == list(range(n))
-    # partial slots: a query tile cut into several items numbers them
-    # consecutively, a single item writes its rows directly
-    per_qt = {}
-    for it in items:
-        per_qt.setdefault((it[0], it[1]), []).append(it[I["SLOT"]])
-    slots = sorted(s for v in per_qt.values() if len(v) > 1 for s in v)
-    assert slots == list(range(info.n_partial_slots))
-    assert all(v == [-1] for v in per_qt.values() if len(v) == 1)
+    for items, fq, n_slots in ((items_f, fq_f, info.n_partial_slots),
+                               (items_d, fq_d, info.n_dq_partial_slots)):
+        seen = np.zeros((w.hkv, qtph, len(tiles)), np.int32)
+        draft = np.zeros((w.hkv, qtph), np.int32)
+        for it in items:
+            hd, qt, t0, t1 = it[I["HEAD"]], it[I["QT"]], it[I["T0"]], it[I["T1"]]
+            seen[hd, qt, t0:t1] += 1
+            draft[hd, qt] += it[I["FLAGS"]] & 1
+            b0 = qt * (QTILE // G) // BLOCK
+            b1 = min(w.nb, -(-((qt + 1) * (QTILE // G)) // BLOCK))
+            want = ITEM_COST + STEP_COST * (t1 - t0)
+            if it[I["FLAGS"]] & 1:
+                want += STEP_COST * -(-((b1 - b0) * BLOCK) // 64)
+            assert it[I["COST"]] == want
+        for qt in range(qtph):
+            b0 = qt * (QTILE // G) // BLOCK
+            b1 = min(w.nb, -(-((qt + 1) * (QTILE // G)) // BLOCK))
+            vis = np.array([oracle.tile_pairs_visible(g.anchors[b0:b1], g.lo[b0:b1], t[1],
+                                                      t[1] + t[2]) > 0 for t in tiles], bool)
+            for hd in range(w.hkv):
+                assert np.array_equal(seen[hd, qt] > 0, vis)
+                assert seen[hd, qt].max(initial=0) <= 1
+                assert draft[hd, qt] == int(prob.c.with_draft)
+        assert sorted(i for q in fq for i in q) == list(range(len(items)))
+        # partial slots: a query tile cut into several items numbers them
+        # consecutively, a single item writes its rows directly
+        per_qt = {}
+        for it in items:
+            per_qt.setdefault((it[0], it[1]), []).append(it[I["SLOT"]])
+        slots = sorted(s for v in per_qt.values() if len(v) > 1 for s in v)
+        assert slots == list(range(n_slots))
+        assert all(v == [-1] for v in per_qt.values() if len(v) == 1)
+    assert sorted(i for q in kq for i in q) == list(range(len(kv)))
+    # dQ's split records: one per cut query tile, naming its slots
+    recs = sorted(((int(r[0]), int(r[1])), int(r[2]), int(r[3])) for r in split_d)
+    cut = {}
+    for it in items_d:
+        if it[I["SLOT"]] >= 0:
+            cut.setdefault((int(it[0]), int(it[1])), []).append(int(it[I["SLOT"]]))
+    assert recs == sorted((k, min(v), len(v)) for k, v in cut.items())
+    assert info.n_dq_items == len(items_d) and info.n_dq_split_qtiles == len(split_d)
+    # the backward workspace holds dQ's slots, the forward's holds the forward's
+    assert info.bwd_workspace_bytes >= info.n_dq_partial_slots * QTILE * w.d * 4
+    assert info.fwd_workspace_bytes >= info.n_partial_slots * QTILE * (w.d + 1) * 4
 
 
 def _times(loads, speed8):
@@ -110,49 +136,39 @@ def _times(loads, speed8):
                                             ("varlen8_fwdbwd", 3, {}),
                                             ("cp64_rank0_ctx512k", 2, {})])
 def test_xcd_plan_balances_time_at_unequal_speeds(name, seed, over):
-    """With XCD speeds 0.95-1.05 the slowest queue never finishes later
-    than in the uniform plan timed at the same speeds; where the items are
-    fine enough (the uniform plan balances equal speeds within 2 %), queue
-    time is balanced within 2.5 % while the uniform plan, at these speeds,
-    is off by several per cent.  The forward and dQ share their queues, planned so
-    that a unit of work gets the mean of its two kernels' times: that mean
-    is what is balanced (and each kernel's own time when their speeds
-    agree); dK/dV queues at their own speed.  info reports the
-    speed-normalised maximum."""
+    """With XCD speeds 0.95-1.05 (different in each kernel) the slowest
+    queue of each kernel never finishes later than in the uniform plan
+    timed at the same speeds; where the items are fine enough (the uniform
+    plan balances equal speeds within 2 %), queue time is balanced within
+    2.5 % while the uniform plan, at these speeds, is off by several per
+    cent.  The forward, dQ and dK/dV are each planned at their own speeds.
+    info reports each plan's speed-normalised maximum."""
     w, g, prob = _case(name, seed, 0 if name.startswith("cp64") else None, **over)
     sp = _speeds(seed + 10, 0.05)
     base, _ = skv.skv_schedule_build(prob, 256)
     bloads = skv.queue_loads(base).astype(np.float64)
-    for same in (True, False):
-        if same:
-            sp[1] = sp[0]
-        image, info = skv.skv_schedule_build_xcd(prob, 256, sp)
-        loads = skv.queue_loads(image).astype(np.float64)
-        both = _times(loads[0], sp[0]) + _times(loads[1], sp[1])
-        both_base = _times(bloads[0], sp[0]) + _times(bloads[1], sp[1])
-        # (time at the speeds, uniform plan's time at the speeds, uniform
-        # plan's own load imbalance: the granularity of the items)
-        checks = [(both, both_base, bloads[0]),
-                  (_times(loads[2], sp[2]), _times(bloads[2], sp[2]), bloads[2])]
-        if same:
-            checks.append((_times(loads[0], sp[0]), _times(bloads[0], sp[0]), bloads[0]))
-        for t, tb, lu in checks:
-            # never slower than the uniform plan at these speeds (the
-            # builder keeps whichever finishes first) ...
-            assert t.max() <= tb.max() * (1 + 1e-9), (same, t.max(), tb.max())
-            # ... and where the items are fine enough for the uniform plan
-            # to balance equal speeds within 2 %, within 2.5 % here and
-            # clearly better than the uniform plan
-            grain = lu.max() / lu.mean() - 1
-            if grain < 0.02:
-                imb = t.max() / t.mean() - 1
-                imb_base = tb.max() / tb.mean() - 1
-                assert imb < 0.025, (same, imb, grain)
-                assert imb < imb_base - 0.01, (same, imb, imb_base)
-        s_fd = 2 / (1 / sp[0] + 1 / sp[1])
-        norm = loads[0] * s_fd.mean() / np.array([s_fd[v % 8] for v in range(256)])
-        assert abs(info.item_cost_max_bin - norm.max()) <= 1
-        assert info.item_cost_total == int(loads[0].sum())
+    image, info = skv.skv_schedule_build_xcd(prob, 256, sp)
+    loads = skv.queue_loads(image).astype(np.float64)
+    for k in range(3):
+        t, tb, lu = _times(loads[k], sp[k]), _times(bloads[k], sp[k]), bloads[k]
+        # never slower than the uniform plan at these speeds (the builder
+        # keeps whichever finishes first) ...
+        assert t.max() <= tb.max() * (1 + 1e-9), (k, t.max(), tb.max())
+        # ... and where the items are fine enough for the uniform plan to
+        # balance equal speeds within 2 %, within 2.5 % here and clearly
+        # better than the uniform plan
+        grain = lu.max() / lu.mean() - 1
+        if grain < 0.02:
+            imb = t.max() / t.mean() - 1
+            imb_base = tb.max() / tb.mean() - 1
+            assert imb < 0.025, (k, imb, grain)
+            assert imb < imb_base - 0.01, (k, imb, imb_base)
+    for k, mx, tot in ((0, info.item_cost_max_bin, info.item_cost_total),
+                       (1, info.dq_cost_max_bin, info.dq_cost_total),
+                       (2, info.kv_cost_max_bin, info.kv_cost_total)):
+        norm = loads[k] * sp[k].mean() / np.array([sp[k][v % 8] for v in range(256)])
+        assert abs(mx - norm.max()) <= 1, k
+        assert tot == int(loads[k].sum()), k
 
 
 def test_xcd_plan_keeps_heads_home_at_equal_speeds():
@@ -161,11 +177,13 @@ def test_xcd_plan_keeps_heads_home_at_equal_speeds():
     speeds only a few per cent of it does."""
     w, g, prob = _case("ctx32k_q2k", 1)
     for spread, bound in ((0.0, 0.0), (0.05, 0.08)):
-        image, _ = skv.skv_schedule_build_xcd(prob, 256, np.ones((3, 8)) + spread *
-                                              np.sin(np.arange(24)).reshape(3, 8))
+        image, info = skv.skv_schedule_build_xcd(prob, 256, np.ones((3, 8)) + spread *
+                                                 np.sin(np.arange(24)).reshape(3, 8))
         h, tiles, items, kv, fq, kq = _decode(image)
+        items_d, fq_d, _ = _decode_dq(image, info)
         ncls = h["NCLASS"]
         for qs, heads, cost in ((fq, items[:, I["HEAD"]], items[:, I["COST"]]),
+                                (fq_d, items_d[:, I["HEAD"]], items_d[:, I["COST"]]),
                                 (kq, kv[:, K["HEAD"]], kv[:, K["COST"]])):
             away = sum(int(cost[i]) for v, q in enumerate(qs) for i in q
                        if heads[i] % ncls != v % ncls)
@@ -190,10 +208,17 @@ def test_xcd_plan_arguments():
     st = skv.lib().skv_schedule_build_xcd(ctypes.byref(prob.c), 8, None, None, 0,
                                           ctypes.byref(info))
     assert skv.STATUS_NAMES[st] == "SKV_ERR_INVALID_ARG"
-    # without speeds the image keeps one queue set and no XCD claim
+    # without speeds the image keeps one queue set, shared by the forward
+    # and dQ, and no XCD claim
     image, info = skv.skv_schedule_build(prob, 8)
     h = {k: int(image[v]) for k, v in H.items()}
     assert info.xcd_mode == 0 and h["XCD"] == 0
+    for f in ("ITEMS", "QOFF", "QUEUE", "SPLIT"):
+        assert h["OFF_DQ_" + f] == h["OFF_" + f]
+    assert (info.n_dq_items, info.n_dq_split_qtiles, info.n_dq_partial_slots,
+            info.dq_cost_total, info.dq_cost_max_bin) == (
+        info.n_items, info.n_split_qtiles, info.n_partial_slots, info.item_cost_total,
+        info.item_cost_max_bin)
 
 
 def test_speeds_from_stamps_invert_a_known_speed():
