@@ -642,18 +642,29 @@ def run_workload(args, workload):
     xcd = None
     # (--compare-plans reorders the uniform plan's queues: it keeps that plan)
     if not args.uniform_plan and not args.compare_plans and n_wg % 8 == 0:
-        # per-XCD speeds from stamps of the uniform plan, then the plan made
-        # for them (outside the timed region); the step below uses it
+        # per-XCD speeds and measured cost scales from stamps of the uniform
+        # plan, a plan made for them, then a refit over the stamps of both
+        # plans and the plan the step below uses (all outside the timed
+        # region)
         runs = stamp_runs(step, n_wg, 6, torch)
-        speed = xcd_speeds(sh.image, runs, args.fwd_only)
+        uni_realized = {k: v["realized_imbalance_median"] for k, v in
+                        realized_balance(step, sh.info, 0, torch, args.fwd_only,
+                                         runs=runs).items()}
+        data = [(sh.image, runs, None)]
+        for rnd in range(2):
+            speed, scale = calibrate(data, args.fwd_only)
+            sh = skv.Shard(prob, n_workgroups=n_wg, xcd_speed=speed, cost_scale=scale)
+            for _ in range(args.warmup):
+                step()
+            torch.cuda.synchronize()
+            if rnd == 0:
+                data.append((sh.image, stamp_runs(step, n_wg, 6, torch), scale))
         xcd = {"speed": np.round(speed, 4).tolist(),
-               "uniform_plan_realized": {
-                   k: v["realized_imbalance_median"] for k, v in
-                   realized_balance(step, sh.info, 0, torch, args.fwd_only, runs=runs).items()}}
-        sh = skv.Shard(prob, n_workgroups=n_wg, xcd_speed=speed)
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
+               "cost_scale_range": [[round(float(x.min()), 4), round(float(x.max()), 4)]
+                                    for x in scale],
+               "calibration": "two rounds of 6 stamped steps (uniform plan, then the "
+                              "first calibrated plan)",
+               "uniform_plan_realized": uni_realized}
     skv.skv_timing_collect()  # discard anything recorded before
     skv.skv_timing_enable(True)
     start = torch.cuda.Event(enable_timing=True)
@@ -748,8 +759,9 @@ def run_workload(args, workload):
                 "kv_items": sh.info.n_kv_items, "kv_item_imbalance_256cu": kv_imb,
                 "chunk_imbalance_256bins": chunk_imb, "plan_ms": 1e3 * float(np.median(plan_times)),
                 "workgroups": n_wg,
-                "plan": ("per-XCD speeds measured from clock stamps of the uniform plan "
-                         "(skv_schedule_build_xcd)" if xcd else "uniform (skv_schedule_build)"),
+                "plan": ("per-XCD speeds and per-(kv head, query tile group) cost scales "
+                         "fitted to clock stamps (skv_schedule_build_xcd)" if xcd
+                         else "uniform (skv_schedule_build)"),
                 "xcd": xcd,
                 "realized": {k: {"imbalance_median": v["realized_imbalance_median"],
                                  "on_xcd_w_plus_c_mod_8": v["on_xcd_w_plus_c_mod_8"],
@@ -945,16 +957,16 @@ def realized_balance(step, info, steps, torch, fwd_only=False, runs=None):
                          ("fwd_bf16", "bwd_dq", "bwd_dkdv"))
 
 
-def xcd_speeds(image, runs, fwd_only):
-    """Per-XCD speeds of the three kernels from stamps of a plan (its
-    queue loads over the time spent on each XCD); a forward-only run gives
-    dQ the forward's speeds and dK/dV equal ones."""
+def calibrate(data, fwd_only):
+    """Per-XCD speeds and cost scales fitted to stamped runs of one or more
+    plans (skv.calibrate_from_stamps); a forward-only run gives dQ the
+    forward's and dK/dV equal speeds."""
     from block_sparse_split_amd import splitkv as skv
-    sp = skv.xcd_speeds_from_stamps(image, runs)
+    sp, sc = skv.calibrate_from_stamps(data)
     if fwd_only:
-        sp[1] = sp[0]
+        sp[1], sc[1] = sp[0], sc[0]
         sp[2] = 1.0
-    return sp
+    return sp, sc
 
 
 def wg_balance(args):
@@ -986,13 +998,25 @@ def wg_balance(args):
     prob = shards.whole_context_problem(w, g)
     runs = stamp_runs(step, n, args.steps, torch)
     plans = {"uniform": realized_balance(step, sh.info, 0, torch, runs=runs)}
-    speed = xcd_speeds(sh.image, runs, False)
+    data = [(sh.image, runs, None)]
+    speed, scale = calibrate(data, False)
     if n % 8 == 0:
         # the same steps with the plan made for the XCD speeds just measured
+        # (no cost scales), then with speeds and cost scales fitted to the
+        # uniform plan's stamps and, in a second round, to those of the first
+        # calibrated plan as well
         sh = skv.Shard(prob, n_workgroups=n, xcd_speed=speed)
         for _ in range(max(1, args.warmup)):
             step()
         plans["xcd"] = realized_balance(step, sh.info, args.steps, torch)
+        for rnd in range(2):
+            speed, scale = calibrate(data, False)
+            sh = skv.Shard(prob, n_workgroups=n, xcd_speed=speed, cost_scale=scale)
+            for _ in range(max(1, args.warmup)):
+                step()
+            runs = stamp_runs(step, n, args.steps, torch)
+            data.append((sh.image, runs, scale))
+        plans["calibrated"] = realized_balance(step, sh.info, 0, torch, runs=runs)
     for plan, out in plans.items():
         for name, v in out.items():
             log(f"{plan} {name}: planned {v['planned_imbalance'] * 100:.2f} %, realised "
@@ -1001,7 +1025,10 @@ def wg_balance(args):
     print(json.dumps({"metric": "workgroup_balance", "workload": w.name, "workgroups": n,
                       "clock": "s_memrealtime, 100 MHz", "steps": args.steps,
                       "xcd_speed": np.round(speed, 4).tolist(),
-                      "kernels": plans["uniform"], "kernels_xcd_plan": plans.get("xcd")}),
+                      "cost_scale_range": [[round(float(x.min()), 4), round(float(x.max()), 4)]
+                                           for x in scale],
+                      "kernels": plans["uniform"], "kernels_xcd_plan": plans.get("xcd"),
+                      "kernels_calibrated_plan": plans.get("calibrated")}),
           flush=True)
 
 

@@ -245,15 +245,21 @@ struct SplitJob {
 // b has speed speed[b] and its time is load / speed.  Pieces in the same
 // order go to the bin of least time (ties: lower bin), with the cut rule
 // above against a target time T (a bin's room is (T - time) * speed).
-// With every speed equal this is the placement above.
+// With every speed equal this is the placement above.  With `scale`, unit
+// u's costs (fixed part and steps alike) are multiplied by scale[u] and
+// rounded: a measured correction of the cost model for that unit's work.
 struct SpeedJob {
   std::vector<int64_t> extra;
   std::vector<int32_t> steps;
   std::vector<double> speed;
+  std::vector<double> scale;  // per unit; empty: 1
   int64_t item_cost = 0, step_cost = 0;
 
+  int64_t scaled(int32_t u, int64_t c) const {
+    return scale.empty() ? c : int64_t(std::llround(scale[u] * double(c)));
+  }
   int64_t cost(int32_t u, int32_t k0) const {
-    return item_cost + (k0 == 0 ? extra[u] : 0) + step_cost * (steps[u] - k0);
+    return scaled(u, item_cost + (k0 == 0 ? extra[u] : 0) + step_cost * (steps[u] - k0));
   }
 
   std::vector<Piece> pass(double target, std::vector<int64_t>* load_out) const {
@@ -284,13 +290,13 @@ struct SpeedJob {
       const int64_t head = item_cost + (pc.k0 == 0 ? extra[pc.unit] : 0);
       const double room = (target - time[b]) * speed[b];
       if (time[b] + double(pc.cost) / speed[b] > target && n - pc.k0 > 1 &&
-          room >= double(head + step_cost)) {
+          room >= double(scaled(pc.unit, head + step_cost))) {
         int64_t acc = head;
         int32_t k = pc.k0;
-        while (k < n && double(acc + step_cost) <= room) acc += step_cost, ++k;
+        while (k < n && double(scaled(pc.unit, acc + step_cost)) <= room) acc += step_cost, ++k;
         if (k < n) {
           k_end = k;
-          placed = acc;
+          placed = scaled(pc.unit, acc);
           pend.push({cost(pc.unit, k), pc.unit, k});
         }
       }
@@ -361,7 +367,8 @@ std::vector<int32_t> share_classes(std::vector<int64_t> cost, const std::vector<
                                    const std::vector<double>& cls_speed,
                                    const std::vector<int32_t>* steps, int64_t step_cost,
                                    int64_t tail_fixed, double tol,
-                                   std::vector<std::pair<int32_t, int32_t>>* tails) {
+                                   std::vector<std::pair<int32_t, int32_t>>* tails,
+                                   const std::vector<double>* unit_scale = nullptr) {
   const int32_t n_cls = int32_t(cls_speed.size());
   std::vector<int32_t> where = home;
   std::vector<double> have(n_cls, 0.0), want(n_cls, 0.0);
@@ -394,16 +401,19 @@ std::vector<int32_t> share_classes(std::vector<int64_t> cost, const std::vector<
         const int32_t u = *it, n = (*steps)[u];
         if (n < 2) continue;
         // tail of t steps: moves tail_fixed + t * step_cost, the head keeps
-        // the rest (the unit's cost less t * step_cost)
+        // the rest (the unit's cost less t * step_cost); both scaled by the
+        // unit's cost scale if there is one
+        const double sc = unit_scale ? (*unit_scale)[u] : 1.0;
         const int64_t t = std::min<int64_t>(n - 1, std::max<int64_t>(
-            1, std::llround((excess - double(tail_fixed)) / double(step_cost))));
-        const int64_t moved = tail_fixed + t * step_cost;
+            1, std::llround((excess / sc - double(tail_fixed)) / double(step_cost))));
+        const int64_t moved = std::llround(sc * double(tail_fixed + t * step_cost));
+        const int64_t kept_less = std::llround(sc * double(t * step_cost));
         tails->push_back({u, int32_t(n - t)});
-        cost[u] -= t * step_cost;
+        cost[u] -= kept_less;
         cost.push_back(moved);
         where.push_back(c);
         given.push_back(int32_t(cost.size() - 1));
-        have[c] -= double(t * step_cost);
+        have[c] -= double(kept_less);
         break;
       }
     }
@@ -576,7 +586,8 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 // planned at the speed of XCD v % kXcds and the kernels claim queues by the
 // XCD they run on.
 void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
-                    int32_t* image, int64_t capacity, skv_schedule_info* info) {
+                    const float* cost_scale, int32_t* image, int64_t capacity,
+                    skv_schedule_info* info) {
   require(info != nullptr, "info must not be NULL");
   const Geometry g = check_problem(p);
   if (n_wg == 0) n_wg = device_cu_count();
@@ -592,6 +603,14 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
       }
     for (int k = 0; k < 3; ++k)
       for (int32_t b = 0; b < n_wg; ++b) spd[k].push_back(xcd_speed[k * skv::kXcds + b % skv::kXcds]);
+  }
+  // cost scales: [2][hkv][qt_per_head] (forward, dQ), only with speeds
+  require(cost_scale == nullptr || xcd, "cost scales need per-XCD speeds");
+  if (cost_scale) {
+    const int64_t n_sc = 2 * int64_t(g.hkv) * g.qt_per_head;
+    for (int64_t i = 0; i < n_sc; ++i)
+      require(std::isfinite(cost_scale[i]) && cost_scale[i] > 0.f,
+              "cost scales must be finite and > 0");
   }
   const std::vector<Tile> tiles = build_tiles(p);
   const int32_t nt = int32_t(tiles.size());
@@ -713,7 +732,7 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
   // pieces of `units` placed per class: where[u] is unit u's class, and
   // the class's workgroups run at `speed` (nullptr: uniform SplitJob)
   auto plan_fwd = [&](const std::vector<Unit>& us, const std::vector<int32_t>& where,
-                      const std::vector<double>* speed) {
+                      const std::vector<double>* speed, const std::vector<double>* uscale) {
     FwdPlan pl;
     pl.q.assign(n_wg, {});
     pl.load.assign(n_wg, 0);
@@ -729,13 +748,16 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
         }
       std::vector<int64_t> load;
       std::vector<Piece> pieces;
-      if (speed) {
+      if (speed || uscale) {
         SpeedJob job;
         job.item_cost = kItemCost;
         job.step_cost = kStepCost;
         job.extra = extra;
         job.steps = steps;
-        for (int32_t b = cls; b < n_wg; b += n_cls_fwd) job.speed.push_back((*speed)[b]);
+        for (int32_t b = cls; b < n_wg; b += n_cls_fwd)
+          job.speed.push_back(speed ? (*speed)[b] : 1.0);
+        if (uscale)
+          for (int32_t ui : ids) job.scale.push_back((*uscale)[ui]);
         pieces = job.pass(job.best_target(), &load);
       } else {
         SplitJob job;
@@ -767,29 +789,37 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
   std::vector<int32_t> home_of(units.size());
   for (size_t ui = 0; ui < units.size(); ++ui) home_of[ui] = units[ui].head % n_cls_fwd;
   // the uniform plan, or with speeds the per-XCD plan if its slowest
-  // workgroup finishes first at those speeds
-  auto best_plan = [&](const std::vector<double>* speed) {
-    FwdPlan chosen = plan_fwd(units, home_of, nullptr);
+  // workgroup finishes first at those speeds; with cost scales (kernel k's
+  // slice of cost_scale) both plans place the scaled costs
+  auto best_plan = [&](const std::vector<double>* speed, int k) {
+    std::vector<double> usc;
+    if (cost_scale)
+      for (const Unit& u : units)
+        usc.push_back(cost_scale[(int64_t(k) * g.hkv + u.head) * g.qt_per_head + u.qt]);
+    FwdPlan chosen = plan_fwd(units, home_of, nullptr, cost_scale ? &usc : nullptr);
     if (speed == nullptr) return chosen;
     std::vector<int64_t> ucost;
     std::vector<int32_t> usteps;
-    for (const Unit& u : units) {
-      ucost.push_back(kItemCost + u.draft_cost + kStepCost * (u.k1 - u.k0));
+    for (size_t ui = 0; ui < units.size(); ++ui) {
+      const Unit& u = units[ui];
+      const int64_t c = kItemCost + u.draft_cost + kStepCost * (u.k1 - u.k0);
+      ucost.push_back(cost_scale ? std::llround(usc[ui] * double(c)) : c);
       usteps.push_back(u.k1 - u.k0);
     }
     std::vector<std::pair<int32_t, int32_t>> tails;
     const std::vector<int32_t> where =
         share_classes(ucost, home_of, class_speed(*speed), &usteps, kStepCost, kItemCost,
-                      double(kItemCost), &tails);
+                      double(kItemCost), &tails, cost_scale ? &usc : nullptr);
     std::vector<Unit> us = units;
-    for (const auto& [u, k] : tails) {  // unit u keeps its first k steps
+    for (const auto& [u, keep] : tails) {  // unit u keeps its first `keep` steps
       Unit tail = us[u];
-      tail.k0 = us[u].k0 + k;
+      tail.k0 = us[u].k0 + keep;
       tail.draft_cost = 0;
-      us[u].k1 = us[u].k0 + k;
+      us[u].k1 = us[u].k0 + keep;
       us.push_back(tail);
+      if (cost_scale) usc.push_back(usc[u]);
     }
-    FwdPlan sp = plan_fwd(us, where, speed);
+    FwdPlan sp = plan_fwd(us, where, speed, cost_scale ? &usc : nullptr);
     if (slowest(sp.load, *speed) < slowest(chosen.load, *speed)) chosen = std::move(sp);
     return chosen;
   };
@@ -809,7 +839,7 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
     return slots;
   };
   {
-    FwdPlan chosen = best_plan(xcd ? &spd[0] : nullptr);
+    FwdPlan chosen = best_plan(xcd ? &spd[0] : nullptr, 0);
     items = std::move(chosen.items);
     q = std::move(chosen.q);
     wg_load = std::move(chosen.load);
@@ -824,7 +854,7 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
   std::vector<int32_t> dq_split_rec;
   int32_t dq_slots = n_slots;
   if (dq_own) {
-    dq = best_plan(&spd[1]);
+    dq = best_plan(&spd[1], 1);
     dq_slots = assign_slots(dq.items, dq_split_rec);
   }
   // dK/dV items: two consecutive tiles per item (one if a lone tile is
@@ -1247,15 +1277,18 @@ skv_status skv_plan_lpt_split(const int64_t* extra, const int32_t* steps, int32_
 skv_status skv_schedule_build(const skv_problem* p, int32_t n_workgroups,
                               int32_t* image, int64_t capacity_words,
                               skv_schedule_info* info) {
-  return guarded([&] { build_schedule(p, n_workgroups, nullptr, image, capacity_words, info); });
+  return guarded([&] {
+    build_schedule(p, n_workgroups, nullptr, nullptr, image, capacity_words, info);
+  });
 }
 
 skv_status skv_schedule_build_xcd(const skv_problem* p, int32_t n_workgroups,
-                                  const float* xcd_speed, int32_t* image,
-                                  int64_t capacity_words, skv_schedule_info* info) {
+                                  const float* xcd_speed, const float* cost_scale,
+                                  int32_t* image, int64_t capacity_words,
+                                  skv_schedule_info* info) {
   return guarded([&] {
     require(xcd_speed != nullptr, "xcd_speed must not be NULL");
-    build_schedule(p, n_workgroups, xcd_speed, image, capacity_words, info);
+    build_schedule(p, n_workgroups, xcd_speed, cost_scale, image, capacity_words, info);
   });
 }
 

@@ -270,11 +270,17 @@ def cmd_balance(a):
     if r.get("kernels_xcd_plan"):
         plans.append(("plan for per-XCD speeds (skv_schedule_build_xcd), speeds measured "
                       "on the uniform plan's steps", r["kernels_xcd_plan"]))
+    if r.get("kernels_calibrated_plan"):
+        plans.append(("plan for per-XCD speeds and cost scales (skv_schedule_build_xcd), "
+                      "fitted to the stamps of the uniform and a first calibrated plan",
+                      r["kernels_calibrated_plan"]))
     for title, kernels in plans:
         out += ["", f"## {title}"]
-        if kernels is r.get("kernels_xcd_plan"):
+        if kernels is r.get("kernels_calibrated_plan"):
             for name, sp in zip(("forward", "dQ", "dK/dV"), r["xcd_speed"]):
                 out.append(f"speed {name:<6} " + " ".join(f"{x:.3f}" for x in sp))
+            for name, (lo, hi) in zip(("forward", "dQ"), r.get("cost_scale_range", [])):
+                out.append(f"cost scales {name:<7} {lo:.3f} .. {hi:.3f}")
         out.append("kernel      planned  realised  mean_us  span_us  on XCD (w+c)%8  CUs   "
                    "mean time per XCD (XCC_ID register), relative")
         for k, v in kernels.items():

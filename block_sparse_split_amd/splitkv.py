@@ -85,6 +85,7 @@ def lib():
     L.skv_schedule_build.argtypes = [ctypes.POINTER(SkvProblem), ctypes.c_int32, _i32p,
                                      ctypes.c_int64, ctypes.POINTER(SkvScheduleInfo)]
     L.skv_schedule_build_xcd.argtypes = [ctypes.POINTER(SkvProblem), ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_float),
                                          ctypes.POINTER(ctypes.c_float), _i32p, ctypes.c_int64,
                                          ctypes.POINTER(SkvScheduleInfo)]
     L.skv_attn_fwd_partial.argtypes = [ctypes.POINTER(SkvProblem),
@@ -218,6 +219,11 @@ class Problem:
     def n_local(self):
         return int(self.chunk_off[-1]) if len(self.chunk_off) else 0
 
+    @property
+    def qt_per_head(self):
+        """256-row query tiles per kv head."""
+        return -(-self.nq * (self.c.hq // self.c.hkv) // 256)
+
 
 def skv_schedule_build(problem: Problem, n_workgroups: int = 0):
     info = SkvScheduleInfo()
@@ -232,20 +238,30 @@ def skv_schedule_build(problem: Problem, n_workgroups: int = 0):
     return image, info
 
 
-def skv_schedule_build_xcd(problem: Problem, n_workgroups: int, xcd_speed):
+def skv_schedule_build_xcd(problem: Problem, n_workgroups: int, xcd_speed, cost_scale=None):
     """Schedule planned for per-XCD speeds: xcd_speed is [3, 8] (forward,
-    dQ, dK/dV kernels x XCD), relative work per unit time."""
+    dQ, dK/dV kernels x XCD), relative work per unit time; cost_scale, if
+    given, is [2, hkv, qt_per_head] (forward, dQ): measured multipliers of
+    the cost of each kv head's query tiles."""
     sp = np.ascontiguousarray(np.asarray(xcd_speed, np.float32).reshape(-1))
     if sp.size != 3 * XCDS:
         raise ValueError(f"xcd_speed must hold 3 x {XCDS} values, got {sp.size}")
     fp = sp.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    cp = None
+    if cost_scale is not None:
+        cs = np.ascontiguousarray(np.asarray(cost_scale, np.float32).reshape(-1))
+        want = 2 * problem.c.hkv * problem.qt_per_head
+        if cs.size != want:
+            raise ValueError(f"cost_scale must hold 2 x hkv x qt_per_head = {want} values, "
+                             f"got {cs.size}")
+        cp = cs.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
     info = SkvScheduleInfo()
     L = lib()
     _check("skv_schedule_build_xcd", L.skv_schedule_build_xcd(
-        ctypes.byref(problem.c), n_workgroups, fp, None, 0, ctypes.byref(info)))
+        ctypes.byref(problem.c), n_workgroups, fp, cp, None, 0, ctypes.byref(info)))
     image = np.zeros(info.words, np.int32)
     _check("skv_schedule_build_xcd", L.skv_schedule_build_xcd(
-        ctypes.byref(problem.c), info.n_workgroups, fp, image.ctypes.data_as(_i32p),
+        ctypes.byref(problem.c), info.n_workgroups, fp, cp, image.ctypes.data_as(_i32p),
         len(image), ctypes.byref(info)))
     return image, info
 
@@ -402,13 +418,17 @@ class Shard:
     every layer).  Allocation happens here, never inside the calls."""
 
     def __init__(self, problem: Problem, device="cuda", n_workgroups: int = 0,
-                 xcd_speed=None):
+                 xcd_speed=None, cost_scale=None):
         torch = _torch()
         self.problem = problem
+        self.cost_scale = cost_scale
         if xcd_speed is None:
+            if cost_scale is not None:
+                raise ValueError("cost_scale needs xcd_speed")
             self.image, self.info = skv_schedule_build(problem, n_workgroups)
         else:
-            self.image, self.info = skv_schedule_build_xcd(problem, n_workgroups, xcd_speed)
+            self.image, self.info = skv_schedule_build_xcd(problem, n_workgroups, xcd_speed,
+                                                           cost_scale)
         self.schedule = torch.from_numpy(self.image).to(device)
         nbytes = max(self.info.fwd_workspace_bytes, self.info.bwd_workspace_bytes, 256)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -474,6 +494,102 @@ def xcd_speeds_from_stamps(image, runs):
             v = work[k] / time[k]
             speed[k] = v / v.mean()
     return speed
+
+
+def _plan_sections(image):
+    """(items, queue offsets, queue) of the forward and dQ plans."""
+    from .csrc_layout import H, I_WORDS
+    img = np.asarray(image)
+    h = {k: int(img[v]) for k, v in H.items()}
+    n = h["NWG"]
+    out = []
+    for oi, qo, qq in ((h["OFF_ITEMS"], h["OFF_QOFF"], h["OFF_QUEUE"]),
+                       (h["OFF_DQ_ITEMS"], h["OFF_DQ_QOFF"], h["OFF_DQ_QUEUE"])):
+        off = img[qo: qo + n + 1]
+        q = img[qq: qq + off[-1]]
+        n_items = int(q.max()) + 1 if len(q) else 0
+        out.append((img[oi: oi + n_items * I_WORDS].reshape(-1, I_WORDS), off, q))
+    return h, out
+
+
+def calibrate_from_stamps(datasets, groups_per_head: int = 8, ridge: float = 0.05,
+                          iters: int = 4):
+    """Per-XCD speeds and measured cost scales from per-workgroup stamps.
+
+    datasets: list of (image, runs, cost_scale) -- a schedule image, the
+    stamps of launches with it (as for xcd_speeds_from_stamps) and the cost
+    scales it was built with (None for none).  Returns (speed [3, 8],
+    cost_scale [2, hkv, qt_per_head]) for skv_schedule_build_xcd.
+
+    Model, per forward or dQ launch: queue v on XCD x takes
+    sum over its items i of tau * s_g(i) * c_i / speed_x, with c_i the
+    item's cost before any scale and g(i) its (kv head, group of
+    consecutive query tiles).  Speeds (with the scales fixed) and scales
+    (with the speeds fixed, least squares with a ridge pull towards 1)
+    are fitted in turn, the scales normalised to a cost-weighted mean of 1.
+    Where the stamps cannot tell a kv head's overall cost from the speed of
+    the XCDs that ran it (each head always ran on the same XCDs), the
+    ridge leaves that factor with the speeds.  dK/dV gets speeds only
+    (xcd_speeds_from_stamps)."""
+    from .csrc_layout import I
+    speed = np.ones((3, XCDS))
+    first = None
+    eqs = {0: [], 1: []}
+    for image, runs, used in datasets:
+        h, plans = _plan_sections(image)
+        hkv, qtph, n = h["HKV"], h["QT_PER_HEAD"], h["NWG"]
+        if first is None:
+            first = (hkv, qtph)
+        elif first != (hkv, qtph):
+            raise ValueError("datasets of different problems")
+        per = -(-qtph // groups_per_head)
+        ng = -(-qtph // per)
+        for k, (items, off, q) in enumerate(plans):
+            head, qt = items[:, I["HEAD"]], items[:, I["QT"]]
+            cost = items[:, I["COST"]].astype(np.float64)
+            if used is not None:
+                cost = cost / np.asarray(used, np.float64).reshape(2, hkv, qtph)[k, head, qt]
+            grp = head * ng + qt // per
+            A = np.zeros((n, hkv * ng))
+            for v in range(n):
+                ii = q[off[v]: off[v + 1]]
+                np.add.at(A[v], grp[ii], cost[ii])
+            for r in runs:
+                r = np.asarray(r).reshape(3, n, 4)
+                dur = (r[k, :, 1] - r[k, :, 0]).astype(np.float64)
+                ok = (r[k, :, 1] > 0) & (dur > 0)
+                x = (r[k, :, 2] & 0xF).astype(np.int64) % XCDS
+                eqs[k].append((A[ok], dur[ok], x[ok]))
+    hkv, qtph = first
+    per = -(-qtph // groups_per_head)
+    ng = -(-qtph // per)
+    scale = np.ones((2, hkv, qtph))
+    for k in (0, 1):
+        if not eqs[k]:
+            continue
+        sig = np.ones(hkv * ng)
+        wsum = sum(A.sum(0) for A, _, _ in eqs[k])
+        for _ in range(iters):
+            work, time = np.zeros(XCDS), np.zeros(XCDS)
+            for A, dur, x in eqs[k]:
+                np.add.at(work, x, A @ sig)
+                np.add.at(time, x, dur)
+            if np.all(time > 0) and np.all(work > 0):
+                v = work / time
+                speed[k] = v / v.mean()
+            M = np.vstack([A for A, _, _ in eqs[k]])
+            y = np.concatenate([dur * speed[k][x] for _, dur, x in eqs[k]])
+            tau = y.sum() / M.sum()
+            MtM = M.T @ M
+            lam = ridge * float(np.mean(np.diag(MtM))) + 1e-30
+            beta = np.linalg.solve(MtM + lam * np.eye(len(sig)), M.T @ y + lam * tau)
+            sig = np.clip(beta / tau, 0.5, 2.0)
+            sig /= (sig * wsum).sum() / wsum.sum()
+        scale[k] = np.repeat(sig.reshape(hkv, ng), per, axis=1)[:, :qtph]
+    # dK/dV: speeds from its queues' loads (never scaled)
+    kv_runs = [r for image, runs, _ in datasets[-1:] for r in runs]
+    speed[2] = xcd_speeds_from_stamps(datasets[-1][0], kv_runs)[2]
+    return speed, scale
 
 
 def measure_xcd_speed(shard, step, steps: int = 4):

@@ -253,11 +253,22 @@ skv_status skv_schedule_build(const skv_problem* p, int32_t n_workgroups,
  * live in the last 256 bytes of each workspace (counted in the workspace
  * sizes); the device calls zero them before each launch.  info->xcd_mode
  * is set.  Requires n_workgroups divisible by 8.
+ * cost_scale (NULL: none) corrects the cost model with measured costs:
+ * cost_scale[(k * hkv + h) * qt + t], k = 0 (forward) or 1 (dQ), qt = the
+ * query tiles per kv head (info->n_qtiles / hkv), multiplies the cost of
+ * every unit of kv head h and 256-row query tile t in kernel k's plan (its
+ * fixed part and each step alike; item costs, loads and the cost totals in
+ * info are then the scaled, rounded ones).  Scales fitted to the clock
+ * stamps of an earlier plan let the plan follow costs the model does not
+ * see, such as a kv head whose keys and values the memory system serves
+ * more slowly.
  * Errors: as skv_schedule_build; SKV_ERR_INVALID_ARG for a NULL, zero,
- * negative or non-finite speed or n_workgroups not divisible by 8. */
+ * negative or non-finite speed or cost scale, or n_workgroups not divisible
+ * by 8. */
 skv_status skv_schedule_build_xcd(const skv_problem* p, int32_t n_workgroups,
-                                  const float* xcd_speed, int32_t* image,
-                                  int64_t capacity_words, skv_schedule_info* info);
+                                  const float* xcd_speed, const float* cost_scale,
+                                  int32_t* image, int64_t capacity_words,
+                                  skv_schedule_info* info);
 
 /* ------------------------------------------------------------------------
  * Device calls.

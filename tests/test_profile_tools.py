@@ -112,16 +112,21 @@ def test_bench_tables(tmp_path):
     _json_line(src, {"workload": "w", "clock": "c", "workgroups": 256, "steps": 2,
                      "kernels": {"bwd_dq": k},
                      "kernels_xcd_plan": {"bwd_dq": dict(k, realized_imbalance_median=0.02)},
-                     "xcd_speed": [[1.0] * 8, [1.05] + [1.0] * 7, [0.9] * 8]})
+                     "kernels_calibrated_plan": {"bwd_dq": dict(k,
+                                                                realized_imbalance_median=0.01)},
+                     "xcd_speed": [[1.0] * 8, [1.05] + [1.0] * 7, [0.9] * 8],
+                     "cost_scale_range": [[0.95, 1.02], [0.9, 1.1]]})
     out = tmp_path / "b.txt"
     rs.main(["balance", str(src), "--command", "cmd", "--out", str(out)])
     lines = out.read_text().splitlines()
-    uni, xcd = [l.split() for l in lines if l.startswith("bwd_dq")]
+    uni, xcd, cal = [l.split() for l in lines if l.startswith("bwd_dq")]
     assert uni[1:5] == ["0.50%", "4.00%", "100.0", "110.0"]
     assert uni[5:7] == ["100.0%", "(c=3)"] and uni[7] == "256"
     assert uni[8:10] == ["+1.0%", "-1.0%"]
-    assert xcd[1:3] == ["0.50%", "2.00%"]
+    assert xcd[1:3] == ["0.50%", "2.00%"] and cal[1:3] == ["0.50%", "1.00%"]
     assert [l.split()[2] for l in lines if l.startswith("speed")] == ["1.000", "1.050", "0.900"]
+    assert [l.split()[3:] for l in lines if l.startswith("cost scales")] == [
+        ["0.950", "..", "1.020"], ["0.900", "..", "1.100"]]
     # a record without the per-XCD plan prints the uniform table only
     _json_line(src, {"workload": "w", "clock": "c", "workgroups": 256, "steps": 2,
                      "kernels": {"bwd_dq": k}})

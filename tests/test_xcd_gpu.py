@@ -1,7 +1,8 @@
-"""GPU checks of schedules planned for per-XCD speeds
-(skv_schedule_build_xcd): workgroups claim queues by the XCD they run on,
-every queue runs exactly once, and the forward, backward and
-allocation-free forward match the oracle as with the uniform plan."""
+"""GPU checks of schedules planned for per-XCD speeds and measured cost
+scales (skv_schedule_build_xcd): workgroups claim queues by the XCD they
+run on, every queue runs exactly once, and the forward, backward (through
+dQ's own plan) and allocation-free forward match the oracle as with the
+uniform plan."""
 import numpy as np
 import pytest
 import torch
@@ -44,17 +45,21 @@ def _run(w, t, sh, noalloc=False):
     return O, LSE, dQ, dK, dV, dKd, dVd
 
 
-@pytest.mark.parametrize("seed,n_wg", [(1, 256), (2, 64), (3, 8)])
-def test_xcd_plan_forward_backward_parity(seed, n_wg):
+@pytest.mark.parametrize("seed,n_wg,scaled", [(1, 256, False), (2, 64, True), (3, 8, True)])
+def test_xcd_plan_forward_backward_parity(seed, n_wg, scaled):
     """Forward (and its allocation-free form) and backward through an XCD
-    plan against the oracle; every queue of the three kernels is stamped
-    exactly once (each workgroup stamps the queue it claimed), so none was
-    skipped."""
+    plan (with cost scales: other cuts and queues) against the oracle;
+    every queue of the three kernels is stamped exactly once (each
+    workgroup stamps the queue it claimed), so none was skipped."""
     w, g, t = _small(seed)
     prob = shards.whole_context_problem(w, g)
-    sh = skv.Shard(prob, n_workgroups=n_wg, xcd_speed=_speeds(seed))
+    scale = None
+    if scaled:
+        rng = np.random.default_rng(seed + 100)
+        scale = rng.uniform(0.7, 1.4, (2, w.hkv, prob.qt_per_head))
+    sh = skv.Shard(prob, n_workgroups=n_wg, xcd_speed=_speeds(seed), cost_scale=scale)
     assert sh.info.xcd_mode == 1
-    announce("xcd plan parity", seed, n_wg)
+    announce("xcd plan parity", seed, n_wg, scaled)
     clk = torch.zeros(3 * n_wg * 4, dtype=torch.int64, device="cuda")
     skv.skv_timing_wg_clock(clk)
     try:

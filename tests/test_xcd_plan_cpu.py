@@ -205,7 +205,7 @@ def test_xcd_plan_arguments():
     # the C entry point refuses a NULL speed table
     info = skv.SkvScheduleInfo()
     import ctypes
-    st = skv.lib().skv_schedule_build_xcd(ctypes.byref(prob.c), 8, None, None, 0,
+    st = skv.lib().skv_schedule_build_xcd(ctypes.byref(prob.c), 8, None, None, None, 0,
                                           ctypes.byref(info))
     assert skv.STATUS_NAMES[st] == "SKV_ERR_INVALID_ARG"
     # without speeds the image keeps one queue set, shared by the forward
@@ -246,3 +246,136 @@ def test_speeds_from_stamps_invert_a_known_speed():
         runs.append(r)
     got = skv.xcd_speeds_from_stamps(image, runs)
     np.testing.assert_allclose(got, true / true.mean(1, keepdims=True), rtol=1e-3)
+
+
+def test_cost_scales_scale_the_plan():
+    """Cost scales of 1 give the plan without them, word for word; other
+    scales multiply each unit's cost (item costs are the scaled, rounded
+    base costs of their (kv head, query tile)), every plan still covers the
+    work once, and scales are refused without speeds, with bad values or
+    with the wrong size."""
+    name, seed, shard_of, n_wg, over = CASES[1]
+    w, g, prob = _case(name, seed, shard_of, **over)
+    sp = _speeds(seed, 0.05)
+    qtph = prob.qt_per_head
+    base, binfo = skv.skv_schedule_build_xcd(prob, n_wg, sp)
+    ones, oinfo = skv.skv_schedule_build_xcd(prob, n_wg, sp, np.ones((2, w.hkv, qtph)))
+    assert np.array_equal(base, ones) and oinfo.item_cost_total == binfo.item_cost_total
+    rng = np.random.default_rng(5)
+    scale = rng.uniform(0.8, 1.25, (2, w.hkv, qtph)).astype(np.float32)
+    image, info = skv.skv_schedule_build_xcd(prob, n_wg, sp, scale)
+    h, tiles, items_f, kv, fq_f, kq = _decode(image)
+    items_d, fq_d, _ = _decode_dq(image, info)
+    G = w.hq // w.hkv
+    for k, items, fq in ((0, items_f, fq_f), (1, items_d, fq_d)):
+        seen = np.zeros((w.hkv, qtph, len(tiles)), np.int32)
+        for it in items:
+            hd, qt, t0, t1 = it[I["HEAD"]], it[I["QT"]], it[I["T0"]], it[I["T1"]]
+            seen[hd, qt, t0:t1] += 1
+            b0 = qt * (QTILE // G) // BLOCK
+            b1 = min(w.nb, -(-((qt + 1) * (QTILE // G)) // BLOCK))
+            want = ITEM_COST + STEP_COST * (t1 - t0)
+            if it[I["FLAGS"]] & 1:
+                want += STEP_COST * -(-((b1 - b0) * BLOCK) // 64)
+            assert abs(it[I["COST"]] - float(scale[k, hd, qt]) * want) <= 0.5 + 1e-6
+        assert seen.max() <= 1
+        assert sorted(i for q in fq for i in q) == list(range(len(items)))
+    loads = skv.queue_loads(image)
+    assert info.item_cost_total == loads[0].sum() and info.dq_cost_total == loads[1].sum()
+    with pytest.raises(skv.SplitKVError, match="finite and > 0"):
+        bad = scale.copy()
+        bad[1, 0, 3] = np.nan
+        skv.skv_schedule_build_xcd(prob, n_wg, sp, bad)
+    with pytest.raises(ValueError, match="cost_scale must hold"):
+        skv.skv_schedule_build_xcd(prob, n_wg, sp, scale[:, :, :-1])
+    import ctypes
+    info = skv.SkvScheduleInfo()
+    cs = np.ascontiguousarray(scale.reshape(-1))
+    st = skv.lib().skv_schedule_build(ctypes.byref(prob.c), n_wg, None, 0, ctypes.byref(info))
+    assert skv.STATUS_NAMES[st] == "SKV_OK"
+    # the uniform builder takes no scales; the per-XCD builder needs speeds
+    st = skv.lib().skv_schedule_build_xcd(ctypes.byref(prob.c), n_wg, None,
+                                          cs.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                          None, 0, ctypes.byref(info))
+    assert skv.STATUS_NAMES[st] == "SKV_ERR_INVALID_ARG"
+
+
+def test_calibration_recovers_known_costs():
+    """Stamps made from known per-XCD speeds and known per-(kv head, query
+    tile group) cost scales, over two plans (the second built with scales,
+    whose item costs the fit divides back out), give those speeds and
+    scales back; a plan built with them balances the true queue times
+    better than the plan without them."""
+    w, g, prob = _case("varlen8_fwdbwd", 3, None, len_median=2048, len_min=512, len_max=8192)
+    qtph, hkv = prob.qt_per_head, w.hkv
+    per = -(-qtph // 8)
+    ng = -(-qtph // per)
+    rng = np.random.default_rng(11)
+    true_sig = rng.uniform(0.9, 1.12, (2, hkv, ng))
+    # each head's scales have a cost-weighted mean near 1 only after the
+    # fit's normalisation, so compare shapes: normalise per head below
+    true_scale = np.repeat(true_sig, per, axis=2)[:, :, :qtph]
+    true_speed = np.ones((3, 8)) + 0.04 * np.sin(np.arange(24)).reshape(3, 8)
+
+    def stamps(image, used):
+        _, plans = skv._plan_sections(image)
+        loads_kv = skv.queue_loads(image)[2]
+        n = len(plans[0][1]) - 1
+        runs = []
+        for c in (0, 5):
+            r = np.zeros((3, n, 4), np.int64)
+            for k, (items, off, q) in enumerate(plans):
+                cost = items[:, I["COST"]].astype(float)
+                hd, qt = items[:, I["HEAD"]], items[:, I["QT"]]
+                if used is not None:
+                    cost = cost / used[k, hd, qt]
+                t = cost * true_scale[k, hd, qt]
+                for v in range(n):
+                    x = (v + c) % 8
+                    r[k, v, 0] = 100
+                    r[k, v, 1] = 100 + int(round(t[q[off[v]:off[v + 1]]].sum() / true_speed[k, x]))
+                    r[k, v, 2] = x
+            for v in range(n):
+                x = (v + c) % 8
+                r[2, v, :3] = (100, 100 + int(round(loads_kv[v] / true_speed[2, x])), x)
+            runs.append(r)
+        return runs
+
+    base, _ = skv.skv_schedule_build(prob, 64)
+    sp1, sc1 = skv.calibrate_from_stamps([(base, stamps(base, None), None)], ridge=1e-4)
+    second, _ = skv.skv_schedule_build_xcd(prob, 64, sp1, sc1)
+    data = [(base, stamps(base, None), None), (second, stamps(second, sc1), sc1)]
+    sp, sc = skv.calibrate_from_stamps(data, ridge=1e-4)
+    # dK/dV: the speeds themselves
+    np.testing.assert_allclose(sp[2], true_speed[2] / true_speed[2].mean(), rtol=0.01)
+    for k in (0, 1):
+        # the scales' pattern (here each head ran on four XCDs, so heads and
+        # XCDs are told apart) ...
+        np.testing.assert_allclose(sc[k] / sc[k].mean(), true_scale[k] / true_scale[k].mean(),
+                                   rtol=0.01)
+        np.testing.assert_allclose(sp[k], true_speed[k] / true_speed[k].mean(), rtol=0.01)
+        # ... and, with the speeds, every stamped queue time of both plans
+        # up to one overall factor
+        for image, runs, used in data:
+            _, plans = skv._plan_sections(image)
+            items, off, q = plans[k]
+            cost = items[:, I["COST"]].astype(float)
+            hd, qt = items[:, I["HEAD"]], items[:, I["QT"]]
+            if used is not None:
+                cost = cost / used[k, hd, qt]
+            c_fit = cost * sc[k, hd, qt]
+            for r in runs:
+                x = r[k, :, 2] & 15
+                pred = np.array([c_fit[q[off[v]:off[v + 1]]].sum() for v in range(len(x))])
+                pred = pred / sp[k][x]
+                got_t = (r[k, :, 1] - r[k, :, 0]).astype(float)
+                ratio = got_t / pred
+                assert ratio.max() / ratio.min() - 1 < 0.03, (k, ratio.min(), ratio.max())
+    # the calibrated plan balances the true times at least as well
+    def true_max(image, used):
+        runs = stamps(image, used)[0]
+        d = (runs[:2, :, 1] - runs[:2, :, 0]).astype(float)
+        return d.max(1) / d.mean(1) - 1
+    cal, _ = skv.skv_schedule_build_xcd(prob, 64, sp, sc)
+    plain, _ = skv.skv_schedule_build_xcd(prob, 64, sp)
+    assert np.all(true_max(cal, sc) <= true_max(plain, None) + 0.002)
