@@ -33,6 +33,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
+# unstamped steps run back to back before stamping the steps a plan is
+# calibrated on (about 0.1 s of sustained load at 32K)
+SUSTAIN_STEPS = 40
 
 # System-level figures the Split-KV sources report for the whole method (the
 # arXiv abstract of "Split-KV: Efficient Context Parallelism for Training
@@ -646,7 +649,7 @@ def run_workload(args, workload):
         # plan, a plan made for them, then a refit over the stamps of both
         # plans and the plan the step below uses (all outside the timed
         # region)
-        runs = stamp_runs(step, n_wg, 6, torch)
+        runs = stamp_runs(step, n_wg, 6, torch, SUSTAIN_STEPS)
         uni_realized = {k: v["realized_imbalance_median"] for k, v in
                         realized_balance(step, sh.info, 0, torch, args.fwd_only,
                                          runs=runs).items()}
@@ -658,12 +661,13 @@ def run_workload(args, workload):
                 step()
             torch.cuda.synchronize()
             if rnd == 0:
-                data.append((sh.image, stamp_runs(step, n_wg, 6, torch), scale))
+                data.append((sh.image, stamp_runs(step, n_wg, 6, torch, SUSTAIN_STEPS), scale))
         xcd = {"speed": np.round(speed, 4).tolist(),
                "cost_scale_range": [[round(float(x.min()), 4), round(float(x.max()), 4)]
                                     for x in scale],
-               "calibration": "two rounds of 6 stamped steps (uniform plan, then the "
-                              "first calibrated plan)",
+               "calibration": f"two rounds of 6 stamped steps after {SUSTAIN_STEPS} unstamped "
+                              "ones, back to back (uniform plan, then the first calibrated "
+                              "plan)",
                "uniform_plan_realized": uni_realized}
     skv.skv_timing_collect()  # discard anything recorded before
     skv.skv_timing_enable(True)
@@ -922,22 +926,27 @@ def balance_stats(runs, planned, names=("fwd_bf16", "bwd_dq", "bwd_dkdv")):
     return out
 
 
-def stamp_runs(step, n, steps, torch):
+def stamp_runs(step, n, steps, torch, sustain=0):
     """Per-workgroup stamps of `steps` steps (outside any timed region): a
-    list of [3, n, 4] arrays (forward, dQ, dK/dV)."""
+    list of [3, n, 4] arrays (forward, dQ, dK/dV).  The steps run back to
+    back like the timed ones (each launch writes its own buffer; one
+    synchronisation at the end), after `sustain` unstamped steps that bring
+    the GPU to the clocks and temperatures of a sustained run: the per-XCD
+    speeds differ between a GPU that idles between steps and one that does
+    not."""
     from block_sparse_split_amd import splitkv as skv
-    clk = torch.zeros(3 * n * 4, dtype=torch.int64, device="cuda")
-    runs = []
-    skv.skv_timing_wg_clock(clk)
+    clk = torch.zeros((steps, 3 * n * 4), dtype=torch.int64, device="cuda")
+    for _ in range(sustain):
+        step()
     try:
-        for _ in range(steps):
-            clk.zero_()
+        for i in range(steps):
+            skv.skv_timing_wg_clock(clk[i])
             step()
-            torch.cuda.synchronize()
-            runs.append(clk.view(3, n, 4).cpu().numpy().copy())
     finally:
         skv.skv_timing_wg_clock(None)
-    return runs
+    torch.cuda.synchronize()
+    host = clk.cpu().numpy()
+    return [host[i].reshape(3, n, 4).copy() for i in range(steps)]
 
 
 def planned_imbalance(info):
@@ -996,7 +1005,7 @@ def wg_balance(args):
     for _ in range(max(1, args.warmup)):
         step()
     prob = shards.whole_context_problem(w, g)
-    runs = stamp_runs(step, n, args.steps, torch)
+    runs = stamp_runs(step, n, args.steps, torch, SUSTAIN_STEPS)
     plans = {"uniform": realized_balance(step, sh.info, 0, torch, runs=runs)}
     data = [(sh.image, runs, None)]
     speed, scale = calibrate(data, False)
@@ -1006,15 +1015,12 @@ def wg_balance(args):
         # uniform plan's stamps and, in a second round, to those of the first
         # calibrated plan as well
         sh = skv.Shard(prob, n_workgroups=n, xcd_speed=speed)
-        for _ in range(max(1, args.warmup)):
-            step()
-        plans["xcd"] = realized_balance(step, sh.info, args.steps, torch)
+        plans["xcd"] = realized_balance(step, sh.info, 0, torch, runs=stamp_runs(
+            step, n, args.steps, torch, SUSTAIN_STEPS))
         for rnd in range(2):
             speed, scale = calibrate(data, False)
             sh = skv.Shard(prob, n_workgroups=n, xcd_speed=speed, cost_scale=scale)
-            for _ in range(max(1, args.warmup)):
-                step()
-            runs = stamp_runs(step, n, args.steps, torch)
+            runs = stamp_runs(step, n, args.steps, torch, SUSTAIN_STEPS)
             data.append((sh.image, runs, scale))
         plans["calibrated"] = realized_balance(step, sh.info, 0, torch, runs=runs)
     for plan, out in plans.items():

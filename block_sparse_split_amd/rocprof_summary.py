@@ -21,7 +21,7 @@ Usage:
       --command "..." [--trace TRACE_CSV --skip-first N --bench-json OUT] [--out FILE]
   python -m block_sparse_split_amd.rocprof_summary traffic KERNEL \\
       --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV \\
-      --copy-bytes N --workload NAME --command "..." [--out FILE]
+      --copy-bytes N --workload NAME --command "..." [--skip-first N] [--out FILE]
   python -m block_sparse_split_amd.rocprof_summary counters CSV \\
       --workload NAME --command "..." [--skip-first N] [--out FILE]
   python -m block_sparse_split_amd.rocprof_summary l2 CSV \\
@@ -68,17 +68,18 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def counter_per_dispatch(path, counter, match):
+def counter_per_dispatch(path, counter, match, skip_first=0):
     """Mean over dispatches of `counter` (summed over its per-dimension rows)
-    for kernels whose name satisfies `match`."""
+    for kernels whose name satisfies `match`, without the first
+    `skip_first` dispatches (in dispatch order)."""
     per_dispatch = defaultdict(float)
     for row in csv.DictReader(open(path)):
         if row["Counter_Name"] != counter or not match(row["Kernel_Name"]):
             continue
         per_dispatch[row["Dispatch_Id"]] += float(row["Counter_Value"])
-    if not per_dispatch:
+    vals = [per_dispatch[d] for d in sorted(per_dispatch, key=int)][skip_first:]
+    if not vals:
         raise SystemExit(f"{path}: no {counter} rows for the requested kernel")
-    vals = list(per_dispatch.values())
     return sum(vals) / len(vals), len(vals)
 
 
@@ -121,8 +122,8 @@ def cmd_kernels(a):
 def cmd_traffic(a):
     is_k = lambda n: short_name(n) == a.kernel
     is_copy = lambda n: "neg_kernel" in n
-    f_kib, nf = counter_per_dispatch(a.fetch, "FETCH_SIZE", is_k)
-    w_kib, nw = counter_per_dispatch(a.write, "WRITE_SIZE", is_k)
+    f_kib, nf = counter_per_dispatch(a.fetch, "FETCH_SIZE", is_k, a.skip_first)
+    w_kib, nw = counter_per_dispatch(a.write, "WRITE_SIZE", is_k, a.skip_first)
     cf_kib, _ = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", is_copy)
     cw_kib, _ = counter_per_dispatch(a.copy_write, "WRITE_SIZE", is_copy)
     f_scale = a.copy_bytes / (cf_kib * 1024.0)
@@ -133,6 +134,7 @@ def cmd_traffic(a):
         f"kernel: {a.kernel}",
         f"workload: {a.workload}",
         f"kernel_source_sha256: {kernel_source_hash()}",
+        f"dispatches skipped as warm-up (each run): {a.skip_first}",
         f"dispatches_fetch: {nf}",
         f"dispatches_write: {nw}",
         f"fetch_kib_per_dispatch_raw: {f_kib:.1f}",
@@ -364,6 +366,7 @@ def main(argv=None):
     for opt in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--workload", "--command"):
         t.add_argument(opt, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--skip-first", type=int, default=0)
     t.add_argument("--out")
     c = sub.add_parser("counters")
     c.add_argument("csv")
