@@ -47,7 +47,7 @@ SHORT = {
     "merge_split_kernel": "merge_split", "merge_kernel": "merge",
     "bwd_pre_kernel": "bwd_pre", "bwd_dq_kernel": "bwd_dq",
     "dq_reduce_kernel": "dq_reduce", "bwd_dkdv_kernel": "bwd_dkdv",
-    "dq_finalize_kernel": "dq_finalize",
+    "dq_finalize_kernel": "dq_finalize", "xcd_reset_kernel": "xcd_reset",
 }
 
 
