@@ -558,6 +558,8 @@ def calibrate_from_stamps(datasets, groups_per_head: int = 8, ridge: float = 0.0
                 r = np.asarray(r).reshape(3, n, 4)
                 dur = (r[k, :, 1] - r[k, :, 0]).astype(np.float64)
                 ok = (r[k, :, 1] > 0) & (dur > 0)
+                if not ok.any():   # a kernel that did not run (forward-only steps)
+                    continue
                 x = (r[k, :, 2] & 0xF).astype(np.int64) % XCDS
                 eqs[k].append((A[ok], dur[ok], x[ok]))
     hkv, qtph = first

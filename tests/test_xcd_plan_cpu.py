@@ -379,3 +379,24 @@ def test_calibration_recovers_known_costs():
     cal, _ = skv.skv_schedule_build_xcd(prob, 64, sp, sc)
     plain, _ = skv.skv_schedule_build_xcd(prob, 64, sp)
     assert np.all(true_max(cal, sc) <= true_max(plain, None) + 0.002)
+
+
+def test_calibration_without_backward_stamps():
+    """Stamps of forward-only steps (the dQ and dK/dV regions stay zero)
+    calibrate the forward and leave dQ and dK/dV at speed 1 and scale 1,
+    with no NaN."""
+    w, g, prob = _case("ctx32k_q2k", 2, None, ctx=4096, anchor_lo=512, anchor_hi=4096,
+                       blocks_per_seq=16)
+    image, _ = skv.skv_schedule_build(prob, 64)
+    loads = skv.queue_loads(image)
+    true = 1.0 + 0.05 * np.cos(np.arange(8))
+    r = np.zeros((3, 64, 4), np.int64)
+    for v in range(64):
+        r[0, v] = (10, 10 + int(round(1e3 * loads[0, v] / true[v % 8])), v % 8, 0)
+    import warnings
+    with warnings.catch_warnings():
+        warnings.simplefilter("error")
+        sp, sc = skv.calibrate_from_stamps([(image, [r, r], None)])
+    assert np.all(np.isfinite(sp)) and np.all(np.isfinite(sc))
+    np.testing.assert_allclose(sp[0], true / true.mean(), rtol=0.01)
+    assert np.all(sp[1:] == 1.0) and np.all(sc[1] == 1.0)
