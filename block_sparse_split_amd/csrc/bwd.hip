@@ -39,15 +39,19 @@ namespace {
 // accumulators start from it, so they end as dP - D), LSE * log2(e) (+inf
 // for a row that sees no key) and the row's visible context interval
 // [lo, anchor) of its anchor block.  It also zeroes the per-XCD queue
-// counters of the dQ and dK/dV kernels that follow it on the stream.
+// counters of the dQ and dK/dV kernels that follow it on the stream, and
+// the dK/dV kernel's claim counters (one per queue).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const int32_t* sched, const __bf16* O,
                                                       const __bf16* dO, const float* LSE,
                                                       float* nDrm, float* L2rm, int32_t* LOrm,
                                                       int32_t* HIrm, int64_t rows, int hq, int G,
-                                                      uint32_t* xcd_count) {
+                                                      uint32_t* xcd_count, uint32_t* kv_front,
+                                                      int n_wg) {
   if (xcd_count != nullptr && blockIdx.x == 0 && threadIdx.x < 2 * kXcds)
     xcd_count[threadIdx.x] = 0u;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n_wg; i += 256) kv_front[i] = 0u;
   constexpr int TPR = D / 8;
   constexpr int RPB = 256 / TPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
@@ -361,6 +365,78 @@ struct KvCfg {
   static constexpr int kPrefetchTr = 4;
 };
 
+// Work claiming of the dK/dV kernel, called by every thread of the
+// workgroup (one barrier).  A workgroup first runs its own queue v in order:
+// front[v] (zero at launch) counts its claimed positions, and lane 0 of
+// wave 0 claims the next one a call ahead (`pending`) so that the atomic's
+// latency overlaps an item.  Once its queue is exhausted (`own` cleared),
+// wave 0 reads every queue's counter and takes the next position of the
+// queue with the most planned work left (the image's suffix costs), until
+// no queue has any: idle workgroups take over the items of slow ones, so
+// speed differences the static plan did not foresee even out.  Every item
+// is claimed exactly once (atomic counters), and its outputs do not depend
+// on the workgroup that runs it.  A failed claim finds its queue
+// exhausted for good, so the search ends within n_wg + n_items tries.
+// Returns the item, or -1 when none is left.
+__device__ __forceinline__ int kv_claim(sched_t S, uint32_t* front, int v, int& own,
+                                        int& pending, int call) {
+  __shared__ int slot[2];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (wave == 0) {
+    const sched_t qoff = S + S[H_OFF_KVQOFF];
+    const sched_t queue = S + S[H_OFF_KVQUEUE];
+    const sched_t suf = S + S[H_OFF_KVSUF];
+    int item = -1;
+    if (own) {
+      const int b = qoff[v], len = qoff[v + 1] - b;
+      const int i = __shfl(pending, 0);
+      if (i < len) {
+        item = queue[b + i];
+        if (lane == 0) pending = (int)atomicAdd(&front[v], 1u);
+      } else {
+        own = 0;
+      }
+    }
+    if (!own) {
+      const int n = S[H_NWG], cap = n + S[H_NKV];
+      for (int tries = 0; item < 0 && tries <= cap; ++tries) {
+        int best = 0, bu = -1;
+        for (int u = lane; u < n; u += 64) {
+          const int b = qoff[u], len = qoff[u + 1] - b;
+          const int f =
+              (int)__hip_atomic_load(&front[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (f < len && suf[b + f] > best) {
+            best = suf[b + f];
+            bu = u;
+          }
+        }
+        // the most work left over the wave (ties: the lower queue)
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+          const int ob = __shfl_xor(best, o), ou = __shfl_xor(bu, o);
+          if (ob > best || (ob == best && ou >= 0 && (bu < 0 || ou < bu))) {
+            best = ob;
+            bu = ou;
+          }
+        }
+        const int U = __builtin_amdgcn_readfirstlane(bu);
+        if (__builtin_amdgcn_readfirstlane(best) <= 0 || U < 0) break;
+        int got = -1;
+        if (lane == 0) {
+          const int b = qoff[U], len = qoff[U + 1] - b;
+          const uint32_t i = atomicAdd(&front[U], 1u);
+          if (i < (uint32_t)len) got = queue[b + (int)i];
+        }
+        item = __shfl(got, 0);
+      }
+    }
+    if (lane == 0) slot[call & 1] = item;
+  }
+  __syncthreads();
+  return slot[call & 1];
+}
+
 // The two roles run separate copies of the whole item loop, so that the
 // compiler never keeps one role's loop state live in the other's.
 template <int D, bool PW>
@@ -384,8 +460,6 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int vq) {
   const int lgG = __builtin_ctz(G), lgR = 4 + lgG;
   const sched_t tiles = S + S[H_OFF_TILES];
   const sched_t kvs = S + S[H_OFF_KV];
-  const sched_t queue = S + S[H_OFF_KVQUEUE];
-  const int qbeg = S[S[H_OFF_KVQOFF] + vq], qend = S[S[H_OFF_KVQOFF] + vq + 1];
   const float c = a.scale * kLog2e;
   const __bf16* Qg = static_cast<const __bf16*>(a.Q);
   const __bf16* dOg = static_cast<const __bf16*>(a.dO);
@@ -403,8 +477,13 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int vq) {
   const i32x4 stat_res = buf_res(a.ws_nD, 16 * a.stat_words);
   const uint32_t stat_off = (uint32_t)(((lane >> 4) * a.stat_words + 4 * (lane & 15)) * 4);
 
-  for (int qi = qbeg; qi < qend; ++qi) {
-    const sched_t it = kvs + queue[qi] * K_WORDS;
+  // items: the own queue, then the others' (kv_claim)
+  int own = 1, pending = 0;
+  if (tid == 0) pending = (int)atomicAdd(&a.kv_front[vq], 1u);
+  for (int call = 0;; ++call) {
+    const int item = kv_claim(S, a.kv_front, vq, own, pending, call);
+    if (item < 0) break;
+    const sched_t it = kvs + item * K_WORDS;
     const int head = it[K_HEAD], t0 = it[K_T0], nt = it[K_NT];
     const int dtok0 = it[K_DTOK0], nd = it[K_NDRAFT], b0 = it[K_B0], b1 = it[K_B1];
     // row tiles every row of which sees all of the item's keys
@@ -679,7 +758,8 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
   constexpr int RPB = 256 / (D / 8);
   SKV_LAUNCH("bwd_pre", bwd_pre_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256), 0, s,
              a.sched, static_cast<const __bf16*>(a.O), static_cast<const __bf16*>(a.dO), a.LSE,
-             a.ws_nD, a.ws_L2, a.ws_LO, a.ws_HI, rows, a.hq, a.hq / a.hkv, a.xcd_count);
+             a.ws_nD, a.ws_L2, a.ws_LO, a.ws_HI, rows, a.hq, a.hq / a.hkv, a.xcd_count,
+             a.kv_front, a.n_wg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static LdsLimit lds_dq, lds_kv;

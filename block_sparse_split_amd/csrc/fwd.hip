@@ -11,8 +11,9 @@
 // 64-key tiles); items were placed on persistent workgroups by LPT on the
 // host.  A query tile holds the rows (token, head) of the G query heads that
 // share kv head g, token-major, so the rows of one anchor block are adjacent
-// and share one mask bound.  Four waves per workgroup each own 64 rows (two
-// 32-query MFMA columns blocks).
+// and share one mask bound.  The bf16 kernel runs eight waves of 32 rows
+// (two groups half a step apart, below); the fp32 kernel four waves of 64
+// rows (two 32-query MFMA column blocks).
 //
 // Per 64-key step, each wave computes S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T held in registers),

@@ -1017,6 +1017,7 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
   const int64_t off_kv = off; off += int64_t(kv.size()) * K_WORDS;
   const int64_t off_kvqoff = off; off += n_wg + 1;
   const int64_t off_kvqueue = off; off += int64_t(kv.size());
+  const int64_t off_kvsuf = off; off += int64_t(kv.size());
   // dQ sections: the forward's unless dQ has a plan of its own
   int64_t off_dq_items = off_items, off_dq_qoff = off_qoff, off_dq_queue = off_queue,
           off_dq_split = off_split;
@@ -1035,10 +1036,12 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
   const int64_t fwd_ws = align_up(int64_t(n_slots) * rows_slot * g.d * 4, 256) +
                          align_up(int64_t(n_slots) * rows_slot * 4, 256) +
                          (xcd ? kXcdCounterBytes : 0);
-  // per-row statistics: per kv head, its rows plus kStatPad padding rows
+  // per-row statistics: per kv head, its rows plus kStatPad padding rows;
+  // then dQ's partial slots, the dK/dV claim counters (one per queue) and,
+  // in XCD mode, the per-XCD counters
   const int64_t bwd_ws = 4 * align_up(int64_t(g.hkv) * (g.rows_per_head + skv::kStatPad) * 4, 256) +
                          align_up(int64_t(dq_slots) * rows_slot * g.d * 4, 256) +
-                         (xcd ? kXcdCounterBytes : 0);
+                         align_up(int64_t(n_wg) * 4, 256) + (xcd ? kXcdCounterBytes : 0);
   std::memset(info, 0, sizeof(*info));
   info->words = words;
   info->n_workgroups = n_wg;
@@ -1104,6 +1107,7 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
   H[H_OFF_DQ_QOFF] = int32_t(off_dq_qoff);
   H[H_OFF_DQ_QUEUE] = int32_t(off_dq_queue);
   H[H_OFF_DQ_SPLIT] = int32_t(off_dq_split);
+  H[H_OFF_KVSUF] = int32_t(off_kvsuf);
   std::memcpy(image + off_anchors, A, size_t(g.nb) * 4);
   std::memcpy(image + off_lo, L, size_t(g.nb) * 4);
   for (int32_t t = 0; t < nt; ++t) {
@@ -1154,6 +1158,12 @@ void build_schedule(const skv_problem* p, int32_t n_wg, const float* xcd_speed,
   for (int32_t w = 0; w < n_wg; ++w) {
     image[off_kvqoff + w] = pos;
     for (int32_t it : kq[w]) image[off_kvqueue + pos++] = it;
+    // summed cost of each position and the rest of its queue
+    int64_t rest = 0;
+    for (int32_t j = pos - 1; j >= image[off_kvqoff + w]; --j) {
+      rest += kv[image[off_kvqueue + j]].cost;
+      image[off_kvsuf + j] = int32_t(std::min<int64_t>(rest, INT32_MAX));
+    }
   }
   image[off_kvqoff + n_wg] = pos;
 }
@@ -1457,6 +1467,14 @@ skv_status skv_attn_bwd(const skv_problem* p, const skv_schedule_info* info,
     a.ws_HI = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 3 * stat_bytes);
     a.ws_dQ = reinterpret_cast<float*>(static_cast<char*>(workspace) + 4 * stat_bytes);
     a.stat_words = stat_bytes / 4;
+    const int64_t dq_bytes =
+        align_up(int64_t(info->n_dq_partial_slots) * skv::kQTile * p->d * 4, 256);
+    const int64_t front_bytes = align_up(int64_t(info->n_workgroups) * 4, 256);
+    require(info->bwd_workspace_bytes >= 4 * stat_bytes + dq_bytes + front_bytes +
+                                             (info->xcd_mode ? skv::kXcdCounterBytes : 0),
+            "inconsistent schedule info (backward workspace)");
+    a.kv_front = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + 4 * stat_bytes +
+                                             dq_bytes);
     if (info->xcd_mode) {
       require(info->n_workgroups % skv::kXcds == 0 &&
                   info->bwd_workspace_bytes >= 4 * stat_bytes + skv::kXcdCounterBytes,

@@ -73,6 +73,7 @@ struct BwdArgs {
   unsigned long long* wg_clock_dq;  // per-workgroup (start, end) stamps, or null
   unsigned long long* wg_clock_kv;
   uint32_t* xcd_count;      // dQ then dK/dV per-XCD queue counters, or null (zeroed by pre)
+  uint32_t* kv_front;       // per dK/dV queue: positions claimed (n_wg words, zeroed by pre)
   int32_t grad_bf16, dtype_bf16;
   int32_t hq, hkv, d, nb, n_local;
   int32_t n_wg, n_split, n_slots, with_draft;

@@ -11,6 +11,11 @@
 // sections, or at dQ's own when the schedule was planned per XCD (the two
 // kernels' XCD speeds differ, so each gets its own cuts and queues).
 //
+// The dK/dV kernel takes its items from its queues at run time: a
+// workgroup runs the next unclaimed position of its own queue, then of the
+// queue with the most planned work left, read from H_OFF_KVSUF (per queue
+// position, the summed cost of that position and the rest of its queue).
+//
 // Queues are indexed by a queue number v in [0, n_wg).  Normally workgroup
 // v runs queue v.  When H_XCD is set, queue v was planned for XCD v % 8 at
 // that XCD's measured speed, and each workgroup takes the next unclaimed
@@ -21,7 +26,7 @@
 namespace skv {
 
 constexpr int32_t kMagic = 0x314B5653;  // "SVK1"
-constexpr int32_t kVersion = 3;
+constexpr int32_t kVersion = 4;
 constexpr int kBlock = 16;      // draft tokens per anchor block
 constexpr int kTileK = 64;      // keys per key tile
 constexpr int kQTile = 256;     // query rows (token x head of one kv head) per tile
@@ -36,7 +41,8 @@ enum Hdr : int {
   H_OFF_ANCHORS, H_OFF_LO, H_OFF_TILES, H_OFF_ITEMS, H_OFF_QOFF, H_OFF_QUEUE,
   H_OFF_SPLIT, H_OFF_KV, H_OFF_KVQOFF, H_OFF_KVQUEUE, H_NCLASS,
   H_XCD, H_OFF_DQ_ITEMS, H_OFF_DQ_QOFF, H_OFF_DQ_QUEUE, H_OFF_DQ_SPLIT,
-  H_WORDS = 32
+  H_OFF_KVSUF,
+  H_WORDS = 40
 };
 static_assert(H_OFF_DQ_SPLIT < H_WORDS, "header words overflow the header");
 

@@ -400,3 +400,28 @@ def test_calibration_without_backward_stamps():
     assert np.all(np.isfinite(sp)) and np.all(np.isfinite(sc))
     np.testing.assert_allclose(sp[0], true / true.mean(), rtol=0.01)
     assert np.all(sp[1:] == 1.0) and np.all(sc[1] == 1.0)
+
+
+@pytest.mark.parametrize("xcd", [False, True])
+def test_kv_suffix_costs_and_claim_counters(xcd):
+    """The dK/dV kernel claims its items at run time by the image's suffix
+    costs: per queue position, the summed cost of that position and the rest
+    of its queue; the backward workspace holds one claim counter per queue
+    beyond the statistics and dQ's slots."""
+    w, g, prob = _case("varlen8_fwdbwd", 3, None, len_median=2048, len_min=512, len_max=8192)
+    if xcd:
+        image, info = skv.skv_schedule_build_xcd(prob, 64, _speeds(4, 0.05))
+    else:
+        image, info = skv.skv_schedule_build(prob, 64)
+    h, tiles, items, kv, fq, kq = _decode(image)
+    suf = image[h["OFF_KVSUF"]: h["OFF_KVSUF"] + h["NKV"]]
+    qoff = image[h["OFF_KVQOFF"]: h["OFF_KVQOFF"] + h["NWG"] + 1]
+    cost = kv[:, K["COST"]].astype(np.int64)
+    for v, q in enumerate(kq):
+        want = np.cumsum(cost[q][::-1])[::-1]
+        assert np.array_equal(suf[qoff[v]:qoff[v + 1]], want)
+    G = w.hq // w.hkv
+    stat = -(-(w.hkv * (w.nq * G + 64) * 4) // 256) * 256
+    dq = -(-(info.n_dq_partial_slots * QTILE * w.d * 4) // 256) * 256
+    front = -(-(64 * 4) // 256) * 256
+    assert info.bwd_workspace_bytes == 4 * stat + dq + front + (256 if xcd else 0)
