@@ -217,7 +217,10 @@ typedef struct skv_schedule_info {
  * class (workgroup w runs on XCD w mod 8) so its keys/values share an L2.
  * Backward dK/dV items (kv head, two 64-key tiles) and draft groups (kv
  * head, 128 draft tokens) cost 13 plus 5 per 64-row tile of the anchor
- * blocks that see them, and are placed by plain LPT per XCD class.
+ * blocks that see them, and are placed by plain LPT per XCD class; at run
+ * time a workgroup that has finished its own queue takes the next items of
+ * the queue with the most planned work left (every item still runs once,
+ * and its outputs do not depend on where).
  *   image: host int32 buffer of capacity_words, or NULL to only fill
  *   `info` (size query).  The caller copies the image to device memory
  *   and passes that copy, with `info`, to the device calls below.  The
