@@ -529,8 +529,10 @@ def calibrate_from_stamps(datasets, groups_per_head: int = 8, ridge: float = 0.0
     are fitted in turn, the scales normalised to a cost-weighted mean of 1.
     Where the stamps cannot tell a kv head's overall cost from the speed of
     the XCDs that ran it (each head always ran on the same XCDs), the
-    ridge leaves that factor with the speeds.  dK/dV gets speeds only
-    (xcd_speeds_from_stamps)."""
+    ridge leaves that factor with the speeds.  dK/dV gets the dQ kernel's
+    speeds: its workgroups take items of other queues once their own is
+    done, so its stamps time more than the queue each was planned, and the
+    XCDs that run it are the same."""
     from .csrc_layout import I
     speed = np.ones((3, XCDS))
     first = None
@@ -588,9 +590,7 @@ def calibrate_from_stamps(datasets, groups_per_head: int = 8, ridge: float = 0.0
             sig = np.clip(beta / tau, 0.5, 2.0)
             sig /= (sig * wsum).sum() / wsum.sum()
         scale[k] = np.repeat(sig.reshape(hkv, ng), per, axis=1)[:, :qtph]
-    # dK/dV: speeds from its queues' loads (never scaled)
-    kv_runs = [r for image, runs, _ in datasets[-1:] for r in runs]
-    speed[2] = xcd_speeds_from_stamps(datasets[-1][0], kv_runs)[2]
+    speed[2] = speed[1]
     return speed, scale
 
 

@@ -346,8 +346,8 @@ def test_calibration_recovers_known_costs():
     second, _ = skv.skv_schedule_build_xcd(prob, 64, sp1, sc1)
     data = [(base, stamps(base, None), None), (second, stamps(second, sc1), sc1)]
     sp, sc = skv.calibrate_from_stamps(data, ridge=1e-4)
-    # dK/dV: the speeds themselves
-    np.testing.assert_allclose(sp[2], true_speed[2] / true_speed[2].mean(), rtol=0.01)
+    # dK/dV (whose stamps include items taken from other queues) gets dQ's
+    assert np.array_equal(sp[2], sp[1])
     for k in (0, 1):
         # the scales' pattern (here each head ran on four XCDs, so heads and
         # XCDs are told apart) ...
