@@ -714,7 +714,8 @@ def run_workload(args, workload):
     roof["traffic"] = traffic_for(dom, w.name, kernel_source_hash())
     roof["counters"] = mfma_counters_for(dom, w.name, kernel_source_hash())
 
-    realized = realized_balance(step, sh.info, 5, torch, args.fwd_only)
+    realized = realized_balance(step, sh.info, 5, torch, args.fwd_only, image=sh.image,
+                                plan_speed=None if xcd is None else speed)
     pair_loads = item_pair_loads(sh.image, g, w)
     fwd_ms = sum(kernels[k][1] for k in ("fwd_bf16", "merge_split") if k in kernels) / args.steps
     # the headline step time: the HIP-graph replay of the same step (no
@@ -771,7 +772,8 @@ def run_workload(args, workload):
                                  "on_xcd_w_plus_c_mod_8": v["on_xcd_w_plus_c_mod_8"],
                                  "xcd_rotation_per_run": v["xcd_rotation_per_run"],
                                  "distinct_cus": v["distinct_cus_per_run"],
-                                 "xcd_mean_us": v["xcd_mean_us"]}
+                                 "xcd_mean_us": v["xcd_mean_us"],
+                                 "decomposition": v.get("decomposition")}
                              for k, v in realized.items()}},
         "kernels": per_kernel,
         "roofline": roof,
@@ -886,7 +888,40 @@ SWEEPS = {
 }
 
 
-def balance_stats(runs, planned, names=("fwd_bf16", "bwd_dq", "bwd_dkdv")):
+def spread_decomposition(dur, xcc, load, plan_speed=None):
+    """What the realised spread of one kernel is made of, from its stamped
+    runs (dur, xcc: [runs, n_wg]) and the plan's queue loads (load: [n_wg];
+    queue v planned at plan_speed[v % 8], 1 without one): the spread left
+    if each XCD's mean speed were what the plan assumed (queue times
+    divided by their XCD's mean ratio of measured to planned time in the
+    same run), then if the per-queue residual that repeats in every run
+    (the cost model's error on that queue's items) were matched too; what
+    is still left then is step-to-step noise.  Queues without load are
+    left out."""
+    ok = load > 0
+    sp = np.ones(8) if plan_speed is None else np.asarray(plan_speed, np.float64)
+    planned = load.astype(np.float64) / sp[np.arange(len(load)) % 8]
+    d, x, ld = dur[:, ok], xcc[:, ok], planned[ok]
+    ratio = d / ld[None, :]
+    fac = np.ones_like(ratio)
+    for r in range(len(d)):
+        for c in range(8):
+            m = x[r] == c
+            if m.any():
+                fac[r, m] = ratio[r, m].mean()
+    q = ratio / fac                        # per queue, XCD speed removed
+    stable = q.mean(0) / q.mean()          # the part that repeats every run
+    no_xcd = d / fac
+    no_model = no_xcd / stable[None, :]
+    med = lambda a: float(np.median(a.max(1) / a.mean(1) - 1))
+    return {"if_xcd_speeds_matched": med(no_xcd),
+            "if_queue_residual_matched_too": med(no_model),
+            "queue_residual_rms": float(np.sqrt(np.mean((stable - 1) ** 2))),
+            "queue_residual_max": float(stable.max() - 1)}
+
+
+def balance_stats(runs, planned, names=("fwd_bf16", "bwd_dq", "bwd_dkdv"), loads=None,
+                  plan_speed=None):
     """Per kernel (forward, dQ, dK/dV = index 0, 1, 2 of each run's
     [3, n_wg, 4] array of (start, end, XCC_ID, HW_ID) words, stamps in
     100 MHz ticks): workgroup durations in us, max/mean - 1 per run and its
@@ -895,7 +930,9 @@ def balance_stats(runs, planned, names=("fwd_bf16", "bwd_dq", "bwd_dkdv")):
     workgroups w that ran on XCD w mod 8 and on XCD (w + c) mod 8 for the
     best single rotation c of each run (the plan only needs workgroups
     w = w' mod 8 to share an XCD), and the number of distinct compute units
-    (XCD, SE, CU) used."""
+    (XCD, SE, CU) used.  With the plan's queue loads, the forward and dQ
+    also get spread_decomposition (dK/dV workgroups take items of other
+    queues at run time, so their times are not their queues')."""
     out = {}
     n = runs[0].shape[1]
     for k, name in enumerate(("fwd_bf16", "bwd_dq", "bwd_dkdv")):
@@ -923,6 +960,9 @@ def balance_stats(runs, planned, names=("fwd_bf16", "bwd_dq", "bwd_dkdv")):
                          np.bincount(o, minlength=8).max() / n
                          for o in (xcc - np.arange(n)[None, :]) % 8])),
                      "distinct_cus_per_run": int(np.median([len(np.unique(c)) for c in cu]))}
+        if loads is not None and k < 2 and len(runs) > 1:
+            out[name]["decomposition"] = spread_decomposition(
+                dur, xcc, np.asarray(loads[k]), None if plan_speed is None else plan_speed[k])
     return out
 
 
@@ -956,14 +996,18 @@ def planned_imbalance(info):
             "bwd_dkdv": info.kv_cost_max_bin / (info.kv_cost_total / n) - 1}
 
 
-def realized_balance(step, info, steps, torch, fwd_only=False, runs=None):
+def realized_balance(step, info, steps, torch, fwd_only=False, runs=None, image=None,
+                     plan_speed=None):
     """Stamp every workgroup for `steps` steps (or take `runs`) and return
     balance_stats for the forward, dQ and dK/dV kernels (the forward only
-    with fwd_only)."""
+    with fwd_only); with the schedule image (and the per-XCD speeds it was
+    planned at, if any), the spread decomposition too."""
+    from block_sparse_split_amd import splitkv as skv
     if runs is None:
         runs = stamp_runs(step, info.n_workgroups, steps, torch)
+    loads = skv.queue_loads(image) if image is not None else None
     return balance_stats(runs, planned_imbalance(info), ("fwd_bf16",) if fwd_only else
-                         ("fwd_bf16", "bwd_dq", "bwd_dkdv"))
+                         ("fwd_bf16", "bwd_dq", "bwd_dkdv"), loads, plan_speed)
 
 
 def calibrate(data, fwd_only):
@@ -1006,7 +1050,7 @@ def wg_balance(args):
         step()
     prob = shards.whole_context_problem(w, g)
     runs = stamp_runs(step, n, args.steps, torch, SUSTAIN_STEPS)
-    plans = {"uniform": realized_balance(step, sh.info, 0, torch, runs=runs)}
+    plans = {"uniform": realized_balance(step, sh.info, 0, torch, runs=runs, image=sh.image)}
     data = [(sh.image, runs, None)]
     speed, scale = calibrate(data, False)
     if n % 8 == 0:
@@ -1016,13 +1060,14 @@ def wg_balance(args):
         # calibrated plan as well
         sh = skv.Shard(prob, n_workgroups=n, xcd_speed=speed)
         plans["xcd"] = realized_balance(step, sh.info, 0, torch, runs=stamp_runs(
-            step, n, args.steps, torch, SUSTAIN_STEPS))
+            step, n, args.steps, torch, SUSTAIN_STEPS), image=sh.image, plan_speed=speed)
         for rnd in range(2):
             speed, scale = calibrate(data, False)
             sh = skv.Shard(prob, n_workgroups=n, xcd_speed=speed, cost_scale=scale)
             runs = stamp_runs(step, n, args.steps, torch, SUSTAIN_STEPS)
             data.append((sh.image, runs, scale))
-        plans["calibrated"] = realized_balance(step, sh.info, 0, torch, runs=runs)
+        plans["calibrated"] = realized_balance(step, sh.info, 0, torch, runs=runs,
+                                               image=sh.image, plan_speed=speed)
     for plan, out in plans.items():
         for name, v in out.items():
             log(f"{plan} {name}: planned {v['planned_imbalance'] * 100:.2f} %, realised "

@@ -294,6 +294,26 @@ def cmd_balance(a):
                        f"{v['on_xcd_w_plus_c_mod_8'] * 100:5.1f}% "
                        f"(c={v['xcd_rotation_per_run'][0]})  {v['distinct_cus_per_run']:4d}   "
                        f"{rel}")
+    dec = [(title, k, v["decomposition"]) for title, kernels in plans
+           for k, v in kernels.items() if v.get("decomposition")]
+    if dec:
+        out += ["", "## what the realised spread is made of (forward and dQ)",
+                "plan        kernel      realised  if XCD speeds matched  "
+                "if queue residual matched too  queue residual rms / max"]
+        for title, k, d in dec:
+            tag = title.split(" (")[0].replace("plan for per-XCD speeds and cost scales",
+                                                "calibrated").replace(
+                "plan for per-XCD speeds", "per-XCD").replace("uniform plan", "uniform")
+            real = next(v for t, kk in plans for kn, v in kk.items()
+                        if t == title and kn == k)["realized_imbalance_median"]
+            out.append(f"{tag:<11} {k:<10} {real * 100:8.2f}% "
+                       f"{d['if_xcd_speeds_matched'] * 100:20.2f}% "
+                       f"{d['if_queue_residual_matched_too'] * 100:29.2f}% "
+                       f"{d['queue_residual_rms'] * 100:12.2f}% / {d['queue_residual_max'] * 100:.2f}%")
+        out += ["(queue times divided by their XCD's mean time per unit of planned load in "
+                "the same step,",
+                "then by the per-queue factor that repeats in every step: what is left is "
+                "step-to-step noise)"]
     out += ["", "planned = max/mean - 1 of the plan's workgroup loads (time units; in the "
             "per-XCD plan,",
             "each XCD's loads over its speed); realised = median over the steps of max/mean - 1 of "

@@ -112,8 +112,12 @@ def test_bench_tables(tmp_path):
     _json_line(src, {"workload": "w", "clock": "c", "workgroups": 256, "steps": 2,
                      "kernels": {"bwd_dq": k},
                      "kernels_xcd_plan": {"bwd_dq": dict(k, realized_imbalance_median=0.02)},
-                     "kernels_calibrated_plan": {"bwd_dq": dict(k,
-                                                                realized_imbalance_median=0.01)},
+                     "kernels_calibrated_plan": {"bwd_dq": dict(
+                         k, realized_imbalance_median=0.01,
+                         decomposition={"if_xcd_speeds_matched": 0.008,
+                                        "if_queue_residual_matched_too": 0.005,
+                                        "queue_residual_rms": 0.002,
+                                        "queue_residual_max": 0.006})},
                      "xcd_speed": [[1.0] * 8, [1.05] + [1.0] * 7, [0.9] * 8],
                      "cost_scale_range": [[0.95, 1.02], [0.9, 1.1]]})
     out = tmp_path / "b.txt"
@@ -127,6 +131,9 @@ def test_bench_tables(tmp_path):
     assert [l.split()[2] for l in lines if l.startswith("speed")] == ["1.000", "1.050", "0.900"]
     assert [l.split()[3:] for l in lines if l.startswith("cost scales")] == [
         ["0.950", "..", "1.020"], ["0.900", "..", "1.100"]]
+    # the spread decomposition, for the plans that carry one
+    dec = [l.split() for l in lines if l.startswith("calibrated ")]
+    assert dec == [["calibrated", "bwd_dq", "1.00%", "0.80%", "0.50%", "0.20%", "/", "0.60%"]]
     # a record without the per-XCD plan prints the uniform table only
     _json_line(src, {"workload": "w", "clock": "c", "workgroups": 256, "steps": 2,
                      "kernels": {"bwd_dq": k}})
