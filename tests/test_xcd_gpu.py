@@ -95,3 +95,47 @@ def test_xcd_plan_shard_partials():
     O, L, _ = gpu_fwd(w, g, t, ids[2], False, shard=sh)
     Oo, Lo = oracle_partial(w, g, t, ids[2], False)
     compare(O, L, Oo, Lo, "bf16", "xcd shard")
+
+
+@pytest.mark.parametrize("layout", ["one_queue", "reversed"])
+def test_dkdv_items_claimed_across_queues(layout):
+    """The dK/dV kernel claims items of other queues once its own is done,
+    and an item's outputs do not depend on the workgroup that runs it: with
+    every dK/dV item moved into queue 0 (the other workgroups find their
+    queues empty at once and take everything from it) or with the queues
+    reversed, dK, dV, dKd, dVd and dQ are bit-identical to the planned
+    queues'."""
+    from block_sparse_split_amd.csrc_layout import H, K as KW, K_WORDS
+    w, g, t = _small(4)
+    prob = shards.whole_context_problem(w, g)
+    sh = skv.Shard(prob, n_workgroups=16)
+    announce("dkdv claims across queues", layout)
+    ref = _run(w, t, sh)
+    img = sh.image.copy()
+    h = {k: int(img[v]) for k, v in H.items()}
+    n, nkv = h["NWG"], h["NKV"]
+    qoff = img[h["OFF_KVQOFF"]: h["OFF_KVQOFF"] + n + 1].copy()
+    queue = img[h["OFF_KVQUEUE"]: h["OFF_KVQUEUE"] + nkv].copy()
+    cost = img[h["OFF_KV"]: h["OFF_KV"] + nkv * K_WORDS].reshape(-1, K_WORDS)[:, KW["COST"]]
+    qs = [list(queue[qoff[v]:qoff[v + 1]]) for v in range(n)]
+    if layout == "one_queue":
+        qs = [[i for q in qs for i in q]] + [[] for _ in range(n - 1)]
+    else:
+        qs = qs[::-1]
+    pos = 0
+    for v in range(n):
+        img[h["OFF_KVQOFF"] + v] = pos
+        for i in qs[v]:
+            img[h["OFF_KVQUEUE"] + pos] = i
+            pos += 1
+        # suffix costs of the new queue
+        rest = 0
+        for j in range(pos - 1, img[h["OFF_KVQOFF"] + v] - 1, -1):
+            rest += int(cost[img[h["OFF_KVQUEUE"] + j]])
+            img[h["OFF_KVSUF"] + j] = rest
+    img[h["OFF_KVQOFF"] + n] = pos
+    assert pos == nkv
+    sh.schedule = torch.from_numpy(img).to(sh.schedule.device)
+    got = _run(w, t, sh)
+    for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV", "dKd", "dVd"), ref, got):
+        assert torch.equal(x, y), name
