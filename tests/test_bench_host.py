@@ -1,7 +1,8 @@
-"""Host-side figures of bench.py checked against the oracle's planner (no
-GPU): the chunk-level LPT and contiguous-split imbalances reported for the
-1M-context job follow the oracle's independent LPT scan and contiguous split
-exactly."""
+"""Host-side figures of bench.py (no GPU): the chunk-level LPT and
+contiguous-split imbalances reported for the 1M-context job follow the
+oracle's independent LPT scan and contiguous split exactly, and the
+realised-spread decomposition separates per-XCD, per-queue and per-run
+parts of synthetic queue times."""
 import os
 import sys
 
@@ -106,3 +107,34 @@ def test_item_pair_loads_by_hand():
         assert loads.sum() == (2 + 1) + (3 + 1)
     image, info = skv.skv_schedule_build(prob, 1)
     assert bench.item_pair_loads(image, G_, w).tolist() == [7]
+
+
+def test_spread_decomposition_separates_its_parts():
+    """Queue times built from a plan's loads times known per-XCD factors,
+    known per-queue factors that repeat every run, and small per-run noise:
+    the decomposition's spread without the XCD part is that of the queue
+    factors and noise, without both that of the noise, and the queue
+    residual it reports is the queue factors'.  Queues planned at per-XCD
+    speeds (load / speed) count as on time."""
+    rng = np.random.default_rng(3)
+    n, runs = 64, 8
+    load = rng.uniform(900, 1100, n)
+    speed = 1 + 0.05 * np.sin(np.arange(8))
+    xfac = 1 + 0.04 * np.cos(np.arange(8))           # per-XCD deviation from the plan
+    qfac = 1 + 0.02 * rng.standard_normal(n)         # per-queue model error
+    qfac /= qfac.mean()
+    dur = np.zeros((runs, n))
+    xcc = np.zeros((runs, n), np.int64)
+    for r in range(runs):
+        x = (np.arange(n) + r) % 8                   # a rotation of queues to XCDs
+        xcc[r] = x
+        noise = 1 + 0.002 * rng.standard_normal(n)
+        dur[r] = load / speed[np.arange(n) % 8] * xfac[x] * qfac * noise
+    d = bench.spread_decomposition(dur, xcc, load, speed)
+    planned = load / speed[np.arange(n) % 8]
+    imb = lambda a: a.max() / a.mean() - 1
+    assert abs(d["if_xcd_speeds_matched"] - imb(planned * qfac)) < 0.01
+    assert d["if_queue_residual_matched_too"] < imb(planned) + 0.01
+    assert abs(d["queue_residual_rms"] - np.sqrt(np.mean((qfac - 1) ** 2))) < 0.002
+    # with the XCD factors, the realised spread is clearly larger
+    assert imb(dur[0]) > d["if_xcd_speeds_matched"] + 0.02
