@@ -29,9 +29,10 @@ def check_grad(got, want, what, abs_tol=ABS_TOL):
     return err, scale
 
 
-def gpu_bwd(w, g, t, chunk_ids, with_draft, O, LSE, n_wg=0, grad_dtype=skv.SKV_F32):
+def gpu_bwd(w, g, t, chunk_ids, with_draft, O, LSE, n_wg=0, grad_dtype=skv.SKV_F32,
+            xcd_speed=None):
     prob = shards.shard_problem(w, g, chunk_ids, with_draft)
-    sh = skv.Shard(prob, n_workgroups=n_wg)
+    sh = skv.Shard(prob, n_workgroups=n_wg, xcd_speed=xcd_speed)
     r = rows_of(t, g, chunk_ids)
     dt = w.dtype
     Q, K, V = to_dev(t.Q, dt), to_dev(t.K[r], dt), to_dev(t.V[r], dt)

@@ -139,3 +139,25 @@ def test_dkdv_items_claimed_across_queues(layout):
     got = _run(w, t, sh)
     for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV", "dKd", "dVd"), ref, got):
         assert torch.equal(x, y), name
+
+
+def test_xcd_plan_empty_and_draft_only_shards():
+    """Per-XCD plans of shards without context keys: the empty shard has no
+    dK/dV item at all (every workgroup finds nothing to claim) and adds
+    nothing to dQ; the draft-only shard's dQ share and draft-key gradients
+    match the oracle."""
+    from test_bwd_gpu import gpu_bwd, oracle_fwd_bwd as ofb
+    w, g, t = _small(9, blocks_per_seq=4)
+    allc = np.arange(len(g.chunk_pos))
+    O, L, _ = ofb(w, g, t, allc, True)
+    Od = to_dev(wl.round_to_bf16(O.astype(np.float32)), "bf16")
+    Ld = torch.from_numpy(L.astype(np.float32)).cuda()
+    announce("xcd plan empty shard")
+    dQ, dK, dV, _, _ = gpu_bwd(w, g, t, [], False, Od, Ld, n_wg=16, xcd_speed=_speeds(9))
+    assert dK.shape[0] == 0 and torch.all(dQ == 0)
+    announce("xcd plan draft-only shard")
+    dQ, _, _, dKd, dVd = gpu_bwd(w, g, t, [], True, Od, Ld, n_wg=16, xcd_speed=_speeds(10))
+    _, _, (wq, _, _, wkd, wvd) = ofb(w, g, t, [], True)
+    check_grad(dQ, wq, "xcd draft-only dQ share")
+    check_grad(dKd, wkd, "xcd draft-only dKd")
+    check_grad(dVd, wvd, "xcd draft-only dVd")
