@@ -237,7 +237,9 @@ skv_status skv_schedule_build(const skv_problem* p, int32_t n_workgroups,
  * realised speed of the hardware that runs them enters the cost).
  * xcd_speed[k * 8 + x] is the relative speed (work per unit time, any
  * positive scale) of XCD x in kernel k: 0 the forward, 1 dQ, 2 dK/dV, for
- * instance measured with skv_timing_wg_clock on a schedule without it.
+ * instance measured with skv_timing_wg_clock on a schedule without it
+ * (dK/dV workgroups also run items of other queues, so their stamps do not
+ * time their own queue alone: the dQ kernel's speeds can stand in).
  * Queue v is planned at the speed of XCD v % 8.  Each XCD class (the
  * workgroups that hold one kv head's work) first gets a share of the work
  * in proportion to its total speed: classes above their share pass whole
