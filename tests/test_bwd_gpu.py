@@ -2,6 +2,8 @@
 against the fp64 oracle through the C ABI.  Bar: max-abs <= 2e-2 for the
 bf16 path; every check also bounds the error relative to the largest
 reference value, so small gradients cannot pass by being small."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -10,7 +12,7 @@ import oracle
 from block_sparse_split_amd import splitkv as skv
 from block_sparse_split_amd import shards
 from block_sparse_split_amd import workloads as wl
-from gpu_util import announce, block_rows, gpu_fwd, rows_of, to_dev
+from gpu_util import announce, block_rows, gpu_fwd, measured_like_plan, rows_of, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -30,9 +32,9 @@ def check_grad(got, want, what, abs_tol=ABS_TOL):
 
 
 def gpu_bwd(w, g, t, chunk_ids, with_draft, O, LSE, n_wg=0, grad_dtype=skv.SKV_F32,
-            xcd_speed=None):
+            xcd_speed=None, cost_scale=None):
     prob = shards.shard_problem(w, g, chunk_ids, with_draft)
-    sh = skv.Shard(prob, n_workgroups=n_wg, xcd_speed=xcd_speed)
+    sh = skv.Shard(prob, n_workgroups=n_wg, xcd_speed=xcd_speed, cost_scale=cost_scale)
     r = rows_of(t, g, chunk_ids)
     dt = w.dtype
     Q, K, V = to_dev(t.Q, dt), to_dev(t.K[r], dt), to_dev(t.V[r], dt)
@@ -234,44 +236,60 @@ def test_bwd_varlen_small():
         check_grad(a, b, f"varlen {name}")
 
 
-def test_bwd_full_ctx32k_sampled():
-    """The 32K-context shapes on all CUs: dQ on sampled anchor blocks and
-    dK/dV on sampled key ranges, against the oracle (which recomputes the
-    full forward for the normaliser)."""
-    w, g, t = wl.make("ctx32k_q2k", 1, with_grad=True)
+def full_fwd_bwd(w, g, t, plan):
+    """Forward then backward over the whole context on every CU: with the
+    uniform plan and fp32 gradients, or as the benchmark runs it (a per-XCD
+    plan with cost scales, bf16 gradients)."""
     allc = np.arange(len(g.chunk_pos))
-    announce("bwd full ctx32k")
-    O, L, _ = gpu_fwd(w, g, t, allc, True)
-    dQ, dK, dV, dKd, dVd = gpu_bwd(w, g, t, allc, True, O, L)
+    if plan == "uniform":
+        O, L, _ = gpu_fwd(w, g, t, allc, True)
+        return gpu_bwd(w, g, t, allc, True, O, L)
+    sh, speed, scale = measured_like_plan(w, g, 11)
+    O, L, _ = gpu_fwd(w, g, t, allc, True, shard=sh)
+    return gpu_bwd(w, g, t, allc, True, O, L, grad_dtype=skv.SKV_BF16, xcd_speed=speed,
+                   cost_scale=scale)
+
+
+@functools.lru_cache(maxsize=1)
+def expected_ctx32k():
+    """The 32K workload and the oracle's gradients on sampled anchor blocks
+    (dQ and the draft-key gradients) and sampled key ranges (dK, dV); the
+    oracle recomputes the full forward for the normaliser."""
+    w, g, t = wl.make("ctx32k_q2k", 1, with_grad=True)
     scale = wl.softmax_scale(w.d)
     Oo, Lo = oracle.attention(t.Q, t.K, t.V, t.Kd, t.Vd, g.anchors, g.lo, scale)
     blocks = [0, 5, 63, 64, 126, 127]
-    rows = block_rows(blocks)
     gq = oracle.attention_bwd(t.Q, t.K, t.V, np.arange(g.ctx), g.anchors, g.lo, scale, Oo,
                               t.dO, Lo, t.Kd, t.Vd, blocks=blocks)
-    check_grad(dQ[rows], gq[0][rows], "dQ sampled rows")
-    check_grad(dKd[rows], gq[3][rows], "dKd sampled rows")
-    check_grad(dVd[rows], gq[4][rows], "dVd sampled rows")
     keys = np.concatenate([np.arange(0, 64), np.arange(20000, 20100), np.arange(32700, 32768)])
     gk = oracle.attention_bwd(t.Q, t.K[keys], t.V[keys], keys, g.anchors, g.lo, scale, Oo, t.dO,
                               Lo)
+    return (w, g, t), block_rows(blocks), keys, gq, gk
+
+
+@pytest.mark.parametrize("plan", ["uniform", "xcd_bf16_grads"])
+def test_bwd_full_ctx32k_sampled(plan):
+    """The 32K-context shapes on all CUs: dQ on sampled anchor blocks and
+    dK/dV on sampled key ranges, against the oracle."""
+    (w, g, t), rows, keys, gq, gk = expected_ctx32k()
+    announce("bwd full ctx32k", plan)
+    dQ, dK, dV, dKd, dVd = full_fwd_bwd(w, g, t, plan)
+    check_grad(dQ[rows], gq[0][rows], "dQ sampled rows")
+    check_grad(dKd[rows], gq[3][rows], "dKd sampled rows")
+    check_grad(dVd[rows], gq[4][rows], "dVd sampled rows")
     check_grad(dK[keys], gk[1], "dK sampled keys")
     check_grad(dV[keys], gk[2], "dV sampled keys")
 
 
-def test_bwd_full_varlen_sampled():
+@functools.lru_cache(maxsize=1)
+def expected_varlen():
     """Varlen batch (8 packed sequences, lognormal lengths, late-skewed
-    anchors) on all CUs: dQ and the draft-key gradients on sampled anchor
-    blocks, dK/dV on sampled key ranges (a sequence start, a late range and a
-    sequence end), against the oracle run on exactly the anchor blocks that
-    see those keys."""
+    anchors) and the oracle's gradients on sampled key ranges (a sequence
+    start, a late range and a sequence end) and on exactly the anchor
+    blocks that see those keys, plus three more blocks for dQ."""
     w, g, t = wl.make("varlen8_fwdbwd", 5, with_grad=True)
-    allc = np.arange(len(g.chunk_pos))
-    announce("bwd full varlen")
-    O, L, _ = gpu_fwd(w, g, t, allc, True)
-    dQ, dK, dV, dKd, dVd = gpu_bwd(w, g, t, allc, True, O, L)
     scale = wl.softmax_scale(w.d)
-    s0, l0 = int(g.seq_start[1]), int(g.seq_len[1])
+    s0 = int(g.seq_start[1])
     s1, l1 = int(g.seq_start[3]), int(g.seq_len[3])
     keys = np.concatenate([np.arange(s0, s0 + 32),
                            np.arange(s1 + int(0.92 * l1), s1 + int(0.92 * l1) + 48),
@@ -287,12 +305,23 @@ def test_bwd_full_varlen_sampled():
     Of[rows], Lf[rows] = Ob, Lb
     gq = oracle.attention_bwd(t.Q, t.K, t.V, np.arange(g.ctx), g.anchors, g.lo, scale, Of,
                               t.dO, Lf, t.Kd, t.Vd, blocks=blocks)
-    check_grad(dQ[rows], gq[0][rows], "varlen dQ sampled rows")
-    check_grad(dKd[rows], gq[3][rows], "varlen dKd sampled rows")
-    check_grad(dVd[rows], gq[4][rows], "varlen dVd sampled rows")
     # rows outside `blocks` see none of the sampled keys
     gk = oracle.attention_bwd(t.Q, t.K[keys], t.V[keys], keys, g.anchors, g.lo, scale, Of, t.dO,
                               Lf)
+    return (w, g, t), rows, keys, gq, gk
+
+
+@pytest.mark.parametrize("plan", ["uniform", "xcd_bf16_grads"])
+def test_bwd_full_varlen_sampled(plan):
+    """The varlen batch on all CUs: dQ and the draft-key gradients on
+    sampled anchor blocks, dK/dV on sampled key ranges, against the
+    oracle."""
+    (w, g, t), rows, keys, gq, gk = expected_varlen()
+    announce("bwd full varlen", plan)
+    dQ, dK, dV, dKd, dVd = full_fwd_bwd(w, g, t, plan)
+    check_grad(dQ[rows], gq[0][rows], "varlen dQ sampled rows")
+    check_grad(dKd[rows], gq[3][rows], "varlen dKd sampled rows")
+    check_grad(dVd[rows], gq[4][rows], "varlen dVd sampled rows")
     check_grad(dK[keys], gk[1], "varlen dK sampled keys")
     check_grad(dV[keys], gk[2], "varlen dV sampled keys")
 

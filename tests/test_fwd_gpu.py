@@ -9,8 +9,8 @@ import oracle
 from block_sparse_split_amd import splitkv as skv
 from block_sparse_split_amd import shards
 from block_sparse_split_amd import workloads as wl
-from gpu_util import (announce, block_rows, compare, gpu_fwd, oracle_partial, rows_of,
-                      to_dev)
+from gpu_util import (announce, block_rows, compare, gpu_fwd, measured_like_plan,
+                      oracle_partial, rows_of, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -237,13 +237,20 @@ def _sample_blocks(g, n_extra=4, seed=0):
     return sorted(set(fixed) | set(rng.choice(nb, n_extra, replace=False).tolist()))
 
 
-def test_full_ctx32k_sampled_rows():
+def _full_plan(w, g, plan):
+    """None (the uniform plan on every CU) or a per-XCD plan with cost
+    scales, as the benchmark times."""
+    return None if plan == "uniform" else measured_like_plan(w, g, 12)[0]
+
+
+@pytest.mark.parametrize("plan", ["uniform", "xcd"])
+def test_full_ctx32k_sampled_rows(plan):
     """32K context, 2048 queries, 32q/8kv, d=128 on all CUs (the benchmark
     launch): sampled anchor blocks x all heads against the oracle."""
     w, g, t = wl.make("ctx32k_q2k", 1)
     allc = np.arange(len(g.chunk_pos))
-    announce("full ctx32k")
-    O, L, _ = gpu_fwd(w, g, t, allc, True)
+    announce("full ctx32k", plan)
+    O, L, _ = gpu_fwd(w, g, t, allc, True, shard=_full_plan(w, g, plan))
     blocks = _sample_blocks(g)
     Oo, Lo = oracle.attention(t.Q, t.K, t.V, t.Kd, t.Vd, g.anchors, g.lo,
                               wl.softmax_scale(w.d), blocks=blocks)
@@ -266,11 +273,12 @@ def test_full_cp64_rank0_sampled_rows():
     compare(O[rows], L[rows], Oo, Lo, "bf16", "cp64 rank0 sampled")
 
 
-def test_full_varlen_fwd_sampled_rows():
+@pytest.mark.parametrize("plan", ["uniform", "xcd"])
+def test_full_varlen_fwd_sampled_rows(plan):
     w, g, t = wl.make("varlen8_fwdbwd", 3)
     allc = np.arange(len(g.chunk_pos))
-    announce("full varlen fwd")
-    O, L, _ = gpu_fwd(w, g, t, allc, True)
+    announce("full varlen fwd", plan)
+    O, L, _ = gpu_fwd(w, g, t, allc, True, shard=_full_plan(w, g, plan))
     blocks = _sample_blocks(g, n_extra=6, seed=2)
     Oo, Lo = oracle.attention(t.Q, t.K, t.V, t.Kd, t.Vd, g.anchors, g.lo,
                               wl.softmax_scale(w.d), blocks=blocks)
