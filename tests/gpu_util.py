@@ -48,11 +48,10 @@ def gpu_fwd(w, g, t, chunk_ids, with_draft, n_wg=0, o_dtype=None, shard=None):
     return O, LSE, sh
 
 
-def measured_like_plan(w, g, seed):
+def measured_like_plan(w, prob, seed):
     """Per-XCD speeds and per-(kv head, query tile) cost scales spread as
     measured ones are (a few per cent): the kind of plan the benchmark
     times, built for every CU."""
-    prob = shards.whole_context_problem(w, g)
     rng = np.random.default_rng(seed)
     speed = (1.0 + 0.04 * rng.uniform(-1, 1, (3, 8))).astype(np.float32)
     scale = rng.uniform(0.97, 1.03, (2, w.hkv, prob.qt_per_head))

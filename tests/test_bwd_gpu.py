@@ -244,7 +244,7 @@ def full_fwd_bwd(w, g, t, plan):
     if plan == "uniform":
         O, L, _ = gpu_fwd(w, g, t, allc, True)
         return gpu_bwd(w, g, t, allc, True, O, L)
-    sh, speed, scale = measured_like_plan(w, g, 11)
+    sh, speed, scale = measured_like_plan(w, shards.whole_context_problem(w, g), 11)
     O, L, _ = gpu_fwd(w, g, t, allc, True, shard=sh)
     return gpu_bwd(w, g, t, allc, True, O, L, grad_dtype=skv.SKV_BF16, xcd_speed=speed,
                    cost_scale=scale)

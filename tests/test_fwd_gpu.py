@@ -237,10 +237,14 @@ def _sample_blocks(g, n_extra=4, seed=0):
     return sorted(set(fixed) | set(rng.choice(nb, n_extra, replace=False).tolist()))
 
 
-def _full_plan(w, g, plan):
+def _full_plan(w, g, plan, chunk_ids=None, with_draft=True):
     """None (the uniform plan on every CU) or a per-XCD plan with cost
-    scales, as the benchmark times."""
-    return None if plan == "uniform" else measured_like_plan(w, g, 12)[0]
+    scales, as the benchmark times, of the whole context or of a shard."""
+    if plan == "uniform":
+        return None
+    prob = (shards.whole_context_problem(w, g) if chunk_ids is None
+            else shards.shard_problem(w, g, chunk_ids, with_draft))
+    return measured_like_plan(w, prob, 12)[0]
 
 
 @pytest.mark.parametrize("plan", ["uniform", "xcd"])
@@ -259,14 +263,15 @@ def test_full_ctx32k_sampled_rows(plan):
     assert torch.all(torch.isfinite(L))
 
 
-def test_full_cp64_rank0_sampled_rows():
+@pytest.mark.parametrize("plan", ["uniform", "xcd"])
+def test_full_cp64_rank0_sampled_rows(plan):
     """512K context split over 64 LPT ranks; rank 0's chunks against all
     4096 queries; sampled blocks against the oracle partial."""
     w, g, _ = wl.make("cp64_rank0_ctx512k", 2, tensors=False)
     ids, _, _, _ = shards.lpt_shards(w, g, w.n_shards)
     t = wl.draw_tensors(w, g, 2, chunk_ids=ids[0])
-    announce("full cp64 rank0")
-    O, L, _ = gpu_fwd(w, g, t, ids[0], True)
+    announce("full cp64 rank0", plan)
+    O, L, _ = gpu_fwd(w, g, t, ids[0], True, shard=_full_plan(w, g, plan, ids[0], True))
     blocks = _sample_blocks(g, seed=1)
     Oo, Lo = oracle_partial(w, g, t, ids[0], True, blocks=blocks)
     rows = block_rows(blocks)
